@@ -1,0 +1,470 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix (CPU only).
+
+Every check here is independent of the oracle's own code path: closed forms,
+invariants, brute force over tiny inputs, special cases that reduce to a
+library routine, and a fixture worked by hand from the pages' rules.  The
+mutation tests at the end plant plausible mistakes in the oracle (on the CPU)
+and confirm that a pin catches each one.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.hinm as oh
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bits_of(w_bf16: torch.Tensor) -> np.ndarray:
+    return w_bf16.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def run_pack(w: synth.Workload, v_s=None):
+    p = oh.plan(w.cout, w.cin, w.tile_rows, w.t_s, w.v_s if v_s is None else v_s)
+    packed, inter = oh.pack(bits_of(w.w_bf16), w.importance.numpy(), w.perm.numpy(), p,
+                            with_intermediates=True)
+    return p, packed, inter
+
+
+# --------------------------------------------------------------------------------------
+# Closed form of the region counts (FlexHiNM-GP notes, key design 1)
+# --------------------------------------------------------------------------------------
+
+def check_counts(cin, t_s, v_s):
+    p = oh.plan(64, cin, 64, t_s, v_s)
+    assert p.n_dense + p.n_24 + p.n_pruned == cin
+    assert p.n_24 % 4 == 0 and min(p.n_dense, p.n_24, p.n_pruned) >= 0
+    # 2:4 vectors lose half their entries: zeros = pruned + n_24 / 2 exactly.
+    assert 2 * p.z == 2 * p.n_pruned + p.n_24
+    assert abs(Fraction(p.z, cin) - Fraction(t_s)) <= Fraction(1, 2 * cin)
+    # The page's identity t = v + (1 - v) p / 2 holds exactly for the realised fractions.
+    v_eff = Fraction(p.n_pruned, cin)
+    if p.n_dense + p.n_24:
+        p_eff = Fraction(p.n_24, p.n_dense + p.n_24)
+        assert v_eff + (1 - v_eff) * p_eff / 2 == Fraction(p.z, cin)
+    assert abs(p.n_pruned - v_s * cin) <= 1.5 + 1e-9
+    assert abs(p.n_24 - 2 * (t_s - v_s) * cin) <= 2 + 1e-9
+    return p
+
+
+def test_counts_closed_form_random():
+    rng = np.random.default_rng(7)
+    for _ in range(400):
+        cin = 4 * int(rng.integers(1, 3000))
+        t = float(rng.uniform(0, 0.99))
+        lo = max(0.0, 2 * t - 1)
+        v = float(rng.uniform(lo, t))
+        check_counts(cin, t, v)
+
+
+def test_counts_exact_when_integral():
+    # When t*cin and (t - v)*cin/2 are integers the realised fractions equal the page's.
+    for cin, t, v in [(4096, 0.5, 0.25), (4096, 0.75, 0.5), (256, 0.75, 0.5), (1024, 0.625, 0.375)]:
+        p = check_counts(cin, t, v)
+        assert p.n_pruned == v * cin
+        assert abs(p.n_24 / (p.n_24 + p.n_dense) - 2 * (t - v) / (1 - v)) < 1e-12
+        assert abs(p.p_s - 2 * (t - v) / (1 - v)) < 1e-15
+
+
+def test_counts_endpoints():
+    # v = t gives p = 0 (no 2:4 region, vector pruning only);
+    # v = 2t - 1 gives p = 1 (no dense region: HiNM-V, vector pruning then uniform 2:4).
+    for cin, t in [(4096, 0.75), (11008, 0.75), (256, 0.6), (4096, 0.5)]:
+        p = oh.plan(64, cin, 64, t, t)
+        assert p.n_24 == 0 and p.n_dense == cin - p.z
+        p = oh.plan(64, cin, 64, t, max(0.0, 2 * t - 1))
+        assert p.n_dense <= 2, p   # only rounding slack remains
+        if (t * cin) % 1 == 0 and ((1 - t) * cin) % 2 == 0:
+            assert p.n_dense == 0
+
+
+def test_counts_of_the_workloads():
+    # The region counts of the LLaMA-7B-shaped workloads follow from the same formula.
+    assert (lambda p: (p.n_dense, p.n_24, p.n_pruned))(oh.plan(128, 256, 32, 0.75, 0.5)) == (0, 128, 128)
+    assert (lambda p: (p.n_dense, p.n_24, p.n_pruned))(oh.plan(4096, 4096, 64, 0.5, 0.25)) == (1024, 2048, 1024)
+    assert (lambda p: (p.n_dense, p.n_24, p.n_pruned))(oh.plan(11008, 4096, 64, 0.75, 0.55)) == (204, 1640, 2252)
+    assert (lambda p: (p.n_dense, p.n_24, p.n_pruned))(oh.plan(4096, 11008, 64, 0.75, 0.55)) == (550, 4404, 6054)
+
+
+@pytest.mark.parametrize("args", [
+    (64, 256, 48, 0.5, 0.25),    # tile_rows not a multiple of 16... 48 is; cout % 48 != 0
+    (64, 254, 64, 0.5, 0.25),    # cin % 4
+    (64, 256, 64, 0.5, 0.6),     # v > t
+    (64, 256, 64, 0.75, 0.4),    # v < 2t - 1
+    (64, 256, 64, 1.0, 0.99),    # t = 1
+    (64, 256, 64, float("nan"), 0.0),
+])
+def test_plan_rejects(args):
+    with pytest.raises(oracle.OracleError):
+        oh.plan(*args)
+
+
+# --------------------------------------------------------------------------------------
+# Hand-worked fixture
+# --------------------------------------------------------------------------------------
+
+def handworked():
+    g = json.load(open(os.path.join(GOLDEN, "handworked_16x8.json")))
+    R, C = g["cout"], g["cin"]
+    w = np.array([[(r + 1) + c / 8 for c in range(C)] for r in range(R)], dtype=np.float32)
+    base = np.array(g["base"], dtype=np.float32)
+    d = np.tile(base, (R, 1))
+    a, b = g["odd_row_swap"]
+    d[1::2, a], d[1::2, b] = base[b], base[a]
+    x = np.array([[c + 1, (-1) ** c] for c in range(C)], dtype=np.float64)
+    return g, w, d, x
+
+
+def test_handworked_fixture():
+    g, w, d, x = handworked()
+    p = oh.plan(g["cout"], g["cin"], g["tile_rows"], g["t_s"], g["v_s"])
+    for k, v in g["counts"].items():
+        assert getattr(p, k) == v, k
+    wb = bits_of(torch.from_numpy(w).to(torch.bfloat16))
+    packed, inter = oh.pack(wb, d, np.array([g["perm"]]), p, with_intermediates=True)
+    assert inter["scores"][0].tolist() == g["scores"]
+    reg = inter["regions"][0]
+    assert sorted(np.nonzero(reg == oh.DENSE)[0].tolist()) == g["dense"]
+    assert sorted(np.nonzero(reg == oh.TWO_FOUR)[0].tolist()) == g["two_four"]
+    assert sorted(np.nonzero(reg == oh.PRUNED)[0].tolist()) == g["pruned"]
+    assert packed["idx_dense"][0, :2].tolist() == g["idx_dense"]
+    assert (packed["idx_dense"][0, 2:] == -1).all()
+    assert packed["idx_24"][0, :4].tolist() == g["idx_24"]
+    assert (packed["idx_24"][0, 4:] == -1).all()
+    meta = packed["meta_24"][0, 0]
+    assert all(int(meta[r]) == int(g["meta_even"], 16) for r in range(0, 16, 2))
+    assert all(int(meta[r]) == int(g["meta_odd"], 16) for r in range(1, 16, 2))
+    for r in range(16):
+        cols = g["val24_even_cols"] if r % 2 == 0 else g["val24_odd_cols"]
+        assert packed["val_24"][0, 0, r, :2].tolist() == [int(wb[r, c]) for c in cols]
+        assert (packed["val_24"][0, 0, r, 2:] == 0).all()
+        assert packed["val_dense"][0, 0, r, :2].tolist() == [int(wb[r, 3]), int(wb[r, 7])]
+        kept = g["kept_even"] if r % 2 == 0 else g["kept_odd"]
+        assert np.nonzero(inter["mask"][r])[0].tolist() == kept
+    # Y by a brute-force sum over the hand-derived kept set.
+    y = oh.spmm(oh.unpack(packed, p), x)
+    for r in range(16):
+        kept = g["kept_even"] if r % 2 == 0 else g["kept_odd"]
+        for n in range(2):
+            assert y[r, n] == math.fsum(float(w[r, c]) * x[c, n] for c in kept)
+
+
+# --------------------------------------------------------------------------------------
+# Invariants and brute force
+# --------------------------------------------------------------------------------------
+
+def check_sparsity(p, inter):
+    kept = inter["mask"].sum(axis=1)
+    assert (kept == p.cin - p.z).all()
+    assert p.cout * p.cin - int(inter["mask"].sum()) == p.cout * p.z   # achieved sparsity is Z/cin exactly
+
+
+def check_region_order(p, inter):
+    s, reg = inter["scores"], inter["regions"]
+    for t in range(p.n_tiles):
+        sd, s4, sp = s[t][reg[t] == oh.DENSE], s[t][reg[t] == oh.TWO_FOUR], s[t][reg[t] == oh.PRUNED]
+        assert sd.size == p.n_dense and s4.size == p.n_24 and sp.size == p.n_pruned
+        if sd.size and s4.size:
+            assert sd.min() >= s4.max()
+        if s4.size and sp.size:
+            assert s4.min() >= sp.max()
+        if sd.size and sp.size:
+            assert sd.min() >= sp.max()
+
+
+def check_24(p, packed, d, perm):
+    """Exactly two kept per group; the kept pair maximises retained importance."""
+    if p.groups == 0:
+        return
+    nib_all = []
+    for t in range(p.n_tiles):
+        for q in range(p.n_24_pad // 4):
+            kb, ql = divmod(q, 16)
+            nib = (packed["meta_24"][t, kb] >> np.uint64(4 * ql)) & np.uint64(0xF)
+            if q >= p.groups:
+                assert (nib == oh.PAD_NIBBLE).all()
+                assert (packed["val_24"][t, kb, :, 2 * ql:2 * ql + 2] == 0).all()
+                continue
+            nib_all.append(nib)
+            cols = packed["idx_24"][t, 4 * q:4 * q + 4]
+            rows = np.arange(t * p.tile_rows, (t + 1) * p.tile_rows)
+            a = d[np.ix_(rows, cols)].astype(np.float64)
+            i0, i1 = (nib & np.uint64(3)).astype(int), (nib >> np.uint64(2)).astype(int)
+            assert (i0 < i1).all()
+            best = np.max([a[:, u] + a[:, v] for u, v in itertools.combinations(range(4), 2)], axis=0)
+            got = a[np.arange(len(rows)), i0] + a[np.arange(len(rows)), i1]
+            assert np.array_equal(got, best)
+    u = np.unique(np.concatenate(nib_all)).tolist()
+    assert set(u) <= set(oh.LEGAL_NIBBLES)
+
+
+def test_invariants_random_small():
+    for seed in range(6):
+        rng = np.random.default_rng(100 + seed)
+        cin = 4 * int(rng.integers(8, 40))
+        t = float(rng.uniform(0.3, 0.9))
+        v = float(rng.uniform(max(0, 2 * t - 1), t))
+        w = synth.small(64, cin, 32, t, v, 3, seed)
+        p, packed, inter = run_pack(w)
+        check_sparsity(p, inter)
+        check_region_order(p, inter)
+        check_24(p, packed, w.importance.numpy(), w.perm.numpy())
+        assert np.array_equal(oh.unpack(packed, p), oh.masked_weight(bits_of(w.w_bf16), inter["mask"]))
+
+
+def test_workload_tiny_invariants():
+    w = synth.tiny()
+    p, packed, inter = run_pack(w)
+    check_sparsity(p, inter)
+    check_region_order(p, inter)
+    check_24(p, packed, w.importance.numpy(), w.perm.numpy())
+
+
+def test_regions_brute_force():
+    """Kept set = max-sum subset; dense set = max-sum subset of the kept ones (ties: lowest columns)."""
+    rng = np.random.default_rng(3)
+    for trial in range(40):
+        cin = 12
+        t = float(rng.choice([0.5, 0.625, 0.75]))
+        v = float(rng.uniform(max(0, 2 * t - 1), t))
+        p = oh.plan(16, cin, 16, t, v)
+        # integer-valued importance makes ties frequent
+        d = rng.integers(0, 3, size=(16, cin)).astype(np.float32)
+        s = oh.vector_scores(d, p)[0]
+        reg = oh.regions(s[None, :], p)[0]
+
+        def best_subset(cands, k):
+            best = None
+            for sub in itertools.combinations(sorted(cands), k):
+                key = (sum(s[list(sub)]), [-c for c in sub])
+                if best is None or key > best[0]:
+                    best = (key, sub)
+            return set(best[1])
+        kept = best_subset(range(cin), cin - p.n_pruned)
+        dense = best_subset(kept, p.n_dense)
+        assert set(np.nonzero(reg != oh.PRUNED)[0].tolist()) == kept
+        assert set(np.nonzero(reg == oh.DENSE)[0].tolist()) == dense
+
+
+def test_scores_brute_force():
+    rng = np.random.default_rng(5)
+    d = rng.random((32, 8), dtype=np.float32) * np.float32(1e3)
+    p = oh.plan(32, 8, 16, 0.5, 0.25)
+    s = oh.vector_scores(d, p)
+    for t in range(2):
+        for c in range(8):
+            acc = 0.0
+            for r in range(16):
+                acc += float(d[16 * t + r, c])
+            assert s[t, c] == acc
+
+
+def test_topk_special_case():
+    """t=0.5, v=0, identity perm, D=|W|: the mask is the plain 2:4 top-2 of the N:M article."""
+    w = synth.small(64, 128, 32, 0.5, 0.0, 2, 11, identity_perm=True)
+    p, packed, inter = run_pack(w)
+    assert p.n_24 == 128 and p.n_dense == 0 and p.n_pruned == 0
+    wf = w.w_bf16.to(torch.float32)
+    wr = wf.view(64, 32, 4)
+    _, top = torch.topk(wr.abs(), k=2, dim=-1)
+    ref = torch.zeros_like(wr).scatter_(-1, top, 1.0).view(64, 128).bool().numpy()
+    # Compare groups whose four magnitudes are distinct, so the library's unspecified
+    # tie order cannot matter; almost every group qualifies.
+    srt = np.sort(wr.abs().numpy(), axis=-1)
+    tie_free = (np.diff(srt, axis=-1) > 0).all(axis=-1)          # [64, 32]
+    assert tie_free.mean() > 0.95
+    got = inter["mask"].reshape(64, 32, 4)[tie_free]
+    assert np.array_equal(got, ref.reshape(64, 32, 4)[tie_free])
+
+
+def test_permutation_invariance():
+    """Relabelling input channels (W columns, D columns, X rows, perm) leaves Y unchanged."""
+    w = synth.small(128, 96, 32, 0.6, 0.3, 5, 21)
+    p, packed, inter = run_pack(w)
+    x = synth.as_f64(w.x_bf16)
+    y = oh.spmm(oh.unpack(packed, p), x)
+    rng = np.random.default_rng(1)
+    sig = rng.permutation(w.cin)
+    inv = np.argsort(sig)
+    wb2 = bits_of(w.w_bf16)[:, sig]
+    d2 = w.importance.numpy()[:, sig]
+    perm2 = inv[w.perm.numpy()]
+    packed2 = oh.pack(wb2, d2, perm2, p)
+    y2 = oh.spmm(oh.unpack(packed2, p), x[sig])
+    np.testing.assert_allclose(y2, y, rtol=1e-12, atol=1e-12 * np.abs(y).max())
+
+
+def test_no_24_region_independent_of_perm():
+    w = synth.small(64, 64, 32, 0.5, 0.5, 4, 2)
+    p, packed, inter = run_pack(w)
+    assert p.n_24 == 0
+    other = np.stack([np.random.default_rng(t).permutation(64) for t in range(2)])
+    packed2 = oh.pack(bits_of(w.w_bf16), w.importance.numpy(), other, p)
+    x = synth.as_f64(w.x_bf16)
+    assert np.array_equal(oh.spmm(oh.unpack(packed, p), x), oh.spmm(oh.unpack(packed2, p), x))
+
+
+def test_dense_special_case_matches_library_gemm():
+    w = synth.small(64, 64, 32, 0.0, 0.0, 7, 4)
+    p, packed, inter = run_pack(w)
+    assert p.n_dense == 64 and p.z == 0
+    x = synth.as_f64(w.x_bf16)
+    y = oh.spmm(oh.unpack(packed, p), x)
+    ref = torch.matmul(w.w_bf16.to(torch.float64), w.x_bf16.to(torch.float64)).numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-13, atol=1e-15)
+
+
+def test_gemm_brute_force():
+    w = synth.small(32, 16, 16, 0.5, 0.25, 3, 9)
+    p, packed, inter = run_pack(w)
+    wh = oh.unpack(packed, p)
+    x = synth.as_f64(w.x_bf16)
+    y = oh.spmm(wh, x)
+    for r in range(32):
+        for n in range(3):
+            ref = math.fsum(wh[r, c] * x[c, n] for c in range(16))
+            assert abs(y[r, n] - ref) <= 1e-14 * max(1.0, abs(ref))
+
+
+def test_pack_rejects_bad_inputs():
+    w = synth.small(64, 32, 32, 0.5, 0.25, 1, 0)
+    p = oh.plan(64, 32, 32, 0.5, 0.25)
+    bad = w.perm.numpy().copy()
+    bad[1, 0] = bad[1, 1]
+    with pytest.raises(oracle.OracleError):
+        oh.pack(bits_of(w.w_bf16), w.importance.numpy(), bad, p)
+    d = w.importance.numpy().copy()
+    d[3, 3] = -1.0
+    with pytest.raises(oracle.OracleError):
+        oh.pack(bits_of(w.w_bf16), d, w.perm.numpy(), p)
+    d[3, 3] = np.inf
+    with pytest.raises(oracle.OracleError):
+        oh.pack(bits_of(w.w_bf16), d, w.perm.numpy(), p)
+
+
+# --------------------------------------------------------------------------------------
+# Boundary search (FlexHiNM-GP notes, key design 1)
+# --------------------------------------------------------------------------------------
+
+def test_boundary_search_rule_and_grid():
+    """Early stop = last grid point before the first strict decrease, and near the grid max.
+
+    The FlexHiNM-GP notes claim the objective is concave (proof in an appendix
+    that is not on the page), which would make the early stop the grid argmax.
+    On these synthetic weights it is concave only up to wiggles of about 1e-4
+    relative near its plateau, so the check is the stopping rule itself plus a
+    bound on the gap to the full scan.
+    """
+    w = synth.draw("dps", 256, 704, 64, 0.7, None, 1, 5, n_outliers=35, importance="sq")
+    v, trace = oh.boundary_search(w.importance.numpy(), w.perm.numpy(), w.cout, w.cin, 64, 0.7)
+    grid = oh.boundary_grid(w.importance.numpy(), w.perm.numpy(), w.cout, w.cin, 64, 0.7)
+    assert trace[0][0] == 0.7 and trace == grid[:len(trace)]
+    k = next((i for i in range(len(grid) - 1) if grid[i + 1][1] < grid[i][1]), len(grid) - 1)
+    pv = oh.plan(w.cout, w.cin, 64, 0.7, v)
+    pk = oh.plan(w.cout, w.cin, 64, 0.7, grid[k][0])
+    assert (pv.n_dense, pv.n_24, pv.n_pruned) == (pk.n_dense, pk.n_24, pk.n_pruned)
+    assert v == pk.n_pruned / w.cin
+    # the snapped value re-plans to the same counts
+    assert oh.plan(w.cout, w.cin, 64, 0.7, v).n_24 == pv.n_24
+    best = max(r for _, r in grid)
+    assert grid[k][1] >= (1 - 1e-3) * best
+    # coarse concavity: the objective rises from v = t_s, then falls toward v = 2 t_s - 1
+    assert grid[0][1] < grid[k][1] and grid[-1][1] < grid[k][1]
+
+
+def test_boundary_first_group_never_loses():
+    """With one 2:4 group per tile, R_total cannot fall below its value at v_s = t_s.
+
+    The single group holds the two weakest dense vectors and the two strongest
+    pruned ones; keeping the top two of four per row retains at least what the
+    two dense vectors held.  A planted sign or index mistake breaks this.
+    """
+    rng = np.random.default_rng(17)
+    for trial in range(10):
+        cin, t = 64, 0.5
+        d = (rng.random((64, cin)) ** 3).astype(np.float32)
+        perm = np.stack([rng.permutation(cin)])
+        p0 = oh.plan(64, cin, 64, t, t)
+        p1 = oh.plan(64, cin, 64, t, t - 2 / cin)
+        assert p1.groups == 1
+        assert oh.retained_importance(d, perm, p1) >= oh.retained_importance(d, perm, p0)
+
+
+def test_retained_importance_brute_force():
+    w = synth.small(32, 16, 16, 0.5, 0.25, 1, 13, importance="sq")
+    p, packed, inter = run_pack(w)
+    d = w.importance.numpy().astype(np.float64)
+    m = inter["mask"]
+    # retained importance = sum of importance over kept entries (dense vectors entirely).
+    assert oh.retained_importance(w.importance.numpy(), w.perm.numpy(), p) == pytest.approx(
+        float(np.sum(d[m])), rel=1e-12)
+
+
+# --------------------------------------------------------------------------------------
+# Mutation tests: a planted mistake in the oracle must trip a pin.
+# --------------------------------------------------------------------------------------
+
+def _mut_regions_ascending(s, p):
+    reg = np.full((p.n_tiles, p.cin), oh.PRUNED, dtype=np.uint8)
+    for t in range(p.n_tiles):
+        order = np.argsort(s[t], kind="stable")          # wrong sign
+        reg[t, order[:p.n_dense]] = oh.DENSE
+        reg[t, order[p.n_dense:p.n_dense + p.n_24]] = oh.TWO_FOUR
+    return reg
+
+
+def _mut_select24_smallest(d, idx_s, p):
+    sel = np.zeros((p.cout, p.groups, 2), dtype=np.int64)
+    for t in range(p.n_tiles):
+        rows = slice(t * p.tile_rows, (t + 1) * p.tile_rows)
+        a = np.asarray(d, np.float32)[rows][:, idx_s[t, :p.n_24]].reshape(p.tile_rows, p.groups, 4)
+        sel[rows] = np.sort(np.argsort(a, axis=-1, kind="stable")[..., :2], axis=-1)
+    return sel
+
+
+def _mut_scores_drop_last_row(d, p):
+    d3 = np.asarray(d, np.float32).reshape(p.n_tiles, p.tile_rows, p.cin)
+    return d3[:, :-1, :].astype(np.float64).sum(axis=1)
+
+
+def _mut_index_lists_ignore_perm(reg, perm, p):
+    ident = np.tile(np.arange(p.cin), (p.n_tiles, 1))
+    return oracle.hinm.__dict__["_orig_index_lists"](reg, ident, p)
+
+
+@pytest.mark.parametrize("name,fn", [
+    ("regions", _mut_regions_ascending),
+    ("select24", _mut_select24_smallest),
+    ("vector_scores", _mut_scores_drop_last_row),
+])
+def test_mutations_are_caught(monkeypatch, name, fn):
+    monkeypatch.setattr(oh, name, fn)
+    caught = False
+    try:
+        test_invariants_random_small()
+        test_handworked_fixture()
+        test_scores_brute_force()
+    except AssertionError:
+        caught = True
+    assert caught, f"planted mistake in {name} went unnoticed"
+
+
+def test_mutation_perm_ignored_is_caught(monkeypatch):
+    monkeypatch.setattr(oh, "_orig_index_lists", oh.index_lists, raising=False)
+    monkeypatch.setattr(oh, "index_lists", _mut_index_lists_ignore_perm)
+    with pytest.raises(AssertionError):
+        test_handworked_fixture()
+
+
+def test_mutation_transposed_product_is_caught(monkeypatch):
+    monkeypatch.setattr(oh, "spmm", lambda w, x: (np.asarray(x, np.float64).T @ np.asarray(w, np.float64).T).T[:, ::-1])
+    with pytest.raises(AssertionError):
+        test_gemm_brute_force()
