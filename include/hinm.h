@@ -1,0 +1,179 @@
+/*
+ * hinm.h - C ABI of libhinm: hierarchical N:M (HiNM) sparse weight x dense
+ * activation product for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (FlexHiNM-GP paper notes, one-line summary, "整体框架" and key
+ * designs 1, 2 and 4): every output-channel tile of a weight W [cout x cin] is
+ * cut into three regions of whole column vectors - dense (4:4), 2:4 (top two of
+ * every four consecutive entries along the input dimension, 2-bit positions as
+ * in the 2:4 structured-sparsity article, section 3) and pruned (0:4).  The
+ * sizes of the regions follow the closed form
+ *     t_s = v_s + (1 - v_s) * p_s / 2,   p_s = 2 (t_s - v_s) / (1 - v_s)
+ * where t_s is the target sparsity and v_s the pruned-vector fraction.  The
+ * input channels of each tile are permuted (PermLLM summary, problem
+ * definition: W_hat = W P); the product gathers rows of X through per-tile
+ * kept-vector indices that already include the permutation, so the result is
+ *     Y = (W (.) M) X,    Y [cout x batch], X [cin x batch].
+ *
+ * Conventions shared by every entry point
+ *   - All matrices are row-major.  W, X and Y hold bf16 values (raw 16-bit
+ *     patterns, passed as void*), importance holds fp32.  Accumulation is fp32.
+ *   - Device pointers are device memory owned by the caller; the library never
+ *     allocates or frees device memory and keeps no device state.  Host
+ *     pointers are marked "host".
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   - Functions return a hinm_status and never throw.  On failure a message is
+ *     available from hinm_last_error() in the calling thread.  Argument errors
+ *     are detected on the host before anything is launched.
+ *   - Functions are re-entrant; calls that share output or workspace buffers
+ *     must not overlap in time.
+ */
+#ifndef HINM_H_
+#define HINM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HINM_ABI_VERSION 1
+
+/* K-block sizes of the packed layout: 32 dense columns; 64 positions
+ * (16 groups of 4) of the 2:4 region. */
+#define HINM_KB_DENSE 32
+#define HINM_KB_24 64
+
+typedef enum {
+  HINM_OK = 0,
+  HINM_EINVAL = 1,      /* null pointer, non-finite or out-of-range t_s / v_s        */
+  HINM_ESHAPE = 2,      /* sizes: cout % tile_rows, cin % 4, tile_rows % 16, ld < n  */
+  HINM_EPERM = 3,       /* a perm row is not a permutation of 0..cin-1 (device check) */
+  HINM_EIMPORTANCE = 4, /* importance has a negative or non-finite entry (device)    */
+  HINM_EALIGN = 5,      /* a pointer is not aligned as documented                    */
+  HINM_EWORKSPACE = 6,  /* workspace missing or smaller than required                */
+  HINM_EHIP = 7,        /* a HIP runtime call or kernel launch failed                */
+  HINM_EDEVICE = 8      /* no usable gfx950 device                                   */
+} hinm_status;
+
+/* Region counts and buffer sizes of one weight.  Plain data, computed on the
+ * host by hinm_plan; identical in every output tile. */
+typedef struct {
+  int32_t abi_version;  /* HINM_ABI_VERSION                                          */
+  int32_t cout, cin;    /* W is cout x cin                                           */
+  int32_t tile_rows;    /* rows per output-channel tile (R)                          */
+  int32_t n_tiles;      /* cout / tile_rows                                          */
+  int32_t z;            /* zeros per row: floor(t_s * cin + 1/2)                     */
+  int32_t groups;       /* 2:4 groups per tile row: n_24 / 4                         */
+  int32_t n_dense;      /* dense (4:4) vectors per tile                              */
+  int32_t n_24;         /* 2:4 vectors per tile                                      */
+  int32_t n_pruned;     /* pruned (0:4) vectors per tile                             */
+  int32_t n_dense_pad;  /* n_dense rounded up to HINM_KB_DENSE                       */
+  int32_t n_24_pad;     /* n_24 rounded up to HINM_KB_24                             */
+  int32_t kb_dense;     /* HINM_KB_DENSE                                             */
+  int32_t kb_24;        /* HINM_KB_24                                                */
+  double t_s, v_s;      /* the arguments                                             */
+  double p_s;           /* 2 (t_s - v_s) / (1 - v_s), informational                  */
+  int64_t bytes_val_dense; /* n_tiles * n_dense_pad * tile_rows * 2                  */
+  int64_t bytes_idx_dense; /* n_tiles * n_dense_pad * 4                              */
+  int64_t bytes_val_24;    /* n_tiles * (n_24_pad / 2) * tile_rows * 2               */
+  int64_t bytes_meta_24;   /* n_tiles * (n_24_pad / 64) * tile_rows * 8              */
+  int64_t bytes_idx_24;    /* n_tiles * n_24_pad * 4                                 */
+} hinm_plan_t;
+
+/* A packed weight: the plan plus five caller-owned device buffers (each at
+ * least 16-byte aligned, sized by the plan; a buffer of size 0 may be NULL).
+ *   val_dense  bf16   [n_tiles][n_dense_pad/32][tile_rows][32]
+ *              val_dense[t][kb][r][k] = W[t*R + r][idx_dense[t][32*kb + k]]
+ *   idx_dense  int32  [n_tiles][n_dense_pad]   dense columns in permuted order
+ *   val_24     bf16   [n_tiles][n_24_pad/64][tile_rows][32]
+ *              two kept values per group, group g of block kb at [2g, 2g+1],
+ *              lower in-group position first
+ *   meta_24    uint64 [n_tiles][n_24_pad/64][tile_rows]
+ *              group g's nibble (i0 | i1 << 2, i0 < i1, positions 0..3 within
+ *              the group) at bits 4g..4g+3
+ *   idx_24     int32  [n_tiles][n_24_pad]      2:4 columns in permuted order;
+ *              group q of a tile is idx_24[t][4q .. 4q+3]
+ * Padding: indices -1, values +0, nibbles 0x4. */
+typedef struct {
+  hinm_plan_t plan;
+  void* val_dense;
+  int32_t* idx_dense;
+  void* val_24;
+  uint64_t* meta_24;
+  int32_t* idx_24;
+} hinm_packed_t;
+
+/* Library ABI version (HINM_ABI_VERSION of the build). */
+int hinm_abi_version(void);
+
+/* Region counts for a cout x cin weight (FlexHiNM-GP notes, key design 1).
+ * Host only, touches no device.  Requires cout, cin > 0, tile_rows % 16 == 0,
+ * cout % tile_rows == 0, cin % 4 == 0 (pad the input dimension as the N:M
+ * article's section 2 does), 0 <= t_s < 1 and
+ * max(0, 2 t_s - 1) <= v_s <= t_s, so that p_s lies in [0, 1].
+ * Counts: z = floor(t_s*cin + 1/2); g = floor((t_s - v_s)*cin/2 + 1/2)
+ * clamped to [0, floor(min(z, cin - z)/2)]; n_24 = 4g; n_pruned = z - 2g;
+ * n_dense = cin - z - 2g.  Every row keeps cin - z entries.
+ * `out` (host) receives the plan.  Errors: HINM_EINVAL, HINM_ESHAPE. */
+int hinm_plan(int64_t cout, int64_t cin, int32_t tile_rows, double t_s, double v_s,
+              hinm_plan_t* out);
+
+/* Device scratch that hinm_pack needs, in bytes (host only). */
+int hinm_pack_workspace_bytes(const hinm_plan_t* plan, size_t* bytes);
+
+/* Pack a weight (FlexHiNM-GP notes, key designs 1, 2 and 4; 2:4 article,
+ * section 3; PermLLM summary, mask on the permuted importance):
+ *   1. score every column vector of every tile: the float64 sum of its
+ *      importance over the tile's rows, rows in ascending order from +0.0;
+ *   2. rank columns by (-score, column): the first n_dense are dense, the
+ *      next n_24 are 2:4, the rest pruned;
+ *   3. list dense and 2:4 columns in the tile's permuted order perm[t][0..];
+ *   4. in every 2:4 group of 4 listed columns and every row keep the two
+ *      entries with the largest importance (ties: lower position);
+ *   5. write the packed buffers of `out` (layout above).
+ * Inputs (device): w_bf16 [cout][ldw], importance fp32 [cout][ldi] (finite,
+ * >= 0), perm int32 [n_tiles][cin] or NULL for the identity; perm[t][j] is
+ * the original column at position j of tile t.  `plan` (host) comes from
+ * hinm_plan; `out` (host) holds the plan copy and the output pointers, which
+ * the caller allocates from the plan's sizes.  workspace (device, 256-byte
+ * aligned) of hinm_pack_workspace_bytes bytes.
+ * Synchronous: returns after the work on `stream` has finished, because a bad
+ * perm or importance is detected on the device (HINM_EPERM, HINM_EIMPORTANCE;
+ * the outputs are then unspecified).  Other errors: HINM_EINVAL, HINM_ESHAPE,
+ * HINM_EALIGN, HINM_EWORKSPACE, HINM_EHIP. */
+int hinm_pack(const hinm_plan_t* plan, const void* w_bf16, int64_t ldw, const float* importance,
+              int64_t ldi, const int32_t* perm, hinm_packed_t* out, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/* Device scratch that hinm_spmm needs for a batch, in bytes (host only).
+ * Zero when the product runs without a split of the reduction dimension. */
+int hinm_spmm_workspace_bytes(const hinm_plan_t* plan, int64_t batch, size_t* bytes);
+
+/* Y = (W (.) M) X for a packed weight (FlexHiNM-GP notes, key design 4: the
+ * kernel gathers X rows through the precomputed indices, with the input
+ * permutation folded in).  X (device) bf16 [cin][ldx], ldx >= batch; Y
+ * (device) bf16 [cout][ldy], ldy >= batch, every element of Y[:, 0:batch] is
+ * written (rounded to nearest even from the fp32 accumulator), nothing else.
+ * X and Y must be 2-byte aligned; 16-byte aligned X with ldx % 8 == 0 takes
+ * the vector-load path.  workspace (device, 256-byte aligned) of at least
+ * hinm_spmm_workspace_bytes(plan, batch) bytes, may be NULL when that is 0.
+ * batch == 0 is a no-op.  Asynchronous on `stream`; no host synchronisation,
+ * no atomics: the same inputs give bitwise-identical Y.
+ * Errors (host-side checks only): HINM_EINVAL, HINM_ESHAPE, HINM_EALIGN,
+ * HINM_EWORKSPACE, HINM_EHIP (launch failure). */
+int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_t batch, int64_t ldx,
+              void* y_bf16, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* hinm_status_str(int status);
+
+/* Detail of the last failure in the calling thread ("" if none). */
+const char* hinm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HINM_H_ */

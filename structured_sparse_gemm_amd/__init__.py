@@ -1,0 +1,261 @@
+"""Python binding of libhinm: hierarchical N:M sparse weight x dense activation on MI355X.
+
+Argument marshalling only.  Every step of the pack and of the product runs in
+the HIP kernels of ``libhinm.so``; PyTorch supplies device memory and the
+current HIP stream.  If the library is not built, every call raises: there is
+no fallback path.
+
+    packed = pack(w_bf16, importance, tile_rows, t_s, v_s, perm=None)
+    y = spmm(packed, x_bf16)          # y = (W (.) M) x, bf16 [cout, batch]
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhinm.so")
+
+HINM_ABI_VERSION = 1
+STATUS = {0: "HINM_OK", 1: "HINM_EINVAL", 2: "HINM_ESHAPE", 3: "HINM_EPERM", 4: "HINM_EIMPORTANCE",
+          5: "HINM_EALIGN", 6: "HINM_EWORKSPACE", 7: "HINM_EHIP", 8: "HINM_EDEVICE"}
+
+# Every symbol the C ABI exports (include/hinm.h).
+EXPORTS = ("hinm_abi_version", "hinm_plan", "hinm_pack_workspace_bytes", "hinm_pack",
+           "hinm_spmm_workspace_bytes", "hinm_spmm", "hinm_status_str", "hinm_last_error")
+
+
+class HinmError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+
+
+class PlanT(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32), ("cout", ctypes.c_int32), ("cin", ctypes.c_int32),
+                ("tile_rows", ctypes.c_int32), ("n_tiles", ctypes.c_int32), ("z", ctypes.c_int32),
+                ("groups", ctypes.c_int32), ("n_dense", ctypes.c_int32), ("n_24", ctypes.c_int32),
+                ("n_pruned", ctypes.c_int32), ("n_dense_pad", ctypes.c_int32), ("n_24_pad", ctypes.c_int32),
+                ("kb_dense", ctypes.c_int32), ("kb_24", ctypes.c_int32),
+                ("t_s", ctypes.c_double), ("v_s", ctypes.c_double), ("p_s", ctypes.c_double),
+                ("bytes_val_dense", ctypes.c_int64), ("bytes_idx_dense", ctypes.c_int64),
+                ("bytes_val_24", ctypes.c_int64), ("bytes_meta_24", ctypes.c_int64),
+                ("bytes_idx_24", ctypes.c_int64)]
+
+
+class PackedT(ctypes.Structure):
+    _fields_ = [("plan", PlanT), ("val_dense", ctypes.c_void_p), ("idx_dense", ctypes.c_void_p),
+                ("val_24", ctypes.c_void_p), ("meta_24", ctypes.c_void_p), ("idx_24", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Loads libhinm.so (built in-tree); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                              "python structured_sparse_gemm_amd/build.py")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, S, I64, I32, D, VP = (ctypes.POINTER(PlanT), ctypes.c_size_t, ctypes.c_int64, ctypes.c_int32,
+                                 ctypes.c_double, ctypes.c_void_p)
+        sig = {
+            "hinm_abi_version": ([], ctypes.c_int),
+            "hinm_plan": ([I64, I64, I32, D, D, P], ctypes.c_int),
+            "hinm_pack_workspace_bytes": ([P, ctypes.POINTER(S)], ctypes.c_int),
+            "hinm_pack": ([P, VP, I64, VP, I64, VP, ctypes.POINTER(PackedT), VP, S, VP], ctypes.c_int),
+            "hinm_spmm_workspace_bytes": ([P, I64, ctypes.POINTER(S)], ctypes.c_int),
+            "hinm_spmm": ([ctypes.POINTER(PackedT), VP, I64, I64, VP, I64, VP, S, VP], ctypes.c_int),
+            "hinm_status_str": ([ctypes.c_int], ctypes.c_char_p),
+            "hinm_last_error": ([], ctypes.c_char_p),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(lib, name)
+            f.argtypes, f.restype = args, res
+        if lib.hinm_abi_version() != HINM_ABI_VERSION:
+            raise ImportError("libhinm ABI version mismatch")
+        _lib = lib
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise HinmError(status, library().hinm_last_error().decode())
+
+
+@dataclasses.dataclass(frozen=True)
+class Plan:
+    cout: int
+    cin: int
+    tile_rows: int
+    n_tiles: int
+    z: int
+    groups: int
+    n_dense: int
+    n_24: int
+    n_pruned: int
+    n_dense_pad: int
+    n_24_pad: int
+    t_s: float
+    v_s: float
+    p_s: float
+    bytes_val_dense: int
+    bytes_idx_dense: int
+    bytes_val_24: int
+    bytes_meta_24: int
+    bytes_idx_24: int
+    raw: PlanT = dataclasses.field(repr=False, compare=False)
+
+    @property
+    def packed_bytes(self) -> int:
+        return (self.bytes_val_dense + self.bytes_idx_dense + self.bytes_val_24 + self.bytes_meta_24
+                + self.bytes_idx_24)
+
+
+def plan(cout: int, cin: int, tile_rows: int, t_s: float, v_s: float) -> Plan:
+    """Region counts (host only, needs no GPU)."""
+    raw = PlanT()
+    _check(library().hinm_plan(cout, cin, tile_rows, float(t_s), float(v_s), ctypes.byref(raw)))
+    kw = {f.name: getattr(raw, f.name) for f in dataclasses.fields(Plan) if f.name != "raw"}
+    return Plan(raw=raw, **kw)
+
+
+@dataclasses.dataclass
+class HinmPacked:
+    """A packed weight: the plan and its five device buffers (torch tensors)."""
+
+    plan: Plan
+    val_dense: torch.Tensor   # int16 bits of bf16 [T, n_dense_pad/32, R, 32]
+    idx_dense: torch.Tensor   # int32 [T, n_dense_pad]
+    val_24: torch.Tensor      # int16 bits of bf16 [T, n_24_pad/64, R, 32]
+    meta_24: torch.Tensor     # int64 bits of uint64 [T, n_24_pad/64, R]
+    idx_24: torch.Tensor      # int32 [T, n_24_pad]
+
+    def struct(self) -> PackedT:
+        def ptr(t):
+            return t.data_ptr() if t.numel() else None
+        return PackedT(self.plan.raw, ptr(self.val_dense), ptr(self.idx_dense), ptr(self.val_24),
+                       ptr(self.meta_24), ptr(self.idx_24))
+
+    @property
+    def device(self) -> torch.device:
+        return self.idx_24.device
+
+    def nbytes(self) -> int:
+        return self.plan.packed_bytes
+
+
+def _stream_ptr(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _empty(shape, dtype, device):
+    # 256-byte aligned by the caching allocator; zero-size buffers stay empty.
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
+def pack_workspace_bytes(p: Plan) -> int:
+    n = ctypes.c_size_t()
+    _check(library().hinm_pack_workspace_bytes(ctypes.byref(p.raw), ctypes.byref(n)))
+    return n.value
+
+
+def alloc_packed(p: Plan, device) -> HinmPacked:
+    T, R = p.n_tiles, p.tile_rows
+    return HinmPacked(
+        p,
+        _empty((T, p.n_dense_pad // 32, R, 32), torch.int16, device),
+        _empty((T, p.n_dense_pad), torch.int32, device),
+        _empty((T, p.n_24_pad // 64, R, 32), torch.int16, device),
+        _empty((T, p.n_24_pad // 64, R), torch.int64, device),
+        _empty((T, p.n_24_pad), torch.int32, device))
+
+
+def pack(w: torch.Tensor, importance: torch.Tensor, tile_rows: int, t_s: float, v_s: float,
+         perm: Optional[torch.Tensor] = None) -> HinmPacked:
+    """Packs a bf16 weight [cout, cin] on its device (synchronous).
+
+    importance: fp32 [cout, cin] (finite, >= 0); perm: int32 [cout/tile_rows, cin]
+    or None for the identity, perm[t][j] = original column at position j of tile t.
+    """
+    if w.dtype != torch.bfloat16 or w.dim() != 2 or not w.is_cuda:
+        raise ValueError("w must be a 2-D bf16 CUDA tensor")
+    if importance.dtype != torch.float32 or importance.shape != w.shape or importance.device != w.device:
+        raise ValueError("importance must be fp32 with the shape and device of w")
+    if w.stride(1) != 1 or importance.stride(1) != 1:
+        raise ValueError("w and importance must have unit column stride")
+    cout, cin = w.shape
+    p = plan(cout, cin, tile_rows, t_s, v_s)
+    if perm is not None:
+        if perm.dtype != torch.int32 or perm.shape != (p.n_tiles, cin) or perm.device != w.device:
+            raise ValueError(f"perm must be int32 [{p.n_tiles}, {cin}] on the device of w")
+        perm = perm.contiguous()
+    out = alloc_packed(p, w.device)
+    ws = torch.empty(pack_workspace_bytes(p), dtype=torch.uint8, device=w.device)
+    st = out.struct()
+    with torch.cuda.device(w.device):
+        _check(library().hinm_pack(ctypes.byref(p.raw), w.data_ptr(), w.stride(0), importance.data_ptr(),
+                                   importance.stride(0), perm.data_ptr() if perm is not None else None,
+                                   ctypes.byref(st), ws.data_ptr(), ws.numel(), _stream_ptr(w.device)))
+    return out
+
+
+def spmm_workspace_bytes(p: Plan, batch: int) -> int:
+    n = ctypes.c_size_t()
+    _check(library().hinm_spmm_workspace_bytes(ctypes.byref(p.raw), batch, ctypes.byref(n)))
+    return n.value
+
+
+_ws_cache = {}
+
+
+def _workspace(device: torch.device, nbytes: int) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    key = (device.type, device.index)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+def spmm(packed: HinmPacked, x: torch.Tensor, out: Optional[torch.Tensor] = None,
+         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = (W (.) M) X: x bf16 [cin, batch] (row stride >= batch), returns bf16 [cout, batch].
+
+    Asynchronous on the current stream.  ``workspace`` (uint8, device) may be
+    given; otherwise a per-device buffer is reused (calls on one device that
+    use it must not overlap on different streams).
+    """
+    p = packed.plan
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[0] != p.cin or x.device != packed.device:
+        raise ValueError(f"x must be bf16 [{p.cin}, batch] on {packed.device}")
+    if x.stride(1) != 1:
+        raise ValueError("x must have unit column stride")
+    batch = x.shape[1]
+    if out is None:
+        out = torch.empty((p.cout, batch), dtype=torch.bfloat16, device=x.device)
+    elif out.dtype != torch.bfloat16 or out.shape != (p.cout, batch) or out.stride(1) != 1 or out.device != x.device:
+        raise ValueError(f"out must be bf16 [{p.cout}, {batch}] with unit column stride on {x.device}")
+    need = spmm_workspace_bytes(p, batch)
+    if workspace is None:
+        workspace = _workspace(x.device, need)
+    st = packed.struct()
+    with torch.cuda.device(x.device):
+        _check(library().hinm_spmm(ctypes.byref(st), x.data_ptr(), batch, max(x.stride(0), batch) if batch else 0,
+                                   out.data_ptr(), max(out.stride(0), batch) if batch else 0,
+                                   workspace.data_ptr() if workspace is not None else None,
+                                   workspace.numel() if workspace is not None else 0, _stream_ptr(x.device)))
+    return out
+
+
+__all__ = ["HinmError", "HinmPacked", "Plan", "plan", "pack", "spmm", "alloc_packed", "pack_workspace_bytes",
+           "spmm_workspace_bytes", "library", "LIB_PATH", "EXPORTS"]

@@ -1,0 +1,41 @@
+// Internal helpers shared by the translation units of libhinm (not installed).
+#ifndef HINM_INTERNAL_H_
+#define HINM_INTERNAL_H_
+
+#include <stdarg.h>
+#include <stdint.h>
+
+#include "hinm.h"
+
+namespace hinm {
+
+// Records a printf-style message for hinm_last_error() in this thread and
+// returns `status`, so call sites read `return fail(HINM_ESHAPE, "...")`.
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+// Host-side validation of a plan handed back by a caller.
+int check_plan(const hinm_plan_t* p);
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Split of the reduction dimension chosen for a batch (1 = no split) and the
+// token-block width; shared by hinm_spmm and hinm_spmm_workspace_bytes so the
+// workspace size always matches what the launch uses.
+struct SpmmShape {
+  int nt;          // tokens per workgroup
+  int n_tblocks;   // token blocks
+  int n_rblocks;   // 64-row blocks per tile
+  int n_kunits;    // K work units per tile (dense block = 1, 2:4 block = 2)
+  int splits;      // K splits (>= 1)
+  int64_t ws_bytes;
+};
+SpmmShape spmm_shape(const hinm_plan_t* p, int64_t batch);
+
+// Current device is a gfx950 part (checked once per device); HINM_OK or
+// HINM_EDEVICE / HINM_EHIP with the message recorded.
+int ensure_device();
+
+}  // namespace hinm
+
+#endif  // HINM_INTERNAL_H_

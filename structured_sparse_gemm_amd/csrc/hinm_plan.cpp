@@ -1,0 +1,159 @@
+// Host-only part of libhinm: region counts, status strings, error text.
+// Makes no HIP call, so it runs (and is tested) on a host without a GPU.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "hinm_internal.h"
+
+static_assert(sizeof(hinm_plan_t) == 120, "hinm_plan_t must have no padding");
+
+namespace hinm {
+
+static thread_local char g_last_error[512];
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+int check_plan(const hinm_plan_t* p) {
+  if (!p) return fail(HINM_EINVAL, "plan is NULL");
+  if (p->abi_version != HINM_ABI_VERSION)
+    return fail(HINM_EINVAL, "plan has abi_version %d, library is %d", p->abi_version, HINM_ABI_VERSION);
+  hinm_plan_t q;
+  int st = hinm_plan(p->cout, p->cin, p->tile_rows, p->t_s, p->v_s, &q);
+  if (st != HINM_OK) return st;
+  if (memcmp(&q, p, sizeof(q)) != 0) return fail(HINM_EINVAL, "plan fields do not match hinm_plan of its arguments");
+  return HINM_OK;
+}
+
+}  // namespace hinm
+
+using hinm::fail;
+
+extern "C" int hinm_abi_version(void) { return HINM_ABI_VERSION; }
+
+// FlexHiNM-GP notes, key design 1: t_s = v_s + (1 - v_s) p_s / 2.  The counts
+// are rounded half-up so that every row keeps exactly cin - z entries:
+// n_pruned + n_24 / 2 = z.
+extern "C" int hinm_plan(int64_t cout, int64_t cin, int32_t tile_rows, double t_s, double v_s,
+                         hinm_plan_t* out) {
+  hinm::clear_error();
+  if (!out) return fail(HINM_EINVAL, "out is NULL");
+  if (cout <= 0 || cin <= 0 || tile_rows <= 0)
+    return fail(HINM_ESHAPE, "sizes must be positive (cout=%lld cin=%lld tile_rows=%d)",
+                (long long)cout, (long long)cin, tile_rows);
+  if (cout > INT32_MAX || cin > INT32_MAX) return fail(HINM_ESHAPE, "cout and cin must fit in int32");
+  if (tile_rows % 16 != 0) return fail(HINM_ESHAPE, "tile_rows=%d is not a multiple of 16", tile_rows);
+  if (cout % tile_rows != 0)
+    return fail(HINM_ESHAPE, "cout=%lld is not a multiple of tile_rows=%d", (long long)cout, tile_rows);
+  if (cin % 4 != 0) return fail(HINM_ESHAPE, "cin=%lld is not a multiple of 4", (long long)cin);
+  if (!isfinite(t_s) || !isfinite(v_s)) return fail(HINM_EINVAL, "t_s and v_s must be finite");
+  if (!(t_s >= 0.0 && t_s < 1.0)) return fail(HINM_EINVAL, "t_s=%g is outside [0, 1)", t_s);
+  double lo = 2.0 * t_s - 1.0;
+  if (lo < 0.0) lo = 0.0;
+  if (!(v_s >= lo && v_s <= t_s))
+    return fail(HINM_EINVAL, "v_s=%g is outside [max(0, 2 t_s - 1), t_s] = [%g, %g]", v_s, lo, t_s);
+  const int64_t z = (int64_t)floor(t_s * (double)cin + 0.5);
+  int64_t g = (int64_t)floor((t_s - v_s) * (double)cin / 2.0 + 0.5);
+  const int64_t gmax = (z < cin - z ? z : cin - z) / 2;
+  if (g < 0) g = 0;
+  if (g > gmax) g = gmax;
+  hinm_plan_t p;
+  memset(&p, 0, sizeof(p));
+  p.abi_version = HINM_ABI_VERSION;
+  p.cout = (int32_t)cout;
+  p.cin = (int32_t)cin;
+  p.tile_rows = tile_rows;
+  p.n_tiles = (int32_t)(cout / tile_rows);
+  p.z = (int32_t)z;
+  p.groups = (int32_t)g;
+  p.n_24 = (int32_t)(4 * g);
+  p.n_pruned = (int32_t)(z - 2 * g);
+  p.n_dense = (int32_t)(cin - z - 2 * g);
+  p.n_dense_pad = (p.n_dense + HINM_KB_DENSE - 1) / HINM_KB_DENSE * HINM_KB_DENSE;
+  p.n_24_pad = (p.n_24 + HINM_KB_24 - 1) / HINM_KB_24 * HINM_KB_24;
+  p.kb_dense = HINM_KB_DENSE;
+  p.kb_24 = HINM_KB_24;
+  p.t_s = t_s;
+  p.v_s = v_s;
+  p.p_s = 2.0 * (t_s - v_s) / (1.0 - v_s);
+  const int64_t T = p.n_tiles, R = tile_rows;
+  p.bytes_val_dense = T * p.n_dense_pad * R * 2;
+  p.bytes_idx_dense = T * p.n_dense_pad * 4;
+  p.bytes_val_24 = T * (p.n_24_pad / 2) * R * 2;
+  p.bytes_meta_24 = T * (p.n_24_pad / HINM_KB_24) * R * 8;
+  p.bytes_idx_24 = T * p.n_24_pad * 4;
+  *out = p;
+  return HINM_OK;
+}
+
+extern "C" const char* hinm_status_str(int status) {
+  switch (status) {
+    case HINM_OK: return "HINM_OK";
+    case HINM_EINVAL: return "HINM_EINVAL: invalid argument";
+    case HINM_ESHAPE: return "HINM_ESHAPE: unsupported or inconsistent sizes";
+    case HINM_EPERM: return "HINM_EPERM: perm row is not a permutation";
+    case HINM_EIMPORTANCE: return "HINM_EIMPORTANCE: importance is negative or not finite";
+    case HINM_EALIGN: return "HINM_EALIGN: pointer misaligned";
+    case HINM_EWORKSPACE: return "HINM_EWORKSPACE: workspace missing or too small";
+    case HINM_EHIP: return "HINM_EHIP: HIP runtime error";
+    case HINM_EDEVICE: return "HINM_EDEVICE: no usable device";
+    default: return "HINM_E?: unknown status";
+  }
+}
+
+extern "C" const char* hinm_last_error(void) { return hinm::g_last_error; }
+
+// Work decomposition of the product.  Decode-sized batches have too few
+// (tile, row block, token block) triples to fill 256 compute units, so the
+// reduction dimension is split; partial sums then go through the workspace.
+namespace hinm {
+SpmmShape spmm_shape(const hinm_plan_t* p, int64_t batch) {
+  SpmmShape s;
+  s.nt = batch <= 16 ? 16 : (batch <= 32 ? 32 : 64);
+  s.n_tblocks = (int)((batch + s.nt - 1) / s.nt);
+  s.n_rblocks = (p->tile_rows + 63) / 64;
+  s.n_kunits = p->n_dense_pad / HINM_KB_DENSE + 2 * (p->n_24_pad / HINM_KB_24);
+  const int64_t wgs = (int64_t)p->n_tiles * s.n_rblocks * s.n_tblocks;
+  int splits = 1;
+  const int64_t target = 1024;  // about four workgroups per compute unit
+  if (wgs < target && s.n_kunits > 1) {
+    splits = (int)((target + wgs - 1) / wgs);
+    int max_splits = s.n_kunits / 4;  // keep at least ~4 K units per split
+    if (max_splits < 1) max_splits = 1;
+    if (splits > max_splits) splits = max_splits;
+    if (splits > 32) splits = 32;
+  }
+  s.splits = splits;
+  s.ws_bytes = splits > 1 ? (int64_t)splits * p->cout * ((batch + 15) / 16 * 16) * 4 : 0;
+  return s;
+}
+}  // namespace hinm
+
+extern "C" int hinm_pack_workspace_bytes(const hinm_plan_t* plan, size_t* bytes) {
+  hinm::clear_error();
+  int st = hinm::check_plan(plan);
+  if (st) return st;
+  if (!bytes) return fail(HINM_EINVAL, "bytes is NULL");
+  const size_t tc = (size_t)plan->n_tiles * plan->cin;
+  // [flag 256 B][scores fp64 T*cin][regions u8 T*cin, rounded to 256]
+  *bytes = 256 + tc * 8 + (tc + 255) / 256 * 256;
+  return HINM_OK;
+}
+
+extern "C" int hinm_spmm_workspace_bytes(const hinm_plan_t* plan, int64_t batch, size_t* bytes) {
+  hinm::clear_error();
+  int st = hinm::check_plan(plan);
+  if (st) return st;
+  if (!bytes) return fail(HINM_EINVAL, "bytes is NULL");
+  if (batch < 0) return fail(HINM_ESHAPE, "batch=%lld is negative", (long long)batch);
+  *bytes = batch == 0 ? 0 : (size_t)hinm::spmm_shape(plan, batch).ws_bytes;
+  return HINM_OK;
+}

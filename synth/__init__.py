@@ -45,6 +45,7 @@ class Workload:
     perm: torch.Tensor            # [cout // tile_rows, cin] int32 (CPU)
     x_bf16: torch.Tensor          # [cin, batch] bf16 (CPU)
     w_f32: Optional[torch.Tensor] = None  # the unrounded weight when drawn in fp32
+    x_f32: Optional[torch.Tensor] = None  # the unrounded activations when drawn in fp32
 
     @property
     def n_tiles(self) -> int:
@@ -84,10 +85,11 @@ def draw(name: str, cout: int, cin: int, tile_rows: int, t_s: float, v_s: Option
         imp = src * src
     else:
         raise ValueError(importance)
-    xb = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+    x32 = torch.from_numpy(x.astype(np.float32))
+    xb = x32.to(torch.bfloat16)
     return Workload(name, cout, cin, tile_rows, t_s, v_s, batch, wb.contiguous(),
                     imp.contiguous(), torch.from_numpy(perm).contiguous(), xb.contiguous(),
-                    w32 if importance_from_f32 else None)
+                    w32 if importance_from_f32 else None, x32 if importance_from_f32 else None)
 
 
 # The five workload families.  Sizes follow LLaMA-7B's linear layers

@@ -1,0 +1,141 @@
+"""The C ABI on a host without a GPU: exports, region counts, host-side errors."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle.hinm as oh
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+hinm = pytest.importorskip("structured_sparse_gemm_amd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hinm.LIB_PATH):
+        pytest.skip("libhinm.so is not built (run __graft_entry__.build())")
+    return hinm.library()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "hinm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hinm_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(hinm.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.hinm_abi_version() == 1
+
+
+@pytest.mark.parametrize("shape", [(128, 256, 32, 0.75, 0.5), (4096, 4096, 64, 0.5, 0.25),
+                                   (11008, 4096, 64, 0.75, 0.55), (4096, 11008, 64, 0.75, 0.55),
+                                   (4096, 11008, 64, 0.6, 0.4), (64, 4, 16, 0.5, 0.0), (16, 8, 16, 0.0, 0.0)])
+def test_plan_matches_oracle(lib, shape):
+    p = hinm.plan(*shape)
+    o = oh.plan(*shape)
+    for f in ("cout", "cin", "tile_rows", "n_tiles", "z", "groups", "n_dense", "n_24", "n_pruned",
+              "n_dense_pad", "n_24_pad"):
+        assert getattr(p, f) == getattr(o, f), f
+    T, R = o.n_tiles, o.tile_rows
+    assert p.bytes_val_dense == T * o.n_dense_pad * R * 2
+    assert p.bytes_val_24 == T * o.n_24_pad // 2 * R * 2
+    assert p.bytes_meta_24 == T * o.n_24_pad // 64 * R * 8
+
+
+def test_plan_matches_oracle_random(lib):
+    rng = np.random.default_rng(99)
+    for _ in range(2000):
+        cin = 4 * int(rng.integers(1, 6000))
+        t = float(rng.uniform(0, 0.999))
+        v = float(rng.uniform(max(0, 2 * t - 1), t))
+        if rng.random() < 0.1:
+            v = t
+        p, o = hinm.plan(64, cin, 64, t, v), oh.plan(64, cin, 64, t, v)
+        assert (p.z, p.n_dense, p.n_24, p.n_pruned) == (o.z, o.n_dense, o.n_24, o.n_pruned), (cin, t, v)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((64, 256, 24, 0.5, 0.25), "HINM_ESHAPE"),
+    ((100, 256, 64, 0.5, 0.25), "HINM_ESHAPE"),
+    ((64, 254, 64, 0.5, 0.25), "HINM_ESHAPE"),
+    ((0, 256, 64, 0.5, 0.25), "HINM_ESHAPE"),
+    ((64, 256, 64, 0.5, 0.6), "HINM_EINVAL"),
+    ((64, 256, 64, 0.75, 0.4), "HINM_EINVAL"),
+    ((64, 256, 64, 1.0, 0.99), "HINM_EINVAL"),
+    ((64, 256, 64, float("nan"), 0.0), "HINM_EINVAL"),
+    ((64, 256, 64, 0.5, float("inf")), "HINM_EINVAL"),
+])
+def test_plan_errors(lib, args, status):
+    with pytest.raises(hinm.HinmError) as e:
+        hinm.plan(*args)
+    assert e.value.name == status
+    assert lib.hinm_last_error().decode()
+
+
+def test_status_strings(lib):
+    for s in range(9):
+        assert lib.hinm_status_str(s).decode().startswith(hinm.STATUS[s])
+
+
+def _fake_packed(p, base=1 << 20):
+    """A packed struct whose pointers are never dereferenced (host checks fail first)."""
+    return hinm.PackedT(p.raw, base, base, base, base, base)
+
+
+def test_spmm_host_errors(lib):
+    p = hinm.plan(4096, 4096, 64, 0.5, 0.25)
+    pk = _fake_packed(p)
+    call = lambda **kw: lib.hinm_spmm(ctypes.byref(kw.get("pk", pk)), kw.get("x", 4096), kw.get("batch", 16),
+                                      kw.get("ldx", 16), kw.get("y", 4096), kw.get("ldy", 16),
+                                      kw.get("ws", None), kw.get("wsb", 0), None)
+    assert call(batch=-1) == 2
+    assert call(ldx=8) == 2
+    assert call(ldy=8) == 2
+    assert call(x=None) == 1
+    assert call(x=4097) == 5
+    assert call(pk=_fake_packed(p, base=(1 << 20) + 8)) == 5
+    assert call(pk=hinm.PackedT(p.raw, None, None, None, None, None)) == 1
+    # decode batch needs a split-K workspace
+    need = hinm.spmm_workspace_bytes(p, 16)
+    assert need > 0
+    assert call(ws=None, wsb=0) == 6
+    assert call(ws=1 << 20, wsb=need - 1) == 6
+    assert call(ws=(1 << 20) + 16, wsb=need) == 5
+    assert call(batch=0, ldx=0, ldy=0) == 0          # empty batch is a no-op
+    bad = hinm.PlanT.from_buffer_copy(p.raw)
+    bad.n_dense += 1
+    assert call(pk=hinm.PackedT(bad, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20)) == 1
+    bad = hinm.PlanT.from_buffer_copy(p.raw)
+    bad.abi_version = 2
+    assert call(pk=hinm.PackedT(bad, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20)) == 1
+
+
+def test_pack_host_errors(lib):
+    p = hinm.plan(128, 256, 32, 0.75, 0.5)
+    wsb = hinm.pack_workspace_bytes(p)
+    assert wsb >= p.n_tiles * p.cin * 9
+    out = _fake_packed(p)
+    call = lambda **kw: lib.hinm_pack(ctypes.byref(p.raw), kw.get("w", 1 << 20), kw.get("ldw", 256),
+                                      kw.get("imp", 1 << 20), kw.get("ldi", 256), kw.get("perm", None),
+                                      ctypes.byref(kw.get("out", out)), kw.get("ws", 1 << 20),
+                                      kw.get("wsb", wsb), None)
+    assert call(w=None) == 1
+    assert call(ldw=255) == 2
+    assert call(imp=(1 << 20) + 2) == 5
+    assert call(ws=None) == 6
+    assert call(wsb=wsb - 1) == 6
+    assert call(ws=(1 << 20) + 64) == 5
+    assert call(out=hinm.PackedT(p.raw, None, None, None, None, None)) == 1
+
+
+def test_workspace_sizes(lib):
+    p = hinm.plan(11008, 4096, 64, 0.75, 0.55)
+    assert hinm.spmm_workspace_bytes(p, 0) == 0
+    assert hinm.spmm_workspace_bytes(p, 2048) == 0        # enough workgroups without a split
+    assert hinm.spmm_workspace_bytes(p, 1) % 256 == 0

@@ -1,0 +1,170 @@
+"""hinm_spmm on the GPU against the float64 oracle product.
+
+Bar: |Y - Y_o| <= 1e-2 (|W_hat| |X|) elementwise and relative Frobenius error
+<= 5e-3, Y_o = (W (.) M) X in float64 from the oracle's own mask.  Full
+outputs where the oracle product takes seconds; a fixed sample of rows (all
+tokens) at the large batches.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.hinm as oh
+import synth
+from helpers import bits_of, check_y, oracle_pack
+
+pytestmark = pytest.mark.gpu
+hinm = pytest.importorskip("structured_sparse_gemm_amd")
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+DEV = torch.device("cuda:0")
+
+
+class Case:
+    """A workload packed on both sides; products checked at several batches."""
+
+    def __init__(self, w: synth.Workload, v_s=None):
+        self.w = w
+        self.v_s = w.v_s if v_s is None else v_s
+        print(f"[spmm] {w.name} {w.cout}x{w.cin} R={w.tile_rows} t_s={w.t_s} v_s={self.v_s}", flush=True)
+        self.pk = hinm.pack(w.w_bf16.to(DEV), w.importance.to(DEV), w.tile_rows, w.t_s, self.v_s, w.perm.to(DEV))
+        self.p, _, inter = oracle_pack(w, v_s)
+        self.w_hat = oh.masked_weight(bits_of(w.w_bf16), inter["mask"])
+
+    def check(self, batch: int, seed: int = 0, rows=None, x=None, label=""):
+        if x is None:
+            g = torch.Generator().manual_seed(1000 + seed)
+            x = torch.randn(self.w.cin, batch, generator=g).to(torch.bfloat16)
+        print(f"[spmm]   batch={batch} rows={'all' if rows is None else len(rows)} {label}", flush=True)
+        y = hinm.spmm(self.pk, x.to(DEV))
+        torch.cuda.synchronize()
+        xf = synth.as_f64(x)
+        wh = self.w_hat if rows is None else self.w_hat[rows]
+        ref = oh.spmm(wh, xf)
+        scale = np.abs(wh) @ np.abs(xf)
+        got = y if rows is None else y[torch.as_tensor(rows, device=DEV)]
+        return check_y(got, ref, scale, f"{self.w.name} batch {batch}")
+
+
+def sample_rows(cout: int, n: int = 384, seed: int = 0) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(cout - 64, cout), rng.choice(cout, n, replace=False)]))
+    return rows
+
+
+def test_spmm_tiny():
+    w = synth.tiny()
+    c = Case(w)
+    c.check(8, x=w.x_bf16)
+    # Secondary oracle on the unrounded fp32 weight and activations: the bf16
+    # rounding of the inputs stays inside the same bound.
+    y = hinm.spmm(c.pk, w.x_bf16.to(DEV))
+    torch.cuda.synchronize()
+    _, _, inter = oracle_pack(w)
+    wf = np.where(inter["mask"], w.w_f32.numpy().astype(np.float64), 0.0)
+    xf = w.x_f32.numpy().astype(np.float64)
+    check_y(y, wf @ xf, np.abs(wf) @ np.abs(xf), "tiny vs fp32 inputs")
+
+
+def test_spmm_q_proj_decode():
+    w = synth.q_proj(batch=16)
+    Case(w).check(16, x=w.x_bf16)
+
+
+def test_spmm_up_proj_prefill():
+    w = synth.up_proj(batch=2048)
+    Case(w).check(2048, x=w.x_bf16, rows=sample_rows(w.cout))
+
+
+@pytest.mark.parametrize("batch", [16, 2048])
+def test_spmm_down_proj(batch):
+    w = synth.down_proj(batch=batch)
+    Case(w).check(batch, x=w.x_bf16, rows=None if batch <= 64 else sample_rows(w.cout))
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2])
+def test_spmm_down_proj_sweep(idx):
+    g = json.load(open(os.path.join(GOLDEN, "down_proj_boundary.json")))["results"][idx]
+    c = Case(synth.down_proj_sweep(g["t_s"], batch=1), v_s=g["v_s"])
+    for b in (1, 64, 512):
+        c.check(b, seed=b, rows=None if b <= 64 else sample_rows(c.w.cout))
+
+
+@pytest.mark.parametrize("layer,proj", [(0, 0), (13, 4), (31, 6)])
+def test_spmm_stack_layers(layer, proj):
+    c = Case(synth.stack_layer(layer, proj, batch=1))
+    for b in (1, 16, 256, 2048):
+        c.check(b, seed=b, rows=None if b <= 256 else sample_rows(c.w.cout))
+
+
+def test_spmm_ragged_batches():
+    c = Case(synth.small(192, 264, 64, 0.6, 0.35, 1, seed=4))
+    for b in (1, 2, 3, 8, 15, 17, 31, 33, 63, 64, 65, 100, 1000):
+        c.check(b, seed=b)
+
+
+@pytest.mark.parametrize("args", [
+    (64, 100, 16, 0.5, 0.25), (96, 132, 48, 0.6, 0.3), (128, 256, 64, 0.0, 0.0),
+    (128, 256, 64, 0.75, 0.75), (128, 256, 64, 0.75, 0.5), (160, 4, 32, 0.5, 0.0), (64, 300, 64, 0.9, 0.85),
+])
+def test_spmm_edge_shapes(args):
+    cout, cin, R, t, v = args
+    c = Case(synth.small(cout, cin, R, t, v, 1, seed=cout + cin))
+    for b in (1, 16, 70):
+        c.check(b, seed=b)
+
+
+def test_spmm_strided_and_unaligned_x():
+    c = Case(synth.small(128, 320, 64, 0.6, 0.3, 1, seed=12))
+    g = torch.Generator().manual_seed(3)
+    big = torch.randn(320, 40, generator=g).to(torch.bfloat16)
+    c.check(24, x=big[:, :24], label="ldx=40")                       # ldx > batch, 16-byte rows
+    raw = torch.randn(320 * 24 + 1, generator=g).to(torch.bfloat16)
+    xv = raw[1:].view(320, 24)                                       # 2-byte aligned only
+    xd =  torch.empty(320 * 24 + 1, dtype=torch.bfloat16, device=DEV)
+    xd[1:].copy_(xv.reshape(-1).to(DEV))
+    xdv = xd[1:].view(320, 24)
+    assert xdv.data_ptr() % 16 != 0
+    y = hinm.spmm(c.pk, xdv)
+    torch.cuda.synchronize()
+    xf = synth.as_f64(xv)
+    check_y(y, c.w_hat @ xf, np.abs(c.w_hat) @ np.abs(xf), "unaligned x")
+    out = torch.full((128, 40), 7.0, dtype=torch.bfloat16, device=DEV)
+    hinm.spmm(c.pk, xdv, out=out[:, :24])
+    torch.cuda.synchronize()
+    check_y(out[:, :24], c.w_hat @ xf, np.abs(c.w_hat) @ np.abs(xf), "ldy=40")
+    assert (out[:, 24:] == 7.0).all(), "columns past the batch were written"
+
+
+def test_spmm_deterministic():
+    c = Case(synth.small(512, 1024, 64, 0.7, 0.45, 1, seed=8))
+    for b in (4, 16, 300):
+        x = torch.randn(1024, b, generator=torch.Generator().manual_seed(b)).to(torch.bfloat16).to(DEV)
+        y1 = hinm.spmm(c.pk, x).clone()
+        y2 = hinm.spmm(c.pk, x)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_spmm_permutation_invariance():
+    """Relabelling input channels of W, importance, perm and X gives a bitwise-identical Y."""
+    w = synth.small(256, 512, 64, 0.6, 0.3, 1, seed=21)
+    x = torch.randn(512, 48, generator=torch.Generator().manual_seed(2)).to(torch.bfloat16)
+    pk = hinm.pack(w.w_bf16.to(DEV), w.importance.to(DEV), 64, 0.6, 0.3, w.perm.to(DEV))
+    y = hinm.spmm(pk, x.to(DEV))
+    sig = torch.from_numpy(np.random.default_rng(1).permutation(512))
+    inv = torch.argsort(sig)
+    perm2 = inv[w.perm.long()].to(torch.int32)
+    pk2 = hinm.pack(w.w_bf16[:, sig].contiguous().to(DEV), w.importance[:, sig].contiguous().to(DEV), 64, 0.6, 0.3,
+                    perm2.to(DEV))
+    y2 = hinm.spmm(pk2, x[sig].contiguous().to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+def test_spmm_empty_batch():
+    c = Case(synth.small(64, 128, 64, 0.5, 0.25, 1, seed=1))
+    y = hinm.spmm(c.pk, torch.empty(128, 0, dtype=torch.bfloat16, device=DEV))
+    assert y.shape == (64, 0)
