@@ -1,0 +1,222 @@
+"""Benchmark of the HiNM sparse-weight x dense-activation product on one MI355X.
+
+Workload: LLaMA-7B down_proj weight 4096 x 11008 (cout x cin) in bf16, HiNM
+packed with tile_rows 64, t_s 0.75, v_s 0.55 (550 dense / 4404 2:4 / 6054
+pruned vectors per tile), random per-tile input permutations; X bf16
+[11008 x batch].  A step is one product Y = (W (.) M) X at batch 2048 (the
+compute-bound point); the batch-16 product (the bandwidth-bound point) and
+the one-time pack are timed beside it and reported in the same JSON line.
+
+Inputs are resident in HBM before timing starts; successive steps rotate
+through enough copies of the packed weight, X and Y (>= 1 GiB) that the
+256 MB last-level cache cannot serve a repeat.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+ROTATE_BYTES = 1 << 30
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--batch", type=int, default=2048)
+    ap.add_argument("--decode-batch", type=int, default=16)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense torch.matmul comparator")
+    return ap.parse_args()
+
+
+def algorithmic(p, batch):
+    """Algorithmic bytes and flops of one product (padding excluded)."""
+    kept = p.cin - p.z
+    val = p.cout * kept * 2
+    meta = p.cout * p.n_24 // 8
+    idx = p.n_tiles * (p.n_dense + p.n_24) * 4
+    xb = p.cin * batch * 2
+    yb = p.cout * batch * 2
+    return {"bytes": val + meta + idx + xb + yb, "useful_flops": 2 * p.cout * kept * batch,
+            "dense_equiv_flops": 2 * p.cout * p.cin * batch,
+            "executed_flops": 2 * p.cout * (p.n_dense_pad + p.n_24_pad // 2) * batch}
+
+
+class Rotation:
+    """k copies of (packed weight, X, Y) so that k * bytes >= ROTATE_BYTES."""
+
+    def __init__(self, hinm, torch, pk, x, batch):
+        per = pk.nbytes() + x.numel() * 2 + pk.plan.cout * batch * 2
+        self.k = max(2, -(-ROTATE_BYTES // per))
+        self.items = []
+        for i in range(self.k):
+            pki = pk if i == 0 else hinm.HinmPacked(pk.plan, pk.val_dense.clone(), pk.idx_dense.clone(),
+                                                    pk.val_24.clone(), pk.meta_24.clone(), pk.idx_24.clone())
+            xi = x if i == 0 else x.clone()
+            yi = torch.empty(pk.plan.cout, batch, dtype=torch.bfloat16, device=x.device)
+            self.items.append((pki, xi, yi))
+        ws_bytes = hinm.spmm_workspace_bytes(pk.plan, batch)
+        self.ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+
+    def __getitem__(self, i):
+        return self.items[i % self.k]
+
+
+def time_spmm(hinm, torch, rot, steps, warmup):
+    """Per-step times from HIP events on the launching stream, plus the whole-loop time."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        pk, x, y = rot[i]
+        hinm.spmm(pk, x, out=y, workspace=rot.ws)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(steps):
+        pk, x, y = rot[warmup + i]
+        hinm.spmm(pk, x, out=y, workspace=rot.ws)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    total_ms = ev[0].elapsed_time(ev[steps])
+    return {"ms_total": total_ms, "ms_mean": total_ms / steps, "ms_median": per[len(per) // 2],
+            "ms_p10": per[len(per) // 10], "ms_p90": per[(9 * len(per)) // 10], "wall_s": wall}
+
+
+def time_dense(torch, w, x, steps, warmup):
+    y = torch.empty(w.shape[0], x.shape[1], dtype=torch.bfloat16, device=x.device)
+    for _ in range(warmup):
+        torch.matmul(w, x, out=y)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        torch.matmul(w, x, out=y)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def cpu_baseline(w, batch):
+    """The CPU oracle as it stands: pack, then the float64 product, on this host's cores."""
+    import numpy as np
+
+    import oracle.hinm as oh
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    p = oh.plan(w.cout, w.cin, w.tile_rows, w.t_s, w.v_s)
+    bits = w.w_bf16.view(__import__("torch").int16).numpy().view(np.uint16)
+    t0 = time.perf_counter()
+    _, inter = oh.pack(bits, w.importance.numpy(), w.perm.numpy(), p, with_intermediates=True)
+    t_pack = time.perf_counter() - t0
+    wh = oh.masked_weight(bits, inter["mask"])
+    xf = synth.as_f64(w.x_bf16)
+    t0 = time.perf_counter()
+    oh.spmm(wh, xf)
+    t_prod = time.perf_counter() - t0
+    useful = 2 * p.cout * (p.cin - p.z) * batch
+    return {"value": round(useful / t_prod / 1e12, 4), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"whole workload once: oracle pack of the 4096x11008 weight ({t_pack:.2f} s) and its "
+                       f"float64 product at batch {batch} ({t_prod:.2f} s); value = useful flops / product time"),
+            "pack_s": round(t_pack, 3), "product_s": round(t_prod, 3),
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the product shards by output tiles with no exchange, see the design notes).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import structured_sparse_gemm_amd as hinm
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, Bd = args.batch, args.decode_batch
+    w = synth.down_proj(batch=B)
+    wd_ = synth.down_proj(batch=Bd)          # same weight and perms (same seed), batch-16 activations
+    p = hinm.plan(w.cout, w.cin, w.tile_rows, w.t_s, w.v_s)
+
+    wgpu, igpu, pgpu = w.w_bf16.to(dev), w.importance.to(dev), w.perm.to(dev)
+    torch.cuda.synchronize()
+    pack_ms = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        pk = hinm.pack(wgpu, igpu, w.tile_rows, w.t_s, w.v_s, pgpu)
+        pack_ms.append((time.perf_counter() - t0) * 1e3)
+    x = w.x_bf16.to(dev)
+    xd = wd_.x_bf16.to(dev)
+
+    rot = Rotation(hinm, torch, pk, x, B)
+    r = time_spmm(hinm, torch, rot, args.steps, args.warmup)
+    alg = algorithmic(p, B)
+    ms = r["ms_mean"]
+    value = alg["useful_flops"] / (ms * 1e-3) / 1e12
+
+    rotd = Rotation(hinm, torch, pk, xd, Bd)
+    rd = time_spmm(hinm, torch, rotd, max(args.steps, 200), args.warmup)
+    algd = algorithmic(p, Bd)
+    gbs_d = algd["bytes"] / (rd["ms_mean"] * 1e-3) / 1e9
+
+    dense = None
+    if not args.no_dense:
+        dense_ms = time_dense(torch, wgpu, x, max(10, args.steps // 2), 3)
+        dense_ms_d = time_dense(torch, wgpu, xd, 200, 10)
+        dense = {"what": "torch.matmul bf16 of the unpruned 4096x11008 weight (hipBLASLt), same shapes",
+                 "batch_2048_ms": round(dense_ms, 4), "batch_16_ms": round(dense_ms_d, 4),
+                 "speedup_batch_2048": round(dense_ms / ms, 3), "speedup_batch_16": round(dense_ms_d / rd["ms_mean"], 3)}
+
+    cpu = None if args.no_cpu else cpu_baseline(w, B)
+
+    line = {
+        "metric": "HiNM SpMM effective TFLOP/s + HBM GB/s, 4096x11008 bf16 at batch 16 and 2048",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,0.02) x LogNormal column scales, random per-tile perms)",
+        "config": {"workload": "down_proj 4096x11008 HiNM SpMM, tile_rows 64, t_s 0.75, v_s 0.55, batch 2048",
+                   "cout": p.cout, "cin": p.cin, "tile_rows": p.tile_rows, "t_s": p.t_s, "v_s": p.v_s,
+                   "batch": B, "regions_per_tile": {"dense": p.n_dense, "two_four": p.n_24, "pruned": p.n_pruned}},
+        "roofline": {"bound": "mfma", "achieved": round(value, 3), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(value / MFMA_BF16_PEAK_TFLOPS, 5), "traffic": None,
+                     "kernel": "spmm_kernel (one launch per step)",
+                     "per_launch": {"useful_flops": alg["useful_flops"], "algorithmic_bytes": alg["bytes"],
+                                    "ms_mean": round(ms, 5), "ms_median": round(r["ms_median"], 5),
+                                    "ms_p10": round(r["ms_p10"], 5), "ms_p90": round(r["ms_p90"], 5)},
+                     "rotation_copies": rot.k},
+        "decode": {"batch": Bd, "ms_mean": round(rd["ms_mean"], 5), "ms_median": round(rd["ms_median"], 5),
+                   "ms_p10": round(rd["ms_p10"], 5), "ms_p90": round(rd["ms_p90"], 5),
+                   "algorithmic_bytes": algd["bytes"], "hbm_gbs": round(gbs_d, 1),
+                   "roofline": {"bound": "hbm", "achieved": round(gbs_d, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(gbs_d / HBM_PEAK_GBS, 4)},
+                   "useful_tflops": round(algd["useful_flops"] / (rd["ms_mean"] * 1e-3) / 1e12, 3),
+                   "rotation_copies": rotd.k},
+        "batch_2048_hbm_gbs": round(alg["bytes"] / (ms * 1e-3) / 1e9, 1),
+        "pack_ms": [round(v, 2) for v in pack_ms],
+        "dense_comparator": dense,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

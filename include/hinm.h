@@ -159,6 +159,10 @@ int hinm_spmm_workspace_bytes(const hinm_plan_t* plan, int64_t batch, size_t* by
  * X and Y must be 2-byte aligned; 16-byte aligned X with ldx % 8 == 0 takes
  * the vector-load path.  workspace (device, 256-byte aligned) of at least
  * hinm_spmm_workspace_bytes(plan, batch) bytes, may be NULL when that is 0.
+ * The workspace must be zero-filled before its first use; every call that
+ * returns HINM_OK leaves it ready for the next one (its arrival counters are
+ * back at zero when the work on `stream` completes).  Calls sharing one
+ * workspace must be ordered (same stream, or synchronised).
  * batch == 0 is a no-op.  Asynchronous on `stream`; no host synchronisation,
  * no atomics: the same inputs give bitwise-identical Y.
  * Errors (host-side checks only): HINM_EINVAL, HINM_ESHAPE, HINM_EALIGN,

@@ -222,7 +222,8 @@ def _workspace(device: torch.device, nbytes: int) -> Optional[torch.Tensor]:
     key = (device.type, device.index)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        # zero-filled: the product keeps its arrival counters here
+        buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf
 

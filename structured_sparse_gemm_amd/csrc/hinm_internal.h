@@ -22,12 +22,21 @@ inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 // Split of the reduction dimension chosen for a batch (1 = no split) and the
 // token-block width; shared by hinm_spmm and hinm_spmm_workspace_bytes so the
 // workspace size always matches what the launch uses.
+// Every workspace starts with a fixed region of arrival counters, kept at
+// zero between calls; partial sums start after it, so products of different
+// shapes can share one workspace.
+constexpr int64_t kWsCounters = 16384;
+constexpr int64_t kWsCounterBytes = kWsCounters * 4;
+
+enum { kPathGeneric = 0, kPathDecode = 1, kPathPrefill = 2, kPathDecodeSplit = 3 };
 struct SpmmShape {
+  int path;        // which kernel runs the product
   int nt;          // tokens per workgroup
   int n_tblocks;   // token blocks
   int n_rblocks;   // 64-row blocks per tile
   int n_kunits;    // K work units per tile (dense block = 1, 2:4 block = 2)
   int splits;      // K splits (>= 1)
+  int64_t ws_counter_bytes;  // arrival counters at the start of the workspace (split decode)
   int64_t ws_bytes;
 };
 SpmmShape spmm_shape(const hinm_plan_t* p, int64_t batch);

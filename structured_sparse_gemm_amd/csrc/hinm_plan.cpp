@@ -2,6 +2,7 @@
 // Makes no HIP call, so it runs (and is tested) on a host without a GPU.
 #include <math.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "hinm_internal.h"
@@ -111,28 +112,75 @@ extern "C" const char* hinm_status_str(int status) {
 
 extern "C" const char* hinm_last_error(void) { return hinm::g_last_error; }
 
-// Work decomposition of the product.  Decode-sized batches have too few
-// (tile, row block, token block) triples to fill 256 compute units, so the
-// reduction dimension is split; partial sums then go through the workspace.
+// Work decomposition of the product.
+//  - batch <= 64 and tile_rows % 64 == 0: the split decode kernel (64-row
+//    workgroups, K split over a power-of-two number of workgroups, partial
+//    sums through the workspace);
+//  - other batch <= 64: the 16-row decode kernel (K split over the waves of
+//    a workgroup, no workspace);
+//  - larger batches with tile_rows % 64 == 0: the prefill kernel (64-row x
+//    128/256-token workgroups, no workspace);
+//  - otherwise the generic kernel, which splits K over workgroups when there
+//    are too few of them and reduces the partials through the workspace.
 namespace hinm {
 SpmmShape spmm_shape(const hinm_plan_t* p, int64_t batch) {
   SpmmShape s;
-  s.nt = batch <= 16 ? 16 : (batch <= 32 ? 32 : 64);
-  s.n_tblocks = (int)((batch + s.nt - 1) / s.nt);
   s.n_rblocks = (p->tile_rows + 63) / 64;
   s.n_kunits = p->n_dense_pad / HINM_KB_DENSE + 2 * (p->n_24_pad / HINM_KB_24);
+  s.splits = 1;
+  s.ws_bytes = 0;
+  s.ws_counter_bytes = 0;
+  if (batch <= 64) {
+    s.nt = batch <= 16 ? 16 : (batch <= 32 ? 32 : 64);
+    s.n_tblocks = (int)((batch + s.nt - 1) / s.nt);
+    const char* dp = getenv("HINM_DECODE_PATH");
+    if (p->tile_rows % 64 == 0 && !(dp && strcmp(dp, "rows16") == 0)) {
+      // 64-row workgroups, K split over a power-of-two number of workgroups
+      // so that about `target` workgroups run, each with >= 4 K-blocks.
+      s.path = kPathDecodeSplit;
+      const int64_t base = (int64_t)p->n_tiles * (p->tile_rows / 64) * s.n_tblocks;
+      const int nblk = p->n_dense_pad / HINM_KB_DENSE + p->n_24_pad / HINM_KB_24;
+      int64_t target = 256;
+      const char* env = getenv("HINM_DECODE_WGS");
+      if (env && atoi(env) > 0) target = atoi(env);
+      int splits = 1;
+      if (base <= kWsCounters)
+        while (splits < 64 && base * splits * 2 <= target && nblk / (splits * 2) >= 4) splits *= 2;
+      s.splits = splits;
+      if (splits > 1) {
+        s.ws_counter_bytes = kWsCounterBytes;
+        s.ws_bytes = kWsCounterBytes + (int64_t)splits * s.n_tblocks * p->cout * s.nt * 4;
+      }
+      return s;
+    }
+    s.path = kPathDecode;
+    return s;
+  }
+  if (p->tile_rows % 64 == 0) {
+    s.path = kPathPrefill;
+    s.nt = batch >= 512 ? 256 : 128;
+    const char* env = getenv("HINM_PREFILL_NT");
+    if (env && (atoi(env) == 128 || atoi(env) == 256)) s.nt = atoi(env);
+    s.n_tblocks = (int)((batch + s.nt - 1) / s.nt);
+    return s;
+  }
+  s.path = kPathGeneric;
+  s.nt = 64;
+  s.n_tblocks = (int)((batch + s.nt - 1) / s.nt);
   const int64_t wgs = (int64_t)p->n_tiles * s.n_rblocks * s.n_tblocks;
-  int splits = 1;
   const int64_t target = 1024;  // about four workgroups per compute unit
   if (wgs < target && s.n_kunits > 1) {
-    splits = (int)((target + wgs - 1) / wgs);
+    int splits = (int)((target + wgs - 1) / wgs);
     int max_splits = s.n_kunits / 4;  // keep at least ~4 K units per split
     if (max_splits < 1) max_splits = 1;
     if (splits > max_splits) splits = max_splits;
     if (splits > 32) splits = 32;
+    s.splits = splits;
   }
-  s.splits = splits;
-  s.ws_bytes = splits > 1 ? (int64_t)splits * p->cout * ((batch + 15) / 16 * 16) * 4 : 0;
+  if (s.splits > 1) {
+    s.ws_counter_bytes = kWsCounterBytes;
+    s.ws_bytes = kWsCounterBytes + (int64_t)s.splits * p->cout * ((batch + 15) / 16 * 16) * 4;
+  }
   return s;
 }
 }  // namespace hinm

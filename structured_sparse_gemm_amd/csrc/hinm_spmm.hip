@@ -18,6 +18,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "hinm_internal.h"
 
 using hinm::fail;
@@ -48,6 +50,8 @@ struct SpmmArgs {
   int nkb_d, nkb_s;          // K-blocks per tile in each region
   int n_rblocks, splits, n_kunits;
   int x_vec;                 // 1: 16-byte aligned X rows (ldx % 8 == 0)
+  int y_vec;                 // 1: 16-byte aligned Y rows (ldy % 8 == 0)
+  int n_tiles;
 };
 
 __device__ inline uint16_t bf16_rne(float f) {
@@ -179,6 +183,481 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ w
   y[row * ldy + n] = bf16_rne(acc);
 }
 
+// ---------------------------------------------------------------------------
+// Shared pieces of the decode and prefill kernels.
+//
+// X tiles sit in LDS row-major (one row per gathered X row, tokens
+// contiguous), exactly as the gather reads them.  The MFMA B operand needs
+// several K positions of one token per lane; ds_read_b64_tr_b16 supplies that
+// transposition: within each 16-lane group, output lane j receives element
+// j%4 of the 8-byte row segment addressed by lane 4q + j/4, for q = 0..3.
+// So lane (i) of a group addresses LDS row "position(4r + i/4)" at token
+// column base + 4*(i%4) to deliver slots 4r..4r+3 of its B operand.
+// ---------------------------------------------------------------------------
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ inline v4i16 tr_read(const uint16_t* lds_elem) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16*)((__attribute__((address_space(3))) char*)((__attribute__((address_space(3))) uint16_t*)lds_elem)));
+}
+
+// Loads 16 bytes (8 tokens) of X row c starting at token nb; zeros past the
+// batch, for a -1 index, or when nb is past the batch.
+__device__ inline u32x4 load_x_chunk(const SpmmArgs& a, int c, int nb) {
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (c < 0 || c >= a.cin || nb >= a.batch) return v;
+  const uint16_t* src = a.x + (int64_t)c * a.ldx + nb;
+  if (a.x_vec && nb + 8 <= a.batch) return *reinterpret_cast<const u32x4*>(src);
+  uint32_t h[8];
+  for (int e = 0; e < 8; ++e) h[e] = (nb + e < a.batch) ? (uint32_t)src[e] : 0u;
+  v[0] = h[0] | (h[1] << 16);
+  v[1] = h[2] | (h[3] << 16);
+  v[2] = h[4] | (h[5] << 16);
+  v[3] = h[6] | (h[7] << 16);
+  return v;
+}
+
+// Loads 16 bytes (8 tokens) of X row c at token nb with no branches: the
+// caller guarantees 16-byte aligned rows and nb + 8 <= batch; a pad index
+// reads row 0 and the chunk is replaced by zeros.
+__device__ inline u32x4 load_x_chunk_fast(const SpmmArgs& a, int c, int nb) {
+  const bool ok = (c >= 0) & (c < a.cin);
+  const u32x4 v = *reinterpret_cast<const u32x4*>(a.x + (int64_t)(ok ? c : 0) * a.ldx + nb);
+  return ok ? v : u32x4{0u, 0u, 0u, 0u};
+}
+
+constexpr int kDecWaves = 8;
+
+// ---------------------------------------------------------------------------
+// Decode kernel, all loads up front (small batches).
+// At decode sizes every compute unit's share of the packed weight is only a
+// few latency-bandwidth products, so each wave issues the loads of up to CH
+// of its K-blocks at once - packed values, metadata and index slices first,
+// then the X rows those indices name - and only then multiplies them.  A
+// block of either region occupies the same registers and issues the same
+// loads (a dense block repeats its 32 indices into the second half), which
+// keeps the code straight-line.  Workgroup = 16 rows of one tile x NTOK
+// tokens, 8 waves over the tile's blocks round-robin; the 8 partial sums are
+// added in wave order through LDS.
+// ---------------------------------------------------------------------------
+template <int NTOK, int CH, bool FAST>
+__global__ __launch_bounds__(kDecWaves * 64) void decode3_kernel(SpmmArgs a) {
+  constexpr int CPR = NTOK / 8;               // 16-byte chunks per X row
+  constexpr int SLOT = 64 * NTOK;
+  constexpr int NB = NTOK / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t xsh[kDecWaves * SLOT];
+  __shared__ float red[kDecWaves * 16 * NTOK];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nrb = a.rows / 16;
+  const int t = blockIdx.x / nrb, rb = blockIdx.x % nrb;
+  const int n0 = blockIdx.y * NTOK;
+  const int row = rb * 16 + (lane & 15);
+  const int kc = lane >> 4, i16 = lane & 15;
+  const int nblk = a.nkb_d + a.nkb_s;
+  const int cnt = wave < nblk ? (nblk - wave + kDecWaves - 1) / kDecWaves : 0;
+  uint16_t* xs = xsh + wave * SLOT;
+
+  f32x4 acc[NB];
+  for (int j = 0; j < NB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int c0 = 0; c0 < cnt; c0 += CH) {
+    u32x4 A[CH];
+    uint64_t M[CH];
+    int I[CH][CPR];
+    u32x4 X[CH][CPR];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int b = wave + kDecWaves * min(c0 + j, cnt - 1);
+      const bool dense = b < a.nkb_d;
+      const int kb = dense ? b : b - a.nkb_d;
+      const int64_t blk = ((int64_t)t * (dense ? a.nkb_d : a.nkb_s) + kb) * a.rows + row;
+      const uint16_t* vp = (dense ? a.val_d : a.val_s) + blk * 32 + 8 * kc;
+      A[j] = *reinterpret_cast<const u32x4*>(vp);
+      M[j] = dense ? *reinterpret_cast<const uint64_t*>(vp) : a.meta[blk];
+      const int32_t* il = dense ? a.idx_d + ((int64_t)t * a.nkb_d + kb) * 32 : a.idx_s + ((int64_t)t * a.nkb_s + kb) * 64;
+      for (int k = 0; k < CPR; ++k) {
+        const int pos = (lane + 64 * k) / CPR;
+        I[j][k] = il[dense ? (pos & 31) : pos];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+      for (int k = 0; k < CPR; ++k) {
+        const int nb = n0 + 8 * ((lane + 64 * k) % CPR);
+        X[j][k] = FAST ? load_x_chunk_fast(a, I[j][k], nb) : load_x_chunk(a, I[j][k], nb);
+      }
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      if (c0 + j < cnt) {
+        const int b = wave + kDecWaves * (c0 + j);
+        for (int k = 0; k < CPR; ++k) *reinterpret_cast<u32x4*>(xs + 8 * (lane + 64 * k)) = X[j][k];
+        const bf16x8 Av = __builtin_bit_cast(bf16x8, A[j]);
+        for (int nb = 0; nb < NB; ++nb) {
+          const uint16_t* base = xs + 16 * nb + 4 * (i16 & 3);
+          const v4i16 b0 = tr_read(base + (8 * kc + 0 + (i16 >> 2)) * NTOK);
+          const v4i16 b1 = tr_read(base + (8 * kc + 4 + (i16 >> 2)) * NTOK);
+          if (b < a.nkb_d) {
+            const bf16x8 B = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, B, acc[nb], 0, 0, 0);
+          } else {
+            const v4i16 b2 = tr_read(base + (32 + 8 * kc + 0 + (i16 >> 2)) * NTOK);
+            const v4i16 b3 = tr_read(base + (32 + 8 * kc + 4 + (i16 >> 2)) * NTOK);
+            const bf16x16 B = __builtin_bit_cast(
+                bf16x16, __builtin_shufflevector(__builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                 __builtin_shufflevector(b2, b3, 0, 1, 2, 3, 4, 5, 6, 7), 0, 1, 2,
+                                                 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15));
+            acc[nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(Av, B, acc[nb],
+                                                                (int)((M[j] >> (16 * kc)) & 0xffffull), 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  // fixed-order sum over the waves, bf16 out; acc[nb][e] is row 4*kc + e, token 16*nb + i16.
+  for (int nb = 0; nb < NB; ++nb)
+    for (int e = 0; e < 4; ++e) red[(wave * 16 + 4 * kc + e) * NTOK + 16 * nb + i16] = acc[nb][e];
+  __syncthreads();
+  for (int o = threadIdx.x; o < 16 * NTOK; o += kDecWaves * 64) {
+    const int r = o / NTOK, n = o % NTOK;
+    float sum = 0.f;
+    for (int w = 0; w < kDecWaves; ++w) sum += red[w * 16 * NTOK + o];
+    if (n0 + n < a.batch) a.y[((int64_t)t * a.rows + rb * 16 + r) * a.ldy + n0 + n] = bf16_rne(sum);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode kernel, split-K over workgroups (small batches, tile_rows % 64 == 0).
+// Workgroup = (64-row block of a tile, K split, token block), 4 waves of 16
+// rows.  All loads of a round - the packed values and metadata of up to MAXB
+// K-blocks into registers, the X rows those blocks gather into LDS (shared by
+// the 4 waves) - are issued before any is waited for: at decode sizes a
+// compute unit's whole share of the weight is only a few latency-bandwidth
+// products.  The splits' fp32 partial sums go to the workspace; the last
+// workgroup of a (row block, token block) to arrive adds them in split order
+// and writes Y (deterministic), then clears its arrival counter; the counters
+// (at the start of the workspace) must be zero before the first call.
+// ---------------------------------------------------------------------------
+template <int NTOK, int MAXB, bool FAST>
+__global__ __launch_bounds__(256) void decode4_kernel(SpmmArgs a, int splits, int n_tb, float* __restrict__ part,
+                                                      unsigned* __restrict__ counters) {
+  constexpr int CPR = NTOK / 8;
+  constexpr int MAXP = MAXB * 64;              // gathered positions per round
+  constexpr int MAXCH = MAXP * CPR / 256;      // X chunks per thread per round
+  constexpr int NB = NTOK / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[MAXP * NTOK];
+  __shared__ int s_last;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kc = lane >> 4, i16 = lane & 15;
+  const int nrb = a.rows / 64;
+  const int split = blockIdx.x % splits;
+  const int trb = blockIdx.x / splits;           // tile * nrb + row block
+  const int t = trb / nrb, rb = trb % nrb;
+  const int tb = blockIdx.y;
+  const int n0 = tb * NTOK;
+  const int row = rb * 64 + wave * 16 + (lane & 15);   // tile row of this lane's A fragment
+  const int nblk = a.nkb_d + a.nkb_s;
+  const int b_lo = (int)((int64_t)split * nblk / splits), b_hi = (int)((int64_t)(split + 1) * nblk / splits);
+
+  f32x4 acc[NB];
+  for (int j = 0; j < NB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int r0 = b_lo; r0 < b_hi; r0 += MAXB) {
+    const int r1 = min(r0 + MAXB, b_hi);
+    const int nbr = r1 - r0;
+    // dense blocks come first in the block order, so the round's positions
+    // are a run of dense columns followed by a run of 2:4 positions.
+    const int nd_r = max(0, min(r1, a.nkb_d) - r0);
+    const int pd = 32 * nd_r;                      // dense positions in the round
+    const int ptot = pd + 64 * (nbr - nd_r);
+    const int32_t* idd = a.idx_d + (int64_t)t * a.nkb_d * 32 + (int64_t)r0 * 32;
+    const int32_t* ids = a.idx_s + (int64_t)t * a.nkb_s * 64 + (int64_t)max(0, r0 - a.nkb_d) * 64;
+
+    // Every load below is unconditional (indices clamped into the round) so
+    // the code stays straight-line: index slices first, then packed values and
+    // metadata, then the X rows; positions past the round gather junk into
+    // LDS space that is never read.
+    int cidx[MAXCH];
+#pragma unroll
+    for (int j = 0; j < MAXCH; ++j) {
+      const int pos = min((int)((threadIdx.x + 256 * j) / CPR), ptot - 1);
+      cidx[j] = *(pos < pd ? idd + pos : ids + (pos - pd));
+    }
+    u32x4 av[MAXB];
+    uint64_t mv[MAXB];
+#pragma unroll
+    for (int j = 0; j < MAXB; ++j) {
+      const int b = r0 + min(j, nbr - 1);
+      const bool dense = b < a.nkb_d;
+      const int64_t blk = dense ? ((int64_t)t * a.nkb_d + b) * a.rows + row
+                                : ((int64_t)t * a.nkb_s + (b - a.nkb_d)) * a.rows + row;
+      const uint16_t* vp = (dense ? a.val_d : a.val_s) + blk * 32 + 8 * kc;
+      av[j] = *reinterpret_cast<const u32x4*>(vp);
+      mv[j] = *(dense ? reinterpret_cast<const uint64_t*>(vp) : a.meta + blk);
+    }
+    u32x4 xr[MAXCH];
+#pragma unroll
+    for (int j = 0; j < MAXCH; ++j) {
+      const int nb = n0 + 8 * ((threadIdx.x + 256 * j) % CPR);
+      xr[j] = FAST ? load_x_chunk_fast(a, cidx[j], nb) : load_x_chunk(a, cidx[j], nb);
+    }
+#pragma unroll
+    for (int j = 0; j < MAXCH; ++j) *reinterpret_cast<u32x4*>(xs + 8 * (threadIdx.x + 256 * j)) = xr[j];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < MAXB; ++j) {
+      if (j < nbr) {
+        const int b = r0 + j;
+        const bf16x8 A = __builtin_bit_cast(bf16x8, av[j]);
+        if (b < a.nkb_d) {
+          const uint16_t* xb = xs + (32 * j) * NTOK;
+          for (int nb = 0; nb < NB; ++nb) {
+            const uint16_t* base = xb + 16 * nb + 4 * (i16 & 3);
+            const v4i16 b0 = tr_read(base + (8 * kc + 0 + (i16 >> 2)) * NTOK);
+            const v4i16 b1 = tr_read(base + (8 * kc + 4 + (i16 >> 2)) * NTOK);
+            const bf16x8 B = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[nb], 0, 0, 0);
+          }
+        } else {
+          const uint16_t* xb = xs + (pd + 64 * (j - nd_r)) * NTOK;
+          const int sidx = (int)((mv[j] >> (16 * kc)) & 0xffffull);
+          for (int nb = 0; nb < NB; ++nb) {
+            const uint16_t* base = xb + 16 * nb + 4 * (i16 & 3);
+            const v4i16 b0 = tr_read(base + (8 * kc + 0 + (i16 >> 2)) * NTOK);
+            const v4i16 b1 = tr_read(base + (8 * kc + 4 + (i16 >> 2)) * NTOK);
+            const v4i16 b2 = tr_read(base + (32 + 8 * kc + 0 + (i16 >> 2)) * NTOK);
+            const v4i16 b3 = tr_read(base + (32 + 8 * kc + 4 + (i16 >> 2)) * NTOK);
+            const bf16x16 B = __builtin_bit_cast(
+                bf16x16, __builtin_shufflevector(__builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                 __builtin_shufflevector(b2, b3, 0, 1, 2, 3, 4, 5, 6, 7), 0, 1, 2,
+                                                 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15));
+            acc[nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(A, B, acc[nb], sidx, 0, 0);
+          }
+        }
+      }
+    }
+    __syncthreads();   // the next round overwrites xs
+  }
+
+  // acc[nb][e]: tile row rb*64 + wave*16 + 4*kc + e, token 16*nb + i16.
+  const int64_t grow0 = (int64_t)t * a.rows + rb * 64 + wave * 16 + 4 * kc;
+  if (splits == 1) {
+    for (int nb = 0; nb < NB; ++nb) {
+      const int n = n0 + 16 * nb + i16;
+      if (n < a.batch)
+        for (int e = 0; e < 4; ++e) a.y[(grow0 + e) * a.ldy + n] = bf16_rne(acc[nb][e]);
+    }
+    return;
+  }
+  // partial sums: part[split][tb][cout][NTOK].  Partials and the arrival
+  // counter go through agent-scope (device-coherent) stores, loads and
+  // atomics, and each workgroup waits for its stores to complete before it
+  // counts itself in; nothing needs a whole-cache writeback or invalidate.
+  float* my = part + (((int64_t)split * n_tb + tb) * a.cout) * NTOK;
+  for (int nb = 0; nb < NB; ++nb)
+    for (int e = 0; e < 4; ++e)
+      __hip_atomic_store(my + (grow0 + e) * NTOK + 16 * nb + i16, acc[nb][e], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  unsigned* ctr = counters + (int64_t)trb * n_tb + tb;
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(splits - 1);
+  __syncthreads();
+  if (!s_last) return;
+  const int64_t grow_base = (int64_t)t * a.rows + rb * 64;
+  // Each thread owns OPT outputs; the splits are read 8 at a time with all
+  // loads of a batch in flight together, then added in split order.
+  constexpr int OPT = 64 * NTOK / 256;
+  const int64_t plane = (int64_t)n_tb * a.cout * NTOK;
+  const float* p0 = part + ((int64_t)tb * a.cout + grow_base) * NTOK;
+  float sum[OPT];
+  for (int k = 0; k < OPT; ++k) sum[k] = 0.f;
+  for (int sp0 = 0; sp0 < splits; sp0 += 8) {
+    float v[8][OPT];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int k = 0; k < OPT; ++k)
+        v[u][k] = __hip_atomic_load(p0 + min(sp0 + u, splits - 1) * plane + threadIdx.x + 256 * k, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int k = 0; k < OPT; ++k) sum[k] = (sp0 + u < splits) ? sum[k] + v[u][k] : sum[k];
+  }
+  for (int k = 0; k < OPT; ++k) {
+    const int o = threadIdx.x + 256 * k;
+    const int r = o / NTOK, n = o % NTOK;
+    if (n0 + n < a.batch) a.y[(grow_base + r) * a.ldy + n0 + n] = bf16_rne(sum[k]);
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next call
+}
+
+// ---------------------------------------------------------------------------
+// Prefill kernel (large batches, MFMA-bound).
+// Workgroup = 64 rows of one tile x NT tokens, 4 waves of 64 rows x NT/4
+// tokens.  Per K-block the workgroup gathers the block's X rows (NT tokens
+// each) into a double-buffered LDS tile while it multiplies the previous one:
+// dense blocks on v_mfma_f32_32x32x16_bf16, 2:4 blocks on
+// v_smfmac_f32_32x32x32_bf16, packed values loaded straight into the A
+// operand.  Workgroups are ordered so that each XCD works through one token
+// block across all tiles, keeping that X slice in its L2.  Y leaves through
+// LDS in 16-byte row chunks.
+// ---------------------------------------------------------------------------
+template <int NT>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
+  constexpr int PITCH = NT + 16;
+  constexpr int TW = NT / 4;          // tokens per wave
+  constexpr int NTB = TW / 32;        // 32-token blocks per wave
+  constexpr int CPR = NT / 8;         // 16-byte chunks per LDS row
+  constexpr int MAXCH = 64 * CPR / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][64 * PITCH];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nrb = a.rows / 64;
+  const int n_tr = a.n_tiles * nrb;
+  const int L = blockIdx.x, nwg = gridDim.x;
+  const int logical = (nwg % 8 == 0) ? (L % 8) * (nwg / 8) + L / 8 : L;
+  const int tb = logical / n_tr, trb = logical % n_tr;
+  const int t = trb / nrb, rb = trb % nrb;
+  const int n0 = tb * NT;
+  const int tok_w = wave * TW;
+  const int g = lane >> 4, i = lane & 15;
+  const int kcb = g >> 1;                       // B-operand K chunk (0..1)
+  const int colb = tok_w + 16 * (g & 1) + 4 * (i & 3);
+  const int kca = lane >> 5;                    // A-operand K chunk (0..1)
+  const int arow = rb * 64 + (lane & 31);       // tile row of A fragment for row block 0
+  const int nblk = a.nkb_d + a.nkb_s;
+
+  f32x16 acc[2][NTB];
+  for (int r = 0; r < 2; ++r)
+    for (int j = 0; j < NTB; ++j)
+      for (int e = 0; e < 16; ++e) acc[r][j][e] = 0.f;
+
+  u32x4 xr[MAXCH];
+  u32x4 a_cur[4], a_nxt[4];
+  uint64_t m_cur[2] = {0, 0}, m_nxt[2] = {0, 0};
+
+  auto load_x = [&](int b) {
+    const bool dense = b < a.nkb_d;
+    const int npos = dense ? 32 : 64;
+    const int32_t* idx = dense ? a.idx_d + ((int64_t)t * a.nkb_d + b) * 32
+                               : a.idx_s + ((int64_t)t * a.nkb_s + (b - a.nkb_d)) * 64;
+    for (int j = 0; j < MAXCH; ++j) {
+      const int q = threadIdx.x + 256 * j;
+      if (q < npos * CPR) xr[j] = load_x_chunk(a, idx[q / CPR], n0 + 8 * (q % CPR));
+    }
+  };
+  auto store_x = [&](int buf, int b) {
+    const int npos = b < a.nkb_d ? 32 : 64;
+    for (int j = 0; j < MAXCH; ++j) {
+      const int q = threadIdx.x + 256 * j;
+      if (q < npos * CPR) *reinterpret_cast<u32x4*>(&xs[buf][(q / CPR) * PITCH + 8 * (q % CPR)]) = xr[j];
+    }
+  };
+  auto load_a = [&](int b, u32x4* av, uint64_t* mv) {
+    if (b < a.nkb_d) {
+      const uint16_t* base = a.val_d + (((int64_t)t * a.nkb_d + b) * a.rows + arow) * 32 + 8 * kca;
+      for (int r = 0; r < 2; ++r)
+        for (int s = 0; s < 2; ++s) av[2 * r + s] = *reinterpret_cast<const u32x4*>(base + r * 32 * 32 + 16 * s);
+    } else {
+      const int64_t blk = ((int64_t)t * a.nkb_s + (b - a.nkb_d)) * a.rows + arow;
+      const uint16_t* base = a.val_s + blk * 32 + 8 * kca;
+      for (int r = 0; r < 2; ++r) {
+        for (int s = 0; s < 2; ++s) av[2 * r + s] = *reinterpret_cast<const u32x4*>(base + r * 32 * 32 + 16 * s);
+        mv[r] = a.meta[blk + 32 * r];
+      }
+    }
+  };
+  auto compute = [&](int buf, int b, const u32x4* av, const uint64_t* mv) {
+    const uint16_t* xb = xs[buf];
+    if (b < a.nkb_d) {
+      for (int s = 0; s < 2; ++s) {               // two K steps of 16 columns
+        for (int j = 0; j < NTB; ++j) {
+          const uint16_t* base = xb + colb + 32 * j;
+          const v4i16 b0 = tr_read(base + (16 * s + 8 * kcb + 0 + (i >> 2)) * PITCH);
+          const v4i16 b1 = tr_read(base + (16 * s + 8 * kcb + 4 + (i >> 2)) * PITCH);
+          const bf16x8 B = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+          for (int r = 0; r < 2; ++r)
+            acc[r][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[2 * r + s]), B,
+                                                                acc[r][j], 0, 0, 0);
+        }
+      }
+    } else {
+      for (int s = 0; s < 2; ++s) {               // two K steps of 32 positions
+        int sidx[2];
+        for (int r = 0; r < 2; ++r) sidx[r] = (int)((mv[r] >> (32 * s + 16 * kca)) & 0xffffull);
+        for (int j = 0; j < NTB; ++j) {
+          const uint16_t* base = xb + colb + 32 * j;
+          const int p0 = 32 * s + 8 * kcb + (i >> 2);
+          const v4i16 b0 = tr_read(base + (p0 + 0) * PITCH);
+          const v4i16 b1 = tr_read(base + (p0 + 4) * PITCH);
+          const v4i16 b2 = tr_read(base + (p0 + 16) * PITCH);
+          const v4i16 b3 = tr_read(base + (p0 + 20) * PITCH);
+          const bf16x16 B = __builtin_bit_cast(
+              bf16x16, __builtin_shufflevector(__builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7),
+                                               __builtin_shufflevector(b2, b3, 0, 1, 2, 3, 4, 5, 6, 7), 0, 1, 2, 3,
+                                               4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15));
+          for (int r = 0; r < 2; ++r)
+            acc[r][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(bf16x8, av[2 * r + s]), B,
+                                                                  acc[r][j], sidx[r], 0, 0);
+        }
+      }
+    }
+  };
+
+  if (nblk > 0) {
+    load_x(0);
+    load_a(0, a_cur, m_cur);
+    store_x(0, 0);
+    __syncthreads();
+    for (int b = 0; b < nblk; ++b) {
+      const bool more = b + 1 < nblk;
+      if (more) {
+        load_x(b + 1);
+        load_a(b + 1, a_nxt, m_nxt);
+      }
+      compute(b & 1, b, a_cur, m_cur);
+      if (more) store_x((b + 1) & 1, b + 1);
+      __syncthreads();
+      for (int k = 0; k < 4; ++k) a_cur[k] = a_nxt[k];
+      m_cur[0] = m_nxt[0];
+      m_cur[1] = m_nxt[1];
+    }
+  }
+
+  // ---- epilogue: bf16 tile through LDS, 16-byte row chunks to Y ----
+  // acc[r][j][e]: row 32r + 8(e/4) + 4(lane/32) + e%4, token tok_w + 32j + lane%32.
+  uint16_t* ys = xs[0];
+  for (int r = 0; r < 2; ++r)
+    for (int j = 0; j < NTB; ++j)
+      for (int e = 0; e < 16; ++e)
+        ys[(32 * r + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * PITCH + tok_w + 32 * j + (lane & 31)] =
+            bf16_rne(acc[r][j][e]);
+  __syncthreads();
+  const bool yvec = a.y_vec;
+  for (int q = threadIdx.x; q < 64 * CPR; q += 256) {
+    const int r = q / CPR, c = q % CPR;
+    const int n = n0 + 8 * c;
+    if (n >= a.batch) continue;
+    uint16_t* dst = a.y + ((int64_t)t * a.rows + rb * 64 + r) * a.ldy + n;
+    const uint16_t* src = ys + r * PITCH + 8 * c;
+    if (yvec && n + 8 <= a.batch) {
+      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+    } else {
+      for (int e = 0; e < 8 && n + e < a.batch; ++e) dst[e] = src[e];
+    }
+  }
+}
+
 }  // namespace
 
 namespace hinm {
@@ -233,7 +712,9 @@ extern "C" int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_
   }
   st = hinm::ensure_device();
   if (st) return st;
-  if ((int64_t)p.n_tiles * sh.n_rblocks > 65535) return fail(HINM_ESHAPE, "too many row blocks for one launch");
+  if (sh.path == hinm::kPathGeneric && (int64_t)p.n_tiles * sh.n_rblocks > 65535)
+    return fail(HINM_ESHAPE, "too many row blocks for one launch");
+  if (sh.path == hinm::kPathDecode && sh.n_tblocks > 65535) return fail(HINM_ESHAPE, "batch too large");
 
   SpmmArgs a;
   a.val_d = static_cast<const uint16_t*>(packed->val_dense);
@@ -243,7 +724,7 @@ extern "C" int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_
   a.idx_s = packed->idx_24;
   a.x = static_cast<const uint16_t*>(x_bf16);
   a.y = static_cast<uint16_t*>(y_bf16);
-  a.ws = static_cast<float*>(workspace);
+  a.ws = sh.ws_bytes > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + sh.ws_counter_bytes) : nullptr;
   a.ldx = ldx;
   a.ldy = ldy;
   a.batch = (int)batch;
@@ -257,18 +738,54 @@ extern "C" int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_
   a.splits = sh.splits;
   a.n_kunits = sh.n_kunits;
   a.x_vec = hinm::aligned(x_bf16, 16) && (ldx % 8 == 0);
+  a.y_vec = hinm::aligned(y_bf16, 16) && (ldy % 8 == 0);
+  a.n_tiles = p.n_tiles;
 
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
-  const dim3 grid(sh.n_tblocks, p.n_tiles * sh.n_rblocks, sh.splits), block(kWaves * 64);
-  switch (sh.nt) {
-    case 16: hipLaunchKernelGGL(spmm_kernel<16>, grid, block, 0, stream, a); break;
-    case 32: hipLaunchKernelGGL(spmm_kernel<32>, grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL(spmm_kernel<64>, grid, block, 0, stream, a); break;
-  }
-  if (sh.splits > 1) {
-    const int64_t n = (int64_t)p.cout * batch;
-    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a.ws, sh.splits, p.cout,
-                       (int)batch, a.batch_pad16, a.y, ldy);
+  if (sh.path == hinm::kPathDecodeSplit) {
+    const bool fast = a.x_vec && (batch % sh.nt == 0);
+    unsigned* counters = static_cast<unsigned*>(workspace);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + sh.ws_counter_bytes);
+    const dim3 grid(p.n_tiles * (p.tile_rows / 64) * sh.splits, sh.n_tblocks), block(256);
+    switch (sh.nt * 2 + (fast ? 1 : 0)) {
+      case 33: hipLaunchKernelGGL((decode4_kernel<16, 24, true>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
+      case 32: hipLaunchKernelGGL((decode4_kernel<16, 24, false>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
+      case 65: hipLaunchKernelGGL((decode4_kernel<32, 12, true>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
+      case 64: hipLaunchKernelGGL((decode4_kernel<32, 12, false>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
+      case 129: hipLaunchKernelGGL((decode4_kernel<64, 6, true>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
+      default: hipLaunchKernelGGL((decode4_kernel<64, 6, false>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
+    }
+  } else if (sh.path == hinm::kPathDecode) {
+    const dim3 grid(p.n_tiles * (p.tile_rows / 16), sh.n_tblocks), block(kDecWaves * 64);
+    const bool fast = a.x_vec && (batch % sh.nt == 0);
+    if (sh.nt == 16) {
+      if (fast) hipLaunchKernelGGL((decode3_kernel<16, 12, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((decode3_kernel<16, 12, false>), grid, block, 0, stream, a);
+    } else if (sh.nt == 32) {
+      if (fast) hipLaunchKernelGGL((decode3_kernel<32, 6, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((decode3_kernel<32, 6, false>), grid, block, 0, stream, a);
+    } else {
+      if (fast) hipLaunchKernelGGL((decode3_kernel<64, 3, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((decode3_kernel<64, 3, false>), grid, block, 0, stream, a);
+    }
+  } else if (sh.path == hinm::kPathPrefill) {
+    const int nwg = p.n_tiles * (p.tile_rows / 64) * sh.n_tblocks;
+    if (sh.nt == 256)
+      hipLaunchKernelGGL(prefill_kernel<256>, dim3(nwg), dim3(256), 0, stream, a, sh.n_tblocks);
+    else
+      hipLaunchKernelGGL(prefill_kernel<128>, dim3(nwg), dim3(256), 0, stream, a, sh.n_tblocks);
+  } else {
+    const dim3 grid(sh.n_tblocks, p.n_tiles * sh.n_rblocks, sh.splits), block(kWaves * 64);
+    switch (sh.nt) {
+      case 16: hipLaunchKernelGGL(spmm_kernel<16>, grid, block, 0, stream, a); break;
+      case 32: hipLaunchKernelGGL(spmm_kernel<32>, grid, block, 0, stream, a); break;
+      default: hipLaunchKernelGGL(spmm_kernel<64>, grid, block, 0, stream, a); break;
+    }
+    if (sh.splits > 1) {
+      const int64_t n = (int64_t)p.cout * batch;
+      hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a.ws, sh.splits,
+                         p.cout, (int)batch, a.batch_pad16, a.y, ldy);
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(HINM_EHIP, "spmm launch: %s", hipGetErrorString(e));

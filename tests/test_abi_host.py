@@ -101,12 +101,17 @@ def test_spmm_host_errors(lib):
     assert call(x=4097) == 5
     assert call(pk=_fake_packed(p, base=(1 << 20) + 8)) == 5
     assert call(pk=hinm.PackedT(p.raw, None, None, None, None, None)) == 1
-    # decode batch needs a split-K workspace
-    need = hinm.spmm_workspace_bytes(p, 16)
+    # the prefill path runs without a workspace; the split decode path needs one
+    assert hinm.spmm_workspace_bytes(p, 2048) == 0
+    assert hinm.spmm_workspace_bytes(p, 16) > 0
+    # tile_rows 48 takes the generic path, which splits K through the workspace
+    p48 = hinm.plan(96 * 8, 4096, 48, 0.5, 0.25)
+    need = hinm.spmm_workspace_bytes(p48, 100)
     assert need > 0
-    assert call(ws=None, wsb=0) == 6
-    assert call(ws=1 << 20, wsb=need - 1) == 6
-    assert call(ws=(1 << 20) + 16, wsb=need) == 5
+    pk48 = _fake_packed(p48)
+    assert call(pk=pk48, batch=100, ldx=100, ldy=100, ws=None, wsb=0) == 6
+    assert call(pk=pk48, batch=100, ldx=100, ldy=100, ws=1 << 20, wsb=need - 1) == 6
+    assert call(pk=pk48, batch=100, ldx=100, ldy=100, ws=(1 << 20) + 16, wsb=need) == 5
     assert call(batch=0, ldx=0, ldy=0) == 0          # empty batch is a no-op
     bad = hinm.PlanT.from_buffer_copy(p.raw)
     bad.n_dense += 1
@@ -136,6 +141,9 @@ def test_pack_host_errors(lib):
 
 def test_workspace_sizes(lib):
     p = hinm.plan(11008, 4096, 64, 0.75, 0.55)
-    assert hinm.spmm_workspace_bytes(p, 0) == 0
-    assert hinm.spmm_workspace_bytes(p, 2048) == 0        # enough workgroups without a split
-    assert hinm.spmm_workspace_bytes(p, 1) % 256 == 0
+    for b in (0, 65, 2048, 4096):
+        assert hinm.spmm_workspace_bytes(p, b) == 0
+    for b in (1, 16, 64):
+        assert hinm.spmm_workspace_bytes(p, b) % 4 == 0
+    p = hinm.plan(96, 4096, 48, 0.75, 0.55)
+    assert hinm.spmm_workspace_bytes(p, 200) % 256 == 0

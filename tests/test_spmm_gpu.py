@@ -112,7 +112,7 @@ def test_spmm_ragged_batches():
 def test_spmm_edge_shapes(args):
     cout, cin, R, t, v = args
     c = Case(synth.small(cout, cin, R, t, v, 1, seed=cout + cin))
-    for b in (1, 16, 70):
+    for b in (1, 16, 24, 40, 70):
         c.check(b, seed=b)
 
 
@@ -168,3 +168,20 @@ def test_spmm_empty_batch():
     c = Case(synth.small(64, 128, 64, 0.5, 0.25, 1, seed=1))
     y = hinm.spmm(c.pk, torch.empty(128, 0, dtype=torch.bfloat16, device=DEV))
     assert y.shape == (64, 0)
+
+
+def test_spmm_shared_workspace_across_shapes():
+    """One workspace serves products of different shapes and split counts in turn."""
+    ws = torch.zeros(1 << 24, dtype=torch.uint8, device=DEV)
+    cases = [Case(synth.small(256, 4096, 64, 0.75, 0.55, 1, seed=31)),
+             Case(synth.small(128, 1024, 64, 0.5, 0.25, 1, seed=32)),
+             Case(synth.small(96, 1024, 48, 0.5, 0.25, 1, seed=33)),      # generic path (tile_rows 48)
+             Case(synth.small(4096, 1024, 64, 0.6, 0.3, 1, seed=34))]     # many tiles
+    for rep in range(3):
+        for c in cases:
+            for b in (1, 16, 40, 100):
+                x = torch.randn(c.w.cin, b, generator=torch.Generator().manual_seed(rep * 100 + b)).to(torch.bfloat16)
+                y = hinm.spmm(c.pk, x.to(DEV), workspace=ws)
+                torch.cuda.synchronize()
+                xf = synth.as_f64(x)
+                check_y(y, c.w_hat @ xf, np.abs(c.w_hat) @ np.abs(xf), f"shared ws rep {rep} batch {b}")
