@@ -158,7 +158,7 @@ SpmmShape spmm_shape(const hinm_plan_t* p, int64_t batch) {
   }
   if (p->tile_rows % 64 == 0) {
     s.path = kPathPrefill;
-    s.nt = batch >= 512 ? 256 : 128;
+    s.nt = batch >= 1024 ? 256 : 128;
     const char* env = getenv("HINM_PREFILL_NT");
     if (env && (atoi(env) == 128 || atoi(env) == 256)) s.nt = atoi(env);
     s.n_tblocks = (int)((batch + s.nt - 1) / s.nt);

@@ -502,26 +502,202 @@ __global__ __launch_bounds__(256) void decode4_kernel(SpmmArgs a, int splits, in
 }
 
 // ---------------------------------------------------------------------------
-// Prefill kernel (large batches, MFMA-bound).
+// Prefill kernel, software-pipelined (large batches, tile_rows % 64 == 0).
 // Workgroup = 64 rows of one tile x NT tokens, 4 waves of 64 rows x NT/4
-// tokens.  Per K-block the workgroup gathers the block's X rows (NT tokens
-// each) into a double-buffered LDS tile while it multiplies the previous one:
-// dense blocks on v_mfma_f32_32x32x16_bf16, 2:4 blocks on
-// v_smfmac_f32_32x32x32_bf16, packed values loaded straight into the A
-// operand.  Workgroups are ordered so that each XCD works through one token
-// block across all tiles, keeping that X slice in its L2.  Y leaves through
-// LDS in 16-byte row chunks.
+// tokens.  K-blocks stream through a double-buffered LDS tile of gathered X
+// rows; while block b is multiplied, the X rows and packed values of block
+// b+1 are in flight into registers and the index slice of block b+2 is being
+// fetched.  Loads go through buffer resources with 32-bit offsets: a gathered
+// row costs one 24-bit multiply-add, and pad indices get an out-of-range
+// offset so the hardware returns zeros.  All loads are unconditional (a dense
+// block repeats its 32 rows into the unused half of the tile) and the loop is
+// unrolled twice over two register sets, so the code is straight-line.
+// Dense blocks: v_mfma_f32_32x32x16_bf16; 2:4 blocks:
+// v_smfmac_f32_32x32x32_bf16; B operands via ds_read_b64_tr_b16 from rows
+// whose pitch is 64 bytes mod 256, which keeps each pair of 16-lane groups
+// of a transpose read on disjoint banks.  Workgroups are ordered so each XCD
+// sweeps one token block across all tiles.  Y leaves through LDS in 16-byte
+// row chunks.
 // ---------------------------------------------------------------------------
+constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9)
+constexpr uint32_t kOob = 0xFFFFFFF0u;     // offset past every buffer: loads return zeros
+
+template <int NT>
+struct PrefillCfg {
+  static constexpr int PITCH = NT + 32;       // bf16 per LDS row: 64 bytes mod 256
+  static constexpr int TW = NT / 4;           // tokens per wave
+  static constexpr int NTB = TW / 32;         // 32-token MFMA blocks per wave
+  static constexpr int CPR = NT / 8;          // 16-byte chunks per gathered row
+  static constexpr int PG = 256 / CPR;        // position groups per workgroup
+  static constexpr int PPT = 64 / PG;         // consecutive positions per thread
+};
+
+template <int NT>
+struct PrefillStage {
+  u32x4 x[PrefillCfg<NT>::PPT];
+  u32x4 av[4];
+  uint64_t mv[2];
+};
+
+struct PrefillRes {
+  __amdgpu_buffer_rsrc_t x, vd, vs, meta, id, is;
+  uint32_t ldx_bytes;
+};
+
+// One region's K-blocks [0, nb) (DENSE: 32-column blocks, else 2:4 blocks of
+// 64 positions), pipelined as described above.  Keeping the two regions in
+// separate loops keeps the accumulators in fixed registers.
+template <int NT, bool FAST, bool DENSE>
+__device__ inline void prefill_phase(const SpmmArgs& a, const PrefillRes& res, uint16_t* xs0, uint16_t* xs1, int t,
+                                     int rb, int n0, f32x16 (&acc)[2][PrefillCfg<NT>::NTB]) {
+  using C = PrefillCfg<NT>;
+  const int nb = DENSE ? a.nkb_d : a.nkb_s;
+  if (nb == 0) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tok_w = wave * C::TW;
+  const int g = lane >> 4, i = lane & 15;
+  const int kcb = g >> 1;                       // B-operand K chunk (0..1)
+  const int colb = tok_w + 16 * (g & 1) + 4 * (i & 3);
+  const int kca = lane >> 5;                    // A-operand K chunk (0..1)
+  const int cnk = threadIdx.x % C::CPR;
+  const int pbase = (threadIdx.x / C::CPR) * C::PPT;     // first of this thread's PPT positions
+  const uint32_t xcol = (uint32_t)(n0 + 8 * cnk) * 2u;
+  constexpr uint32_t KPOS = DENSE ? 32u : 64u;
+  const uint32_t ipos = DENSE ? (uint32_t)(pbase & 31) : (uint32_t)pbase;   // dense: rows 32..63 repeat 0..31
+  const uint32_t aoff = (uint32_t)(rb * 64 + (lane & 31)) * 64u + 16u * kca;
+  const uint32_t moff0 = (uint32_t)(rb * 64 + (lane & 31)) * 8u;
+  const __amdgpu_buffer_rsrc_t rid = DENSE ? res.id : res.is;
+  const __amdgpu_buffer_rsrc_t rv = DENSE ? res.vd : res.vs;
+
+  auto load_idx = [&](int b, int (&ci)[C::PPT]) {
+    b = min(b, nb - 1);
+    const uint32_t off = ((uint32_t)(t * nb + b) * KPOS + ipos) * 4u;
+#pragma unroll
+    for (int j = 0; j < C::PPT; j += 4) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rid, off + 4u * j, 0, 0);
+      for (int k = 0; k < 4; ++k) ci[j + k] = (int)v[k];
+    }
+  };
+  auto load_x = [&](const int (&ci)[C::PPT], PrefillStage<NT>& st) {
+#pragma unroll
+    for (int j = 0; j < C::PPT; ++j) {
+      if constexpr (FAST) {
+        const uint32_t off = ci[j] < 0 ? kOob : __umul24((uint32_t)ci[j], res.ldx_bytes) + xcol;
+        st.x[j] = __builtin_amdgcn_raw_buffer_load_b128(res.x, off, 0, 0);
+      } else {
+        st.x[j] = load_x_chunk(a, ci[j], n0 + 8 * cnk);
+      }
+    }
+  };
+  auto load_a = [&](int b, PrefillStage<NT>& st) {
+    b = min(b, nb - 1);
+    const uint32_t blk = (uint32_t)(t * nb + b);
+    const uint32_t off = blk * (uint32_t)a.rows * 64u + aoff;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        st.av[2 * r + s] = __builtin_amdgcn_raw_buffer_load_b128(rv, off + r * 2048u + 32u * s, 0, 0);
+      if constexpr (!DENSE) {
+        const uint32_t moff = blk * (uint32_t)a.rows * 8u + moff0 + 256u * r;
+        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(res.meta, moff, 0, 0);
+        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(res.meta, moff + 4u, 0, 0);
+        st.mv[r] = (uint64_t)lo | ((uint64_t)hi << 32);
+      }
+    }
+  };
+  auto store_x = [&](uint16_t* xs, const PrefillStage<NT>& st) {
+#pragma unroll
+    for (int j = 0; j < C::PPT; ++j) *reinterpret_cast<u32x4*>(xs + (pbase + j) * C::PITCH + 8 * cnk) = st.x[j];
+  };
+  auto compute = [&](const uint16_t* xb, const PrefillStage<NT>& st) {
+    if constexpr (DENSE) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {               // two K steps of 16 columns
+#pragma unroll
+        for (int j = 0; j < C::NTB; ++j) {
+          const uint16_t* base = xb + colb + 32 * j;
+          const v4i16 b0 = tr_read(base + (16 * s + 8 * kcb + 0 + (i >> 2)) * C::PITCH);
+          const v4i16 b1 = tr_read(base + (16 * s + 8 * kcb + 4 + (i >> 2)) * C::PITCH);
+          const bf16x8 B = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int r = 0; r < 2; ++r)
+            acc[r][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, st.av[2 * r + s]), B,
+                                                                acc[r][j], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {               // two K steps of 32 positions
+        int sidx[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) sidx[r] = (int)((st.mv[r] >> (32 * s + 16 * kca)) & 0xffffull);
+#pragma unroll
+        for (int j = 0; j < C::NTB; ++j) {
+          const uint16_t* base = xb + colb + 32 * j;
+          const int p0 = 32 * s + 8 * kcb + (i >> 2);
+          const v4i16 b0 = tr_read(base + (p0 + 0) * C::PITCH);
+          const v4i16 b1 = tr_read(base + (p0 + 4) * C::PITCH);
+          const v4i16 b2 = tr_read(base + (p0 + 16) * C::PITCH);
+          const v4i16 b3 = tr_read(base + (p0 + 20) * C::PITCH);
+          const bf16x16 B = __builtin_bit_cast(
+              bf16x16, __builtin_shufflevector(__builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7),
+                                               __builtin_shufflevector(b2, b3, 0, 1, 2, 3, 4, 5, 6, 7), 0, 1, 2, 3,
+                                               4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15));
+#pragma unroll
+          for (int r = 0; r < 2; ++r)
+            acc[r][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(bf16x8, st.av[2 * r + s]), B,
+                                                                  acc[r][j], sidx[r], 0, 0);
+        }
+      }
+    }
+  };
+
+  __syncthreads();                   // the LDS tiles may still be read by the previous phase
+  PrefillStage<NT> S0, S1;
+  int iA[C::PPT], iB[C::PPT];
+  load_idx(0, iA);
+  load_idx(1, iB);
+  load_x(iA, S0);
+  load_a(0, S0);
+  load_idx(2, iA);
+  store_x(xs0, S0);
+  load_x(iB, S1);
+  load_a(1, S1);
+  __syncthreads();
+  // steady state, two blocks per trip: block b uses (xs0, S0), block b+1 uses (xs1, S1).
+  int b = 0;
+  for (; b + 2 <= nb; b += 2) {
+    load_idx(b + 3, iB);
+    compute(xs0, S0);
+    store_x(xs1, S1);
+    load_x(iA, S0);                  // X(b+2)
+    load_a(b + 2, S0);
+    __syncthreads();
+    load_idx(b + 4, iA);
+    compute(xs1, S1);
+    store_x(xs0, S0);
+    load_x(iB, S1);                  // X(b+3)
+    load_a(b + 3, S1);
+    __syncthreads();
+  }
+  if (b < nb) compute(xs0, S0);
+}
+
+template <int NT, bool FAST>
+__device__ inline void prefill_body(const SpmmArgs& a, const PrefillRes& res, uint16_t* xs0, uint16_t* xs1, int t,
+                                    int rb, int n0, f32x16 (&acc)[2][PrefillCfg<NT>::NTB]) {
+  prefill_phase<NT, FAST, true>(a, res, xs0, xs1, t, rb, n0, acc);
+  prefill_phase<NT, FAST, false>(a, res, xs0, xs1, t, rb, n0, acc);
+}
+
 template <int NT>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
-  constexpr int PITCH = NT + 16;
-  constexpr int TW = NT / 4;          // tokens per wave
-  constexpr int NTB = TW / 32;        // 32-token blocks per wave
-  constexpr int CPR = NT / 8;         // 16-byte chunks per LDS row
-  constexpr int MAXCH = 64 * CPR / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][64 * PITCH];
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  using C = PrefillCfg<NT>;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][64 * C::PITCH];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nrb = a.rows / 64;
   const int n_tr = a.n_tiles * nrb;
   const int L = blockIdx.x, nwg = gridDim.x;
@@ -529,128 +705,42 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
   const int tb = logical / n_tr, trb = logical % n_tr;
   const int t = trb / nrb, rb = trb % nrb;
   const int n0 = tb * NT;
-  const int tok_w = wave * TW;
-  const int g = lane >> 4, i = lane & 15;
-  const int kcb = g >> 1;                       // B-operand K chunk (0..1)
-  const int colb = tok_w + 16 * (g & 1) + 4 * (i & 3);
-  const int kca = lane >> 5;                    // A-operand K chunk (0..1)
-  const int arow = rb * 64 + (lane & 31);       // tile row of A fragment for row block 0
-  const int nblk = a.nkb_d + a.nkb_s;
+  const int tok_w = wave * C::TW;
 
-  f32x16 acc[2][NTB];
+  PrefillRes res;
+  const uint32_t xbytes = (uint32_t)(((int64_t)(a.cin - 1) * a.ldx + a.batch) * 2);
+  res.x = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, (int)xbytes, kBufferWord3);
+  res.vd = __builtin_amdgcn_make_buffer_rsrc((void*)a.val_d, (short)0, (int)((uint32_t)a.n_tiles * a.nkb_d * a.rows * 64u), kBufferWord3);
+  res.vs = __builtin_amdgcn_make_buffer_rsrc((void*)a.val_s, (short)0, (int)((uint32_t)a.n_tiles * a.nkb_s * a.rows * 64u), kBufferWord3);
+  res.meta = __builtin_amdgcn_make_buffer_rsrc((void*)a.meta, (short)0, (int)((uint32_t)a.n_tiles * a.nkb_s * a.rows * 8u), kBufferWord3);
+  res.id = __builtin_amdgcn_make_buffer_rsrc((void*)a.idx_d, (short)0, (int)((uint32_t)a.n_tiles * a.nkb_d * 32u * 4u), kBufferWord3);
+  res.is = __builtin_amdgcn_make_buffer_rsrc((void*)a.idx_s, (short)0, (int)((uint32_t)a.n_tiles * a.nkb_s * 64u * 4u), kBufferWord3);
+  res.ldx_bytes = (uint32_t)a.ldx * 2u;
+
+  f32x16 acc[2][C::NTB];
   for (int r = 0; r < 2; ++r)
-    for (int j = 0; j < NTB; ++j)
+    for (int j = 0; j < C::NTB; ++j)
       for (int e = 0; e < 16; ++e) acc[r][j][e] = 0.f;
 
-  u32x4 xr[MAXCH];
-  u32x4 a_cur[4], a_nxt[4];
-  uint64_t m_cur[2] = {0, 0}, m_nxt[2] = {0, 0};
+  if (a.x_vec && n0 + NT <= a.batch) prefill_body<NT, true>(a, res, xs[0], xs[1], t, rb, n0, acc);
+  else prefill_body<NT, false>(a, res, xs[0], xs[1], t, rb, n0, acc);
+  __syncthreads();
 
-  auto load_x = [&](int b) {
-    const bool dense = b < a.nkb_d;
-    const int npos = dense ? 32 : 64;
-    const int32_t* idx = dense ? a.idx_d + ((int64_t)t * a.nkb_d + b) * 32
-                               : a.idx_s + ((int64_t)t * a.nkb_s + (b - a.nkb_d)) * 64;
-    for (int j = 0; j < MAXCH; ++j) {
-      const int q = threadIdx.x + 256 * j;
-      if (q < npos * CPR) xr[j] = load_x_chunk(a, idx[q / CPR], n0 + 8 * (q % CPR));
-    }
-  };
-  auto store_x = [&](int buf, int b) {
-    const int npos = b < a.nkb_d ? 32 : 64;
-    for (int j = 0; j < MAXCH; ++j) {
-      const int q = threadIdx.x + 256 * j;
-      if (q < npos * CPR) *reinterpret_cast<u32x4*>(&xs[buf][(q / CPR) * PITCH + 8 * (q % CPR)]) = xr[j];
-    }
-  };
-  auto load_a = [&](int b, u32x4* av, uint64_t* mv) {
-    if (b < a.nkb_d) {
-      const uint16_t* base = a.val_d + (((int64_t)t * a.nkb_d + b) * a.rows + arow) * 32 + 8 * kca;
-      for (int r = 0; r < 2; ++r)
-        for (int s = 0; s < 2; ++s) av[2 * r + s] = *reinterpret_cast<const u32x4*>(base + r * 32 * 32 + 16 * s);
-    } else {
-      const int64_t blk = ((int64_t)t * a.nkb_s + (b - a.nkb_d)) * a.rows + arow;
-      const uint16_t* base = a.val_s + blk * 32 + 8 * kca;
-      for (int r = 0; r < 2; ++r) {
-        for (int s = 0; s < 2; ++s) av[2 * r + s] = *reinterpret_cast<const u32x4*>(base + r * 32 * 32 + 16 * s);
-        mv[r] = a.meta[blk + 32 * r];
-      }
-    }
-  };
-  auto compute = [&](int buf, int b, const u32x4* av, const uint64_t* mv) {
-    const uint16_t* xb = xs[buf];
-    if (b < a.nkb_d) {
-      for (int s = 0; s < 2; ++s) {               // two K steps of 16 columns
-        for (int j = 0; j < NTB; ++j) {
-          const uint16_t* base = xb + colb + 32 * j;
-          const v4i16 b0 = tr_read(base + (16 * s + 8 * kcb + 0 + (i >> 2)) * PITCH);
-          const v4i16 b1 = tr_read(base + (16 * s + 8 * kcb + 4 + (i >> 2)) * PITCH);
-          const bf16x8 B = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
-          for (int r = 0; r < 2; ++r)
-            acc[r][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[2 * r + s]), B,
-                                                                acc[r][j], 0, 0, 0);
-        }
-      }
-    } else {
-      for (int s = 0; s < 2; ++s) {               // two K steps of 32 positions
-        int sidx[2];
-        for (int r = 0; r < 2; ++r) sidx[r] = (int)((mv[r] >> (32 * s + 16 * kca)) & 0xffffull);
-        for (int j = 0; j < NTB; ++j) {
-          const uint16_t* base = xb + colb + 32 * j;
-          const int p0 = 32 * s + 8 * kcb + (i >> 2);
-          const v4i16 b0 = tr_read(base + (p0 + 0) * PITCH);
-          const v4i16 b1 = tr_read(base + (p0 + 4) * PITCH);
-          const v4i16 b2 = tr_read(base + (p0 + 16) * PITCH);
-          const v4i16 b3 = tr_read(base + (p0 + 20) * PITCH);
-          const bf16x16 B = __builtin_bit_cast(
-              bf16x16, __builtin_shufflevector(__builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7),
-                                               __builtin_shufflevector(b2, b3, 0, 1, 2, 3, 4, 5, 6, 7), 0, 1, 2, 3,
-                                               4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15));
-          for (int r = 0; r < 2; ++r)
-            acc[r][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(bf16x8, av[2 * r + s]), B,
-                                                                  acc[r][j], sidx[r], 0, 0);
-        }
-      }
-    }
-  };
-
-  if (nblk > 0) {
-    load_x(0);
-    load_a(0, a_cur, m_cur);
-    store_x(0, 0);
-    __syncthreads();
-    for (int b = 0; b < nblk; ++b) {
-      const bool more = b + 1 < nblk;
-      if (more) {
-        load_x(b + 1);
-        load_a(b + 1, a_nxt, m_nxt);
-      }
-      compute(b & 1, b, a_cur, m_cur);
-      if (more) store_x((b + 1) & 1, b + 1);
-      __syncthreads();
-      for (int k = 0; k < 4; ++k) a_cur[k] = a_nxt[k];
-      m_cur[0] = m_nxt[0];
-      m_cur[1] = m_nxt[1];
-    }
-  }
-
-  // ---- epilogue: bf16 tile through LDS, 16-byte row chunks to Y ----
-  // acc[r][j][e]: row 32r + 8(e/4) + 4(lane/32) + e%4, token tok_w + 32j + lane%32.
+  // epilogue: acc[r][j][e] is row 32r + 8(e/4) + 4(lane/32) + e%4, token tok_w + 32j + lane%32.
   uint16_t* ys = xs[0];
   for (int r = 0; r < 2; ++r)
-    for (int j = 0; j < NTB; ++j)
+    for (int j = 0; j < C::NTB; ++j)
       for (int e = 0; e < 16; ++e)
-        ys[(32 * r + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * PITCH + tok_w + 32 * j + (lane & 31)] =
+        ys[(32 * r + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * C::PITCH + tok_w + 32 * j + (lane & 31)] =
             bf16_rne(acc[r][j][e]);
   __syncthreads();
-  const bool yvec = a.y_vec;
-  for (int q = threadIdx.x; q < 64 * CPR; q += 256) {
-    const int r = q / CPR, c = q % CPR;
+  for (int q = threadIdx.x; q < 64 * C::CPR; q += 256) {
+    const int r = q / C::CPR, c = q % C::CPR;
     const int n = n0 + 8 * c;
     if (n >= a.batch) continue;
     uint16_t* dst = a.y + ((int64_t)t * a.rows + rb * 64 + r) * a.ldy + n;
-    const uint16_t* src = ys + r * PITCH + 8 * c;
-    if (yvec && n + 8 <= a.batch) {
+    const uint16_t* src = ys + r * C::PITCH + 8 * c;
+    if (a.y_vec && n + 8 <= a.batch) {
       *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
     } else {
       for (int e = 0; e < 8 && n + e < a.batch; ++e) dst[e] = src[e];
@@ -703,7 +793,7 @@ extern "C" int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_
     if (b.bytes > 0 && !b.ptr) return fail(HINM_EINVAL, "%s is NULL but holds %lld bytes", b.name, (long long)b.bytes);
     if (b.ptr && !hinm::aligned(b.ptr, 16)) return fail(HINM_EALIGN, "%s is not 16-byte aligned", b.name);
   }
-  const hinm::SpmmShape sh = hinm::spmm_shape(&p, batch);
+  hinm::SpmmShape sh = hinm::spmm_shape(&p, batch);
   if (sh.ws_bytes > 0) {
     if (!workspace || workspace_bytes < (size_t)sh.ws_bytes)
       return fail(HINM_EWORKSPACE, "spmm workspace of %zu bytes given, %lld needed", workspace_bytes,
@@ -742,6 +832,21 @@ extern "C" int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_
   a.n_tiles = p.n_tiles;
 
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  if (sh.path == hinm::kPathPrefill) {
+    // The prefill kernel addresses X and the packed buffers with 32-bit
+    // offsets and gathers with a 24-bit multiply; beyond those ranges the
+    // generic kernel (without a K split, so no workspace) takes over.
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t xbytes = ((int64_t)(p.cin - 1) * ldx + batch) * 2;
+    if (xbytes >= lim || ldx * 2 >= ((int64_t)1 << 24) || p.bytes_val_dense >= lim || p.bytes_val_24 >= lim ||
+        p.bytes_idx_dense >= lim || p.bytes_idx_24 >= lim || p.bytes_meta_24 >= lim) {
+      sh.path = hinm::kPathGeneric;
+      sh.nt = 64;
+      sh.n_tblocks = (int)((batch + 63) / 64);
+      sh.splits = 1;
+      a.splits = 1;
+    }
+  }
   if (sh.path == hinm::kPathDecodeSplit) {
     const bool fast = a.x_vec && (batch % sh.nt == 0);
     unsigned* counters = static_cast<unsigned*>(workspace);
@@ -770,10 +875,11 @@ extern "C" int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_
     }
   } else if (sh.path == hinm::kPathPrefill) {
     const int nwg = p.n_tiles * (p.tile_rows / 64) * sh.n_tblocks;
-    if (sh.nt == 256)
+    if (sh.nt == 256) {
       hipLaunchKernelGGL(prefill_kernel<256>, dim3(nwg), dim3(256), 0, stream, a, sh.n_tblocks);
-    else
+    } else {
       hipLaunchKernelGGL(prefill_kernel<128>, dim3(nwg), dim3(256), 0, stream, a, sh.n_tblocks);
+    }
   } else {
     const dim3 grid(sh.n_tblocks, p.n_tiles * sh.n_rblocks, sh.splits), block(kWaves * 64);
     switch (sh.nt) {
