@@ -18,6 +18,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "hinm_internal.h"
@@ -529,14 +530,14 @@ struct PrefillCfg {
   static constexpr int NTB = TW / 32;         // 32-token MFMA blocks per wave
   static constexpr int CPR = NT / 8;          // 16-byte chunks per gathered row
   static constexpr int PG = 256 / CPR;        // position groups per workgroup
-  static constexpr int PPT = 64 / PG;         // consecutive positions per thread
+  static constexpr int DA = 4;                // packed-value prefetch depth (blocks)
 };
 
-template <int NT>
-struct PrefillStage {
-  u32x4 x[PrefillCfg<NT>::PPT];
-  u32x4 av[4];
-  uint64_t mv[2];
+// This thread's share of one block's packed values (16 bytes) and 2:4
+// metadata (4 bytes, threads 0..127) on the way to LDS.
+struct PrefillA {
+  u32x4 v;
+  uint32_t m;
 };
 
 struct PrefillRes {
@@ -545,12 +546,29 @@ struct PrefillRes {
 };
 
 // One region's K-blocks [0, nb) (DENSE: 32-column blocks, else 2:4 blocks of
-// 64 positions), pipelined as described above.  Keeping the two regions in
-// separate loops keeps the accumulators in fixed registers.
+// 64 positions), pipelined.  Keeping the two regions in separate loops keeps
+// the accumulators in fixed registers.
+//
+// Every byte a workgroup needs is fetched once per workgroup:
+//   - X: thread (position group, chunk) gathers PPT rows x 16 bytes; the 64
+//     positions of a 2:4 block give PPT = 64 / PG, the 32 of a dense block
+//     PPT / 2.
+//   - indices: each wave fetches the WP indices of its own positions with one
+//     32-bit load per lane and hands them out with ds_bpermute.
+//   - packed values: one 16-byte load per thread covers the 64 rows x 64
+//     bytes of a block; they are written into the 64-byte padding at the end
+//     of each X row of the LDS tile (row r's chunk c at chunk c ^ (r/4 % 4),
+//     so 16 consecutive rows of one chunk fall on distinct banks).
+//   - 2:4 metadata: 512 bytes per block, one dword per thread of waves 0-1,
+//     into a small LDS array.
 template <int NT, bool FAST, bool DENSE>
-__device__ inline void prefill_phase(const SpmmArgs& a, const PrefillRes& res, uint16_t* xs0, uint16_t* xs1, int t,
-                                     int rb, int n0, f32x16 (&acc)[2][PrefillCfg<NT>::NTB]) {
+__device__ inline void prefill_phase(const SpmmArgs& a, const PrefillRes& res, uint16_t* xs0, uint16_t* xs1,
+                                     uint32_t* ms0, uint32_t* ms1, int t, int rb, int n0,
+                                     f32x16 (&acc)[2][PrefillCfg<NT>::NTB]) {
   using C = PrefillCfg<NT>;
+  constexpr int KPOS = DENSE ? 32 : 64;       // positions per block
+  constexpr int PPT = KPOS / C::PG;           // gathered rows per thread
+  constexpr int WP = KPOS / 4;                // positions per wave
   const int nb = DENSE ? a.nkb_d : a.nkb_s;
   if (nb == 0) return;
   const int lane = threadIdx.x & 63;
@@ -561,57 +579,57 @@ __device__ inline void prefill_phase(const SpmmArgs& a, const PrefillRes& res, u
   const int colb = tok_w + 16 * (g & 1) + 4 * (i & 3);
   const int kca = lane >> 5;                    // A-operand K chunk (0..1)
   const int cnk = threadIdx.x % C::CPR;
-  const int pbase = (threadIdx.x / C::CPR) * C::PPT;     // first of this thread's PPT positions
+  const int pbase = (threadIdx.x / C::CPR) * PPT;          // first of this thread's PPT positions
+  const int psrc = (lane / C::CPR) * PPT;                  // same, relative to the wave's WP positions
   const uint32_t xcol = (uint32_t)(n0 + 8 * cnk) * 2u;
-  constexpr uint32_t KPOS = DENSE ? 32u : 64u;
-  const uint32_t ipos = DENSE ? (uint32_t)(pbase & 31) : (uint32_t)pbase;   // dense: rows 32..63 repeat 0..31
-  const uint32_t aoff = (uint32_t)(rb * 64 + (lane & 31)) * 64u + 16u * kca;
-  const uint32_t moff0 = (uint32_t)(rb * 64 + (lane & 31)) * 8u;
+  const uint32_t ipos = (uint32_t)(wave * WP + (lane % WP));
   const __amdgpu_buffer_rsrc_t rid = DENSE ? res.id : res.is;
   const __amdgpu_buffer_rsrc_t rv = DENSE ? res.vd : res.vs;
+  const uint32_t vrow = (uint32_t)rb * 64u;
+  const int arow = threadIdx.x >> 2;                       // value row this thread stores
+  const int acol = C::PITCH * arow + NT + 8 * ((threadIdx.x & 3) ^ ((arow >> 2) & 3));
 
-  auto load_idx = [&](int b, int (&ci)[C::PPT]) {
+  auto load_idx = [&](int b) -> int {
     b = min(b, nb - 1);
     const uint32_t off = ((uint32_t)(t * nb + b) * KPOS + ipos) * 4u;
-#pragma unroll
-    for (int j = 0; j < C::PPT; j += 4) {
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rid, off + 4u * j, 0, 0);
-      for (int k = 0; k < 4; ++k) ci[j + k] = (int)v[k];
-    }
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(rid, off, 0, 0);
   };
-  auto load_x = [&](const int (&ci)[C::PPT], PrefillStage<NT>& st) {
+  auto load_x = [&](int iw, u32x4 (&st)[PPT]) {
 #pragma unroll
-    for (int j = 0; j < C::PPT; ++j) {
+    for (int j = 0; j < PPT; ++j) {
+      const int ci = __builtin_amdgcn_ds_bpermute(4 * (psrc + j), iw);
       if constexpr (FAST) {
-        const uint32_t off = ci[j] < 0 ? kOob : __umul24((uint32_t)ci[j], res.ldx_bytes) + xcol;
-        st.x[j] = __builtin_amdgcn_raw_buffer_load_b128(res.x, off, 0, 0);
+        const uint32_t off = ci < 0 ? kOob : __umul24((uint32_t)ci, res.ldx_bytes) + xcol;
+        st[j] = __builtin_amdgcn_raw_buffer_load_b128(res.x, off, 0, 0);
       } else {
-        st.x[j] = load_x_chunk(a, ci[j], n0 + 8 * cnk);
+        st[j] = load_x_chunk(a, ci, n0 + 8 * cnk);
       }
     }
   };
-  auto load_a = [&](int b, PrefillStage<NT>& st) {
+  auto load_a = [&](int b, PrefillA& st) {
     b = min(b, nb - 1);
-    const uint32_t blk = (uint32_t)(t * nb + b);
-    const uint32_t off = blk * (uint32_t)a.rows * 64u + aoff;
+    const uint32_t blk = (uint32_t)(t * nb + b) * (uint32_t)a.rows + vrow;
+    st.v = __builtin_amdgcn_raw_buffer_load_b128(rv, blk * 64u + 16u * threadIdx.x, 0, 0);
+    if constexpr (!DENSE)
+      st.m = __builtin_amdgcn_raw_buffer_load_b32(res.meta, threadIdx.x < 128 ? blk * 8u + 4u * threadIdx.x : kOob,
+                                                  0, 0);
+  };
+  auto store = [&](uint16_t* xs, uint32_t* ms, const u32x4 (&x)[PPT], const PrefillA& st) {
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) *reinterpret_cast<u32x4*>(xs + (pbase + j) * C::PITCH + 8 * cnk) = x[j];
+    *reinterpret_cast<u32x4*>(xs + acol) = st.v;
+    if constexpr (!DENSE)
+      if (threadIdx.x < 128) ms[threadIdx.x] = st.m;
+  };
+  auto compute = [&](const uint16_t* xb, const uint32_t* ms) {
+    u32x4 av[4];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
+      const int row = 32 * r + (lane & 31);
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        st.av[2 * r + s] = __builtin_amdgcn_raw_buffer_load_b128(rv, off + r * 2048u + 32u * s, 0, 0);
-      if constexpr (!DENSE) {
-        const uint32_t moff = blk * (uint32_t)a.rows * 8u + moff0 + 256u * r;
-        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(res.meta, moff, 0, 0);
-        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(res.meta, moff + 4u, 0, 0);
-        st.mv[r] = (uint64_t)lo | ((uint64_t)hi << 32);
-      }
+        av[2 * r + s] = *reinterpret_cast<const u32x4*>(xb + row * C::PITCH + NT + 8 * ((2 * s + kca) ^ ((row >> 2) & 3)));
     }
-  };
-  auto store_x = [&](uint16_t* xs, const PrefillStage<NT>& st) {
-#pragma unroll
-    for (int j = 0; j < C::PPT; ++j) *reinterpret_cast<u32x4*>(xs + (pbase + j) * C::PITCH + 8 * cnk) = st.x[j];
-  };
-  auto compute = [&](const uint16_t* xb, const PrefillStage<NT>& st) {
     if constexpr (DENSE) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {               // two K steps of 16 columns
@@ -623,16 +641,18 @@ __device__ inline void prefill_phase(const SpmmArgs& a, const PrefillRes& res, u
           const bf16x8 B = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
           for (int r = 0; r < 2; ++r)
-            acc[r][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, st.av[2 * r + s]), B,
+            acc[r][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[2 * r + s]), B,
                                                                 acc[r][j], 0, 0, 0);
         }
       }
     } else {
+      const uint64_t* mt = reinterpret_cast<const uint64_t*>(ms);
+      const uint64_t mv[2] = {mt[lane & 31], mt[32 + (lane & 31)]};
 #pragma unroll
       for (int s = 0; s < 2; ++s) {               // two K steps of 32 positions
         int sidx[2];
 #pragma unroll
-        for (int r = 0; r < 2; ++r) sidx[r] = (int)((st.mv[r] >> (32 * s + 16 * kca)) & 0xffffull);
+        for (int r = 0; r < 2; ++r) sidx[r] = (int)((mv[r] >> (32 * s + 16 * kca)) & 0xffffull);
 #pragma unroll
         for (int j = 0; j < C::NTB; ++j) {
           const uint16_t* base = xb + colb + 32 * j;
@@ -647,7 +667,7 @@ __device__ inline void prefill_phase(const SpmmArgs& a, const PrefillRes& res, u
                                                4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15));
 #pragma unroll
           for (int r = 0; r < 2; ++r)
-            acc[r][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(bf16x8, st.av[2 * r + s]), B,
+            acc[r][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(bf16x8, av[2 * r + s]), B,
                                                                   acc[r][j], sidx[r], 0, 0);
         }
       }
@@ -655,56 +675,72 @@ __device__ inline void prefill_phase(const SpmmArgs& a, const PrefillRes& res, u
   };
 
   __syncthreads();                   // the LDS tiles may still be read by the previous phase
-  PrefillStage<NT> S0, S1;
-  int iA[C::PPT], iB[C::PPT];
-  load_idx(0, iA);
-  load_idx(1, iB);
-  load_x(iA, S0);
-  load_a(0, S0);
-  load_idx(2, iA);
-  store_x(xs0, S0);
-  load_x(iB, S1);
-  load_a(1, S1);
+  // Register sets: packed values of DA blocks (A[b % DA]), X rows of 2 blocks
+  // (X[b % 2]), index words of 2 blocks (I[b % 2]).  At block bb: compute bb
+  // from LDS tile bb % 2; write X(bb+1) and the values of bb+1 to the other
+  // tile; issue X(bb+2), values(bb+DA) and indices(bb+3).  The packed values
+  // run further ahead because they come from HBM or the last-level cache,
+  // while the X slice stays in L2.
+  constexpr int DA = C::DA;
+  PrefillA A[DA];
+  u32x4 X[2][PPT];
+  int I[2];
+  uint16_t* const tile[2] = {xs0, xs1};
+  uint32_t* const mtile[2] = {ms0, ms1};
+  I[0] = load_idx(0);
+  I[1] = load_idx(1);
+  load_x(I[0], X[0]);
+  load_a(0, A[0]);
+  load_x(I[1], X[1]);
+#pragma unroll
+  for (int d = 1; d < DA; ++d) load_a(d, A[d]);
+  I[0] = load_idx(2);
+  store(tile[0], mtile[0], X[0], A[0]);
   __syncthreads();
-  // steady state, two blocks per trip: block b uses (xs0, S0), block b+1 uses (xs1, S1).
+  auto step = [&](auto kc, int bb) {
+    constexpr int k = decltype(kc)::value;
+    I[(k + 1) % 2] = load_idx(bb + 3);
+    compute(tile[k % 2], mtile[k % 2]);
+    store(tile[(k + 1) % 2], mtile[(k + 1) % 2], X[(k + 1) % 2], A[(k + 1) % DA]);
+    load_x(I[k % 2], X[k % 2]);      // X(bb+2)
+    load_a(bb + DA, A[k % DA]);
+    __syncthreads();
+  };
   int b = 0;
-  for (; b + 2 <= nb; b += 2) {
-    load_idx(b + 3, iB);
-    compute(xs0, S0);
-    store_x(xs1, S1);
-    load_x(iA, S0);                  // X(b+2)
-    load_a(b + 2, S0);
-    __syncthreads();
-    load_idx(b + 4, iA);
-    compute(xs1, S1);
-    store_x(xs0, S0);
-    load_x(iB, S1);                  // X(b+3)
-    load_a(b + 3, S1);
-    __syncthreads();
+  for (; b + 4 <= nb; b += 4) {
+    step(std::integral_constant<int, 0>{}, b);
+    step(std::integral_constant<int, 1>{}, b + 1);
+    step(std::integral_constant<int, 2>{}, b + 2);
+    step(std::integral_constant<int, 3>{}, b + 3);
   }
-  if (b < nb) compute(xs0, S0);
+  if (b < nb) step(std::integral_constant<int, 0>{}, b);
+  if (b + 1 < nb) step(std::integral_constant<int, 1>{}, b + 1);
+  if (b + 2 < nb) step(std::integral_constant<int, 2>{}, b + 2);
 }
 
 template <int NT, bool FAST>
-__device__ inline void prefill_body(const SpmmArgs& a, const PrefillRes& res, uint16_t* xs0, uint16_t* xs1, int t,
-                                    int rb, int n0, f32x16 (&acc)[2][PrefillCfg<NT>::NTB]) {
-  prefill_phase<NT, FAST, true>(a, res, xs0, xs1, t, rb, n0, acc);
-  prefill_phase<NT, FAST, false>(a, res, xs0, xs1, t, rb, n0, acc);
+__device__ inline void prefill_body(const SpmmArgs& a, const PrefillRes& res, uint16_t* xs0, uint16_t* xs1,
+                                    uint32_t* ms0, uint32_t* ms1, int t, int rb, int n0,
+                                    f32x16 (&acc)[2][PrefillCfg<NT>::NTB]) {
+  prefill_phase<NT, FAST, true>(a, res, xs0, xs1, ms0, ms1, t, rb, n0, acc);
+  prefill_phase<NT, FAST, false>(a, res, xs0, xs1, ms0, ms1, t, rb, n0, acc);
 }
 
+// Persistent launch: gridDim.x = 8 * per_xcd workgroups, workgroup L runs on
+// XCD L % 8 (round-robin dispatch).  The (token block, tile row block) items,
+// token-block major, are cut into 8 contiguous ranges, one per XCD; the XCD's
+// workgroups take its range in order, so each XCD works through its token
+// blocks one after another and keeps the current X slice in its L2.
 template <int NT>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
   using C = PrefillCfg<NT>;
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][64 * C::PITCH];
+  __shared__ __attribute__((aligned(16))) uint32_t ms[2][128];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nrb = a.rows / 64;
   const int n_tr = a.n_tiles * nrb;
-  const int L = blockIdx.x, nwg = gridDim.x;
-  const int logical = (nwg % 8 == 0) ? (L % 8) * (nwg / 8) + L / 8 : L;
-  const int tb = logical / n_tr, trb = logical % n_tr;
-  const int t = trb / nrb, rb = trb % nrb;
-  const int n0 = tb * NT;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8, per_xcd = gridDim.x / 8;
   const int tok_w = wave * C::TW;
 
   PrefillRes res;
@@ -717,33 +753,43 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
   res.is = __builtin_amdgcn_make_buffer_rsrc((void*)a.idx_s, (short)0, (int)((uint32_t)a.n_tiles * a.nkb_s * 64u * 4u), kBufferWord3);
   res.ldx_bytes = (uint32_t)a.ldx * 2u;
 
-  f32x16 acc[2][C::NTB];
-  for (int r = 0; r < 2; ++r)
-    for (int j = 0; j < C::NTB; ++j)
-      for (int e = 0; e < 16; ++e) acc[r][j][e] = 0.f;
+  const int items = n_tb * n_tr;
+  const int i_lo = (int)((int64_t)xcd * items / 8), i_hi = (int)((int64_t)(xcd + 1) * items / 8);
+  for (int it = i_lo + slot; it < i_hi; it += per_xcd) {
+    {
+      const int tb = it / n_tr, trb = it % n_tr;
+      const int n0 = tb * NT;
+      const int t = trb / nrb, rb = trb % nrb;
+      f32x16 acc[2][C::NTB];
+      for (int r = 0; r < 2; ++r)
+        for (int j = 0; j < C::NTB; ++j)
+          for (int e = 0; e < 16; ++e) acc[r][j][e] = 0.f;
 
-  if (a.x_vec && n0 + NT <= a.batch) prefill_body<NT, true>(a, res, xs[0], xs[1], t, rb, n0, acc);
-  else prefill_body<NT, false>(a, res, xs[0], xs[1], t, rb, n0, acc);
-  __syncthreads();
+      if (a.x_vec && n0 + NT <= a.batch) prefill_body<NT, true>(a, res, xs[0], xs[1], ms[0], ms[1], t, rb, n0, acc);
+      else prefill_body<NT, false>(a, res, xs[0], xs[1], ms[0], ms[1], t, rb, n0, acc);
+      __syncthreads();
 
-  // epilogue: acc[r][j][e] is row 32r + 8(e/4) + 4(lane/32) + e%4, token tok_w + 32j + lane%32.
-  uint16_t* ys = xs[0];
-  for (int r = 0; r < 2; ++r)
-    for (int j = 0; j < C::NTB; ++j)
-      for (int e = 0; e < 16; ++e)
-        ys[(32 * r + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * C::PITCH + tok_w + 32 * j + (lane & 31)] =
-            bf16_rne(acc[r][j][e]);
-  __syncthreads();
-  for (int q = threadIdx.x; q < 64 * C::CPR; q += 256) {
-    const int r = q / C::CPR, c = q % C::CPR;
-    const int n = n0 + 8 * c;
-    if (n >= a.batch) continue;
-    uint16_t* dst = a.y + ((int64_t)t * a.rows + rb * 64 + r) * a.ldy + n;
-    const uint16_t* src = ys + r * C::PITCH + 8 * c;
-    if (a.y_vec && n + 8 <= a.batch) {
-      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
-    } else {
-      for (int e = 0; e < 8 && n + e < a.batch; ++e) dst[e] = src[e];
+      // epilogue: acc[r][j][e] is row 32r + 8(e/4) + 4(lane/32) + e%4, token tok_w + 32j + lane%32.
+      uint16_t* ys = xs[0];
+      for (int r = 0; r < 2; ++r)
+        for (int j = 0; j < C::NTB; ++j)
+          for (int e = 0; e < 16; ++e)
+            ys[(32 * r + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * C::PITCH + tok_w + 32 * j + (lane & 31)] =
+                bf16_rne(acc[r][j][e]);
+      __syncthreads();
+      for (int q = threadIdx.x; q < 64 * C::CPR; q += 256) {
+        const int r = q / C::CPR, c = q % C::CPR;
+        const int n = n0 + 8 * c;
+        if (n >= a.batch) continue;
+        uint16_t* dst = a.y + ((int64_t)t * a.rows + rb * 64 + r) * a.ldy + n;
+        const uint16_t* src = ys + r * C::PITCH + 8 * c;
+        if (a.y_vec && n + 8 <= a.batch) {
+          *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+        } else {
+          for (int e = 0; e < 8 && n + e < a.batch; ++e) dst[e] = src[e];
+        }
+      }
+      __syncthreads();   // ys aliases the X tile of the next item
     }
   }
 }
@@ -874,7 +920,12 @@ extern "C" int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_
       else hipLaunchKernelGGL((decode3_kernel<64, 3, false>), grid, block, 0, stream, a);
     }
   } else if (sh.path == hinm::kPathPrefill) {
-    const int nwg = p.n_tiles * (p.tile_rows / 64) * sh.n_tblocks;
+    // persistent grid: 8 XCDs x (32 CUs x 2 workgroups), never more than the work items.
+    const int items = p.n_tiles * (p.tile_rows / 64) * sh.n_tblocks;
+    int per_xcd = 64;
+    const char* pe = getenv("HINM_PREFILL_PER_XCD");
+    if (pe && atoi(pe) > 0) per_xcd = atoi(pe);
+    const int nwg = 8 * std::min(per_xcd, (items + 7) / 8);
     if (sh.nt == 256) {
       hipLaunchKernelGGL(prefill_kernel<256>, dim3(nwg), dim3(256), 0, stream, a, sh.n_tblocks);
     } else {
