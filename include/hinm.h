@@ -163,8 +163,9 @@ int hinm_spmm_workspace_bytes(const hinm_plan_t* plan, int64_t batch, size_t* by
  * returns HINM_OK leaves it ready for the next one (its arrival counters are
  * back at zero when the work on `stream` completes).  Calls sharing one
  * workspace must be ordered (same stream, or synchronised).
- * batch == 0 is a no-op.  Asynchronous on `stream`; no host synchronisation,
- * no atomics: the same inputs give bitwise-identical Y.
+ * batch == 0 is a no-op.  Asynchronous on `stream`; no host synchronisation.
+ * Partial sums of a split reduction dimension are added in split order, so
+ * the same inputs give bitwise-identical Y on every call.
  * Errors (host-side checks only): HINM_EINVAL, HINM_ESHAPE, HINM_EALIGN,
  * HINM_EWORKSPACE, HINM_EHIP (launch failure). */
 int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_t batch, int64_t ldx,

@@ -332,30 +332,51 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode3_kernel(SpmmArgs a) {
   }
 }
 
+// Buffer resources (raw buffers, 32-bit offsets; an offset past the end
+// reads zero).
+constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9)
+constexpr uint32_t kOob = 0xFFFFFFF0u;     // offset past every buffer: loads return zeros
+
+struct BufRes {
+  __amdgpu_buffer_rsrc_t x, vd, vs, meta, id, is;
+  uint32_t ldx_bytes;
+};
+
+
 // ---------------------------------------------------------------------------
-// Decode kernel, split-K over workgroups (small batches, tile_rows % 64 == 0).
-// Workgroup = (64-row block of a tile, K split, token block), 4 waves of 16
-// rows.  All loads of a round - the packed values and metadata of up to MAXB
-// K-blocks into registers, the X rows those blocks gather into LDS (shared by
-// the 4 waves) - are issued before any is waited for: at decode sizes a
-// compute unit's whole share of the weight is only a few latency-bandwidth
-// products.  The splits' fp32 partial sums go to the workspace; the last
-// workgroup of a (row block, token block) to arrive adds them in split order
-// and writes Y (deterministic), then clears its arrival counter; the counters
-// (at the start of the workspace) must be zero before the first call.
+// Decode kernel with split K and specialised waves (batch <= 64, tile_rows %
+// 64 == 0).  Workgroup = 64 rows of one tile x NTOK tokens x one K range;
+// waves 0-3 own 16 rows each, waves 4-5 gather X.  The index -> X-row chain
+// is the latency-critical part, so the gather waves issue it first; once
+// their X loads are on their way (one barrier), the four row waves put every
+// packed-value load of their K range in flight at once.  The two roles sit
+// in different waves, so the X rows never wait behind the packed values in
+// a wave's in-order load queue.
+//
+// Every block, dense or 2:4, takes 64 LDS positions and one
+// v_smfmac_f32_16x16x64_bf16: a dense block's 32 columns sit at positions
+// 4q and 4q+1 of its groups (column 2q+e at position 4q+e) and use the fixed
+// index pattern 0x4 (positions 0 and 1 of every group), which is exactly the
+// dense product because the A operand of a dense block is its 32 values in
+// order.  The multiply loop is then the same straight-line code for every
+// block: blocks past the K range get zero values and zero X rows, and blocks
+// alternate between two accumulators so consecutive SMFMACs do not wait on
+// each other.
 // ---------------------------------------------------------------------------
 template <int NTOK, int MAXB, bool FAST>
-__global__ __launch_bounds__(256) void decode4_kernel(SpmmArgs a, int splits, int n_tb, float* __restrict__ part,
+__global__ __launch_bounds__(384) void decode5_kernel(SpmmArgs a, int splits, int n_tb, float* __restrict__ part,
                                                       unsigned* __restrict__ counters) {
-  constexpr int CPR = NTOK / 8;
-  constexpr int MAXP = MAXB * 64;              // gathered positions per round
-  constexpr int MAXCH = MAXP * CPR / 256;      // X chunks per thread per round
+  constexpr int CPR = NTOK / 8;                // 16-byte chunks per X row
+  constexpr int MAXP = MAXB * 64;              // LDS positions per round
+  constexpr int GT = 128;                      // gather threads
+  constexpr int MAXCH = MAXP * CPR / GT;       // X chunks per gather thread per round
   constexpr int NB = NTOK / 16;
   __shared__ __attribute__((aligned(16))) uint16_t xs[MAXP * NTOK];
   __shared__ int s_last;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool gather = wave >= 4;
   const int kc = lane >> 4, i16 = lane & 15;
   const int nrb = a.rows / 64;
   const int split = blockIdx.x % splits;
@@ -363,119 +384,139 @@ __global__ __launch_bounds__(256) void decode4_kernel(SpmmArgs a, int splits, in
   const int t = trb / nrb, rb = trb % nrb;
   const int tb = blockIdx.y;
   const int n0 = tb * NTOK;
-  const int row = rb * 64 + wave * 16 + (lane & 15);   // tile row of this lane's A fragment
+  const int row = rb * 64 + (wave & 3) * 16 + (lane & 15);   // tile row of this lane's A fragment
   const int nblk = a.nkb_d + a.nkb_s;
   const int b_lo = (int)((int64_t)split * nblk / splits), b_hi = (int)((int64_t)(split + 1) * nblk / splits);
 
-  f32x4 acc[NB];
-  for (int j = 0; j < NB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  BufRes res;
+  res.x = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, (int)(uint32_t)(((int64_t)(a.cin - 1) * a.ldx + a.batch) * 2), kBufferWord3);
+  res.vd = __builtin_amdgcn_make_buffer_rsrc((void*)a.val_d, (short)0, (int)((uint32_t)a.n_tiles * a.nkb_d * a.rows * 64u), kBufferWord3);
+  res.vs = __builtin_amdgcn_make_buffer_rsrc((void*)a.val_s, (short)0, (int)((uint32_t)a.n_tiles * a.nkb_s * a.rows * 64u), kBufferWord3);
+  res.meta = __builtin_amdgcn_make_buffer_rsrc((void*)a.meta, (short)0, (int)((uint32_t)a.n_tiles * a.nkb_s * a.rows * 8u), kBufferWord3);
+  res.id = __builtin_amdgcn_make_buffer_rsrc((void*)a.idx_d, (short)0, (int)((uint32_t)a.n_tiles * a.nkb_d * 32u * 4u), kBufferWord3);
+  res.is = __builtin_amdgcn_make_buffer_rsrc((void*)a.idx_s, (short)0, (int)((uint32_t)a.n_tiles * a.nkb_s * 64u * 4u), kBufferWord3);
+  res.ldx_bytes = (uint32_t)a.ldx * 2u;
+
+  f32x4 acc[2][NB];
+  for (int h = 0; h < 2; ++h)
+    for (int j = 0; j < NB; ++j) acc[h][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int r0 = b_lo; r0 < b_hi; r0 += MAXB) {
     const int r1 = min(r0 + MAXB, b_hi);
     const int nbr = r1 - r0;
-    // dense blocks come first in the block order, so the round's positions
-    // are a run of dense columns followed by a run of 2:4 positions.
+    // dense blocks come first in the block order
     const int nd_r = max(0, min(r1, a.nkb_d) - r0);
-    const int pd = 32 * nd_r;                      // dense positions in the round
-    const int ptot = pd + 64 * (nbr - nd_r);
-    const int32_t* idd = a.idx_d + (int64_t)t * a.nkb_d * 32 + (int64_t)r0 * 32;
-    const int32_t* ids = a.idx_s + (int64_t)t * a.nkb_s * 64 + (int64_t)max(0, r0 - a.nkb_d) * 64;
-
-    // Every load below is unconditional (indices clamped into the round) so
-    // the code stays straight-line: index slices first, then packed values and
-    // metadata, then the X rows; positions past the round gather junk into
-    // LDS space that is never read.
-    int cidx[MAXCH];
+    if (gather) {
+      // Gather thread gt takes 16-byte chunk gt % CPR of LDS positions
+      // gt / CPR + PPJ * j; position p is slot p % 64 of block p / 64, so the
+      // block of step j is a compile-time constant and the dense / 2:4
+      // choice is uniform.  Buffer loads: an out-of-range offset reads zero.
+      constexpr int PPJ = GT / CPR;
+      const int gt = threadIdx.x - 256;
+      const int pofs = gt / CPR;
+      const uint32_t xcol = (uint32_t)(n0 + 8 * (gt % CPR)) * 2u;
+      const uint32_t dbase = (uint32_t)(t * a.nkb_d + r0) * 32u;
+      const uint32_t sbase = (uint32_t)(t * a.nkb_s + max(0, r0 - a.nkb_d)) * 64u;
+      int cidx[MAXCH];
 #pragma unroll
-    for (int j = 0; j < MAXCH; ++j) {
-      const int pos = min((int)((threadIdx.x + 256 * j) / CPR), ptot - 1);
-      cidx[j] = *(pos < pd ? idd + pos : ids + (pos - pd));
-    }
-    u32x4 av[MAXB];
-    uint64_t mv[MAXB];
+      for (int j = 0; j < MAXCH; ++j) {
+        const int blk = (PPJ * j) >> 6;
+        const int slot = pofs + ((PPJ * j) & 63);
+        const bool dense = blk < nd_r;
+        const uint32_t li = dense ? dbase + 32u * blk + 2u * (slot >> 2) + (slot & 1)
+                                  : sbase + 64u * (blk - nd_r) + slot;
+        const __amdgpu_buffer_rsrc_t r = dense ? res.id : res.is;
+        cidx[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(r, blk < nbr ? li * 4u : kOob, 0, 0);
+      }
+      u32x4 xr[MAXCH];
 #pragma unroll
-    for (int j = 0; j < MAXB; ++j) {
-      const int b = r0 + min(j, nbr - 1);
-      const bool dense = b < a.nkb_d;
-      const int64_t blk = dense ? ((int64_t)t * a.nkb_d + b) * a.rows + row
-                                : ((int64_t)t * a.nkb_s + (b - a.nkb_d)) * a.rows + row;
-      const uint16_t* vp = (dense ? a.val_d : a.val_s) + blk * 32 + 8 * kc;
-      av[j] = *reinterpret_cast<const u32x4*>(vp);
-      mv[j] = *(dense ? reinterpret_cast<const uint64_t*>(vp) : a.meta + blk);
-    }
-    u32x4 xr[MAXCH];
-#pragma unroll
-    for (int j = 0; j < MAXCH; ++j) {
-      const int nb = n0 + 8 * ((threadIdx.x + 256 * j) % CPR);
-      xr[j] = FAST ? load_x_chunk_fast(a, cidx[j], nb) : load_x_chunk(a, cidx[j], nb);
-    }
-#pragma unroll
-    for (int j = 0; j < MAXCH; ++j) *reinterpret_cast<u32x4*>(xs + 8 * (threadIdx.x + 256 * j)) = xr[j];
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < MAXB; ++j) {
-      if (j < nbr) {
-        const int b = r0 + j;
-        const bf16x8 A = __builtin_bit_cast(bf16x8, av[j]);
-        if (b < a.nkb_d) {
-          const uint16_t* xb = xs + (32 * j) * NTOK;
-          for (int nb = 0; nb < NB; ++nb) {
-            const uint16_t* base = xb + 16 * nb + 4 * (i16 & 3);
-            const v4i16 b0 = tr_read(base + (8 * kc + 0 + (i16 >> 2)) * NTOK);
-            const v4i16 b1 = tr_read(base + (8 * kc + 4 + (i16 >> 2)) * NTOK);
-            const bf16x8 B = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
-            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[nb], 0, 0, 0);
-          }
+      for (int j = 0; j < MAXCH; ++j) {
+        const int blk = (PPJ * j) >> 6;
+        const int ci = blk < nbr ? cidx[j] : -1;       // rows past the K range read as zeros
+        if constexpr (FAST) {
+          const uint32_t off = ci < 0 ? kOob : __umul24((uint32_t)ci, res.ldx_bytes) + xcol;
+          xr[j] = __builtin_amdgcn_raw_buffer_load_b128(res.x, off, 0, 0);
         } else {
-          const uint16_t* xb = xs + (pd + 64 * (j - nd_r)) * NTOK;
-          const int sidx = (int)((mv[j] >> (16 * kc)) & 0xffffull);
-          for (int nb = 0; nb < NB; ++nb) {
-            const uint16_t* base = xb + 16 * nb + 4 * (i16 & 3);
-            const v4i16 b0 = tr_read(base + (8 * kc + 0 + (i16 >> 2)) * NTOK);
-            const v4i16 b1 = tr_read(base + (8 * kc + 4 + (i16 >> 2)) * NTOK);
-            const v4i16 b2 = tr_read(base + (32 + 8 * kc + 0 + (i16 >> 2)) * NTOK);
-            const v4i16 b3 = tr_read(base + (32 + 8 * kc + 4 + (i16 >> 2)) * NTOK);
-            const bf16x16 B = __builtin_bit_cast(
-                bf16x16, __builtin_shufflevector(__builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                 __builtin_shufflevector(b2, b3, 0, 1, 2, 3, 4, 5, 6, 7), 0, 1, 2,
-                                                 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15));
-            acc[nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(A, B, acc[nb], sidx, 0, 0);
-          }
+          xr[j] = load_x_chunk(a, ci, n0 + 8 * (gt % CPR));
         }
       }
+      __syncthreads();   // the X gathers are on their way: let the packed values go
+#pragma unroll
+      for (int j = 0; j < MAXCH; ++j) *reinterpret_cast<u32x4*>(xs + 8 * (gt + GT * j)) = xr[j];
+      __syncthreads();   // X rows are in LDS
+      __syncthreads();   // the row waves are done with them
+    } else {
+      // Each branch holds its own barriers (the condition is uniform per
+      // wave), so the two roles keep disjoint register sets.
+      u32x4 av[MAXB];
+      uint64_t mv[MAXB];
+      __syncthreads();   // wait until the X gathers are issued
+#pragma unroll
+      for (int j = 0; j < MAXB; ++j) {
+        const int b = r0 + min(j, nbr - 1);
+        const bool dense = b < a.nkb_d;
+        const uint32_t brow = dense ? (uint32_t)((t * a.nkb_d + b) * a.rows + row)
+                                    : (uint32_t)((t * a.nkb_s + (b - a.nkb_d)) * a.rows + row);
+        av[j] = __builtin_amdgcn_raw_buffer_load_b128(dense ? res.vd : res.vs, brow * 64u + 16u * kc, 0, 0);
+        mv[j] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(res.meta, dense ? kOob : brow * 8u, 0, 0));
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < MAXB; ++j) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const bf16x8 A = __builtin_bit_cast(bf16x8, j < nbr ? av[j] : z);
+        const int sidx = j < nd_r ? 0x4444 : (int)((mv[j] >> (16 * kc)) & 0xffffull);
+        const uint16_t* xb = xs + (64 * j) * NTOK;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const uint16_t* base = xb + 16 * nb + 4 * (i16 & 3);
+          const v4i16 b0 = tr_read(base + (8 * kc + 0 + (i16 >> 2)) * NTOK);
+          const v4i16 b1 = tr_read(base + (8 * kc + 4 + (i16 >> 2)) * NTOK);
+          const v4i16 b2 = tr_read(base + (32 + 8 * kc + 0 + (i16 >> 2)) * NTOK);
+          const v4i16 b3 = tr_read(base + (32 + 8 * kc + 4 + (i16 >> 2)) * NTOK);
+          const bf16x16 B = __builtin_bit_cast(
+              bf16x16, __builtin_shufflevector(__builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7),
+                                               __builtin_shufflevector(b2, b3, 0, 1, 2, 3, 4, 5, 6, 7), 0, 1, 2,
+                                               3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15));
+          acc[j & 1][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(A, B, acc[j & 1][nb], sidx, 0, 0);
+        }
+      }
+      __syncthreads();   // the next round overwrites xs
     }
-    __syncthreads();   // the next round overwrites xs
   }
+  for (int j = 0; j < NB; ++j) acc[0][j] += acc[1][j];
 
   // acc[nb][e]: tile row rb*64 + wave*16 + 4*kc + e, token 16*nb + i16.
-  const int64_t grow0 = (int64_t)t * a.rows + rb * 64 + wave * 16 + 4 * kc;
+  const int64_t grow0 = (int64_t)t * a.rows + rb * 64 + (wave & 3) * 16 + 4 * kc;
   if (splits == 1) {
-    for (int nb = 0; nb < NB; ++nb) {
-      const int n = n0 + 16 * nb + i16;
-      if (n < a.batch)
-        for (int e = 0; e < 4; ++e) a.y[(grow0 + e) * a.ldy + n] = bf16_rne(acc[nb][e]);
-    }
+    if (!gather)
+      for (int nb = 0; nb < NB; ++nb) {
+        const int n = n0 + 16 * nb + i16;
+        if (n < a.batch)
+          for (int e = 0; e < 4; ++e) a.y[(grow0 + e) * a.ldy + n] = bf16_rne(acc[0][nb][e]);
+      }
     return;
   }
-  // partial sums: part[split][tb][cout][NTOK].  Partials and the arrival
+  // Partial sums: part[split][tb][cout][NTOK].  Partials and the arrival
   // counter go through agent-scope (device-coherent) stores, loads and
   // atomics, and each workgroup waits for its stores to complete before it
-  // counts itself in; nothing needs a whole-cache writeback or invalidate.
+  // counts itself in, so nothing needs a whole-cache writeback or
+  // invalidate.  The last workgroup of a (tile row block, token block) to
+  // arrive adds the partials in split order and puts the counter back to 0.
   float* my = part + (((int64_t)split * n_tb + tb) * a.cout) * NTOK;
-  for (int nb = 0; nb < NB; ++nb)
-    for (int e = 0; e < 4; ++e)
-      __hip_atomic_store(my + (grow0 + e) * NTOK + 16 * nb + i16, acc[nb][e], __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+  if (!gather)
+    for (int nb = 0; nb < NB; ++nb)
+      for (int e = 0; e < 4; ++e)
+        __hip_atomic_store(my + (grow0 + e) * NTOK + 16 * nb + i16, acc[0][nb][e], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   unsigned* ctr = counters + (int64_t)trb * n_tb + tb;
   if (threadIdx.x == 0)
     s_last = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(splits - 1);
   __syncthreads();
-  if (!s_last) return;
+  if (!s_last || threadIdx.x >= 256) return;
   const int64_t grow_base = (int64_t)t * a.rows + rb * 64;
-  // Each thread owns OPT outputs; the splits are read 8 at a time with all
-  // loads of a batch in flight together, then added in split order.
   constexpr int OPT = 64 * NTOK / 256;
   const int64_t plane = (int64_t)n_tb * a.cout * NTOK;
   const float* p0 = part + ((int64_t)tb * a.cout + grow_base) * NTOK;
@@ -520,9 +561,6 @@ __global__ __launch_bounds__(256) void decode4_kernel(SpmmArgs a, int splits, in
 // sweeps one token block across all tiles.  Y leaves through LDS in 16-byte
 // row chunks.
 // ---------------------------------------------------------------------------
-constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9)
-constexpr uint32_t kOob = 0xFFFFFFF0u;     // offset past every buffer: loads return zeros
-
 template <int NT>
 struct PrefillCfg {
   static constexpr int PITCH = NT + 32;       // bf16 per LDS row: 64 bytes mod 256
@@ -540,10 +578,6 @@ struct PrefillA {
   uint32_t m;
 };
 
-struct PrefillRes {
-  __amdgpu_buffer_rsrc_t x, vd, vs, meta, id, is;
-  uint32_t ldx_bytes;
-};
 
 // One region's K-blocks [0, nb) (DENSE: 32-column blocks, else 2:4 blocks of
 // 64 positions), pipelined.  Keeping the two regions in separate loops keeps
@@ -553,8 +587,8 @@ struct PrefillRes {
 //   - X: thread (position group, chunk) gathers PPT rows x 16 bytes; the 64
 //     positions of a 2:4 block give PPT = 64 / PG, the 32 of a dense block
 //     PPT / 2.
-//   - indices: each wave fetches the WP indices of its own positions with one
-//     32-bit load per lane and hands them out with ds_bpermute.
+//   - indices: each wave loads the WP indices of its own positions, one per
+//     lane, and hands them to its lane groups with v_readlane and selects.
 //   - packed values: one 16-byte load per thread covers the 64 rows x 64
 //     bytes of a block; they are written into the 64-byte padding at the end
 //     of each X row of the LDS tile (row r's chunk c at chunk c ^ (r/4 % 4),
@@ -562,7 +596,7 @@ struct PrefillRes {
 //   - 2:4 metadata: 512 bytes per block, one dword per thread of waves 0-1,
 //     into a small LDS array.
 template <int NT, bool FAST, bool DENSE>
-__device__ inline void prefill_phase(const SpmmArgs& a, const PrefillRes& res, uint16_t* xs0, uint16_t* xs1,
+__device__ inline void prefill_phase(const SpmmArgs& a, const BufRes& res, uint16_t* xs0, uint16_t* xs1,
                                      uint32_t* ms0, uint32_t* ms1, int t, int rb, int n0,
                                      f32x16 (&acc)[2][PrefillCfg<NT>::NTB]) {
   using C = PrefillCfg<NT>;
@@ -580,29 +614,44 @@ __device__ inline void prefill_phase(const SpmmArgs& a, const PrefillRes& res, u
   const int kca = lane >> 5;                    // A-operand K chunk (0..1)
   const int cnk = threadIdx.x % C::CPR;
   const int pbase = (threadIdx.x / C::CPR) * PPT;          // first of this thread's PPT positions
-  const int psrc = (lane / C::CPR) * PPT;                  // same, relative to the wave's WP positions
+  constexpr int G = 64 / C::CPR;              // position groups per wave
+  const int grp = lane / C::CPR;
   const uint32_t xcol = (uint32_t)(n0 + 8 * cnk) * 2u;
-  const uint32_t ipos = (uint32_t)(wave * WP + (lane % WP));
   const __amdgpu_buffer_rsrc_t rid = DENSE ? res.id : res.is;
   const __amdgpu_buffer_rsrc_t rv = DENSE ? res.vd : res.vs;
   const uint32_t vrow = (uint32_t)rb * 64u;
   const int arow = threadIdx.x >> 2;                       // value row this thread stores
   const int acol = C::PITCH * arow + NT + 8 * ((threadIdx.x & 3) ^ ((arow >> 2) & 3));
 
+  // Indices: each lane of a wave loads one of the wave's WP indices; lane
+  // group q then takes positions q*PPT .. q*PPT+PPT-1 of them through
+  // v_readlane (uniform values) and per-group selects.
+  const uint32_t ipos = (uint32_t)(wave * WP + (lane % WP));
   auto load_idx = [&](int b) -> int {
     b = min(b, nb - 1);
     const uint32_t off = ((uint32_t)(t * nb + b) * KPOS + ipos) * 4u;
     return (int)__builtin_amdgcn_raw_buffer_load_b32(rid, off, 0, 0);
   };
-  auto load_x = [&](int iw, u32x4 (&st)[PPT]) {
+  auto spread_idx = [&](int iw, int (&ci)[PPT]) {
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
-      const int ci = __builtin_amdgcn_ds_bpermute(4 * (psrc + j), iw);
+      int c = __builtin_amdgcn_readlane(iw, j);
+#pragma unroll
+      for (int q = 1; q < G; ++q) {
+        const int m = -(int)(grp == q);
+        c = (c & ~m) | (__builtin_amdgcn_readlane(iw, q * PPT + j) & m);
+      }
+      ci[j] = c;
+    }
+  };
+  auto load_x = [&](const int (&ci)[PPT], u32x4 (&st)[PPT]) {
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
       if constexpr (FAST) {
-        const uint32_t off = ci < 0 ? kOob : __umul24((uint32_t)ci, res.ldx_bytes) + xcol;
+        const uint32_t off = ci[j] < 0 ? kOob : __umul24((uint32_t)ci[j], res.ldx_bytes) + xcol;
         st[j] = __builtin_amdgcn_raw_buffer_load_b128(res.x, off, 0, 0);
       } else {
-        st[j] = load_x_chunk(a, ci, n0 + 8 * cnk);
+        st[j] = load_x_chunk(a, ci[j], n0 + 8 * cnk);
       }
     }
   };
@@ -676,34 +725,39 @@ __device__ inline void prefill_phase(const SpmmArgs& a, const PrefillRes& res, u
 
   __syncthreads();                   // the LDS tiles may still be read by the previous phase
   // Register sets: packed values of DA blocks (A[b % DA]), X rows of 2 blocks
-  // (X[b % 2]), index words of 2 blocks (I[b % 2]).  At block bb: compute bb
-  // from LDS tile bb % 2; write X(bb+1) and the values of bb+1 to the other
-  // tile; issue X(bb+2), values(bb+DA) and indices(bb+3).  The packed values
-  // run further ahead because they come from HBM or the last-level cache,
-  // while the X slice stays in L2.
+  // (X[b % 2]) and the indices of one block.  At block bb: issue the X
+  // gathers of bb+2 (their indices arrived during bb-1), then the indices of
+  // bb+3 and the values of bb+DA; compute bb from LDS tile bb % 2; write X and
+  // values of bb+1 into the other tile.  An X gather has about two block
+  // times to arrive, a value load DA block times.
   constexpr int DA = C::DA;
   PrefillA A[DA];
   u32x4 X[2][PPT];
-  int I[2];
+  int Iw[2];                          // index words of blocks bb+3 and bb+4
+  int CI[PPT];                        // this thread's indices of block bb+2
   uint16_t* const tile[2] = {xs0, xs1};
   uint32_t* const mtile[2] = {ms0, ms1};
-  I[0] = load_idx(0);
-  I[1] = load_idx(1);
-  load_x(I[0], X[0]);
-  load_a(0, A[0]);
-  load_x(I[1], X[1]);
+  Iw[0] = load_idx(0);
+  Iw[1] = load_idx(1);
+  spread_idx(Iw[0], CI);
+  load_x(CI, X[0]);
+  spread_idx(Iw[1], CI);
+  load_x(CI, X[1]);
+  Iw[0] = load_idx(2);
+  Iw[1] = load_idx(3);
 #pragma unroll
-  for (int d = 1; d < DA; ++d) load_a(d, A[d]);
-  I[0] = load_idx(2);
+  for (int d = 0; d < DA; ++d) load_a(d, A[d]);
+  spread_idx(Iw[0], CI);
   store(tile[0], mtile[0], X[0], A[0]);
   __syncthreads();
   auto step = [&](auto kc, int bb) {
     constexpr int k = decltype(kc)::value;
-    I[(k + 1) % 2] = load_idx(bb + 3);
+    load_x(CI, X[k % 2]);             // X(bb+2)
+    Iw[k % 2] = load_idx(bb + 4);
+    load_a(bb + DA, A[k % DA]);
     compute(tile[k % 2], mtile[k % 2]);
     store(tile[(k + 1) % 2], mtile[(k + 1) % 2], X[(k + 1) % 2], A[(k + 1) % DA]);
-    load_x(I[k % 2], X[k % 2]);      // X(bb+2)
-    load_a(bb + DA, A[k % DA]);
+    spread_idx(Iw[(k + 1) % 2], CI);  // indices of bb+3
     __syncthreads();
   };
   int b = 0;
@@ -719,7 +773,7 @@ __device__ inline void prefill_phase(const SpmmArgs& a, const PrefillRes& res, u
 }
 
 template <int NT, bool FAST>
-__device__ inline void prefill_body(const SpmmArgs& a, const PrefillRes& res, uint16_t* xs0, uint16_t* xs1,
+__device__ inline void prefill_body(const SpmmArgs& a, const BufRes& res, uint16_t* xs0, uint16_t* xs1,
                                     uint32_t* ms0, uint32_t* ms1, int t, int rb, int n0,
                                     f32x16 (&acc)[2][PrefillCfg<NT>::NTB]) {
   prefill_phase<NT, FAST, true>(a, res, xs0, xs1, ms0, ms1, t, rb, n0, acc);
@@ -743,7 +797,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8, per_xcd = gridDim.x / 8;
   const int tok_w = wave * C::TW;
 
-  PrefillRes res;
+  BufRes res;
   const uint32_t xbytes = (uint32_t)(((int64_t)(a.cin - 1) * a.ldx + a.batch) * 2);
   res.x = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, (int)xbytes, kBufferWord3);
   res.vd = __builtin_amdgcn_make_buffer_rsrc((void*)a.val_d, (short)0, (int)((uint32_t)a.n_tiles * a.nkb_d * a.rows * 64u), kBufferWord3);
@@ -878,14 +932,23 @@ extern "C" int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_
   a.n_tiles = p.n_tiles;
 
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  // The prefill and split decode kernels address X and the packed buffers
+  // with 32-bit buffer offsets and gather with a 24-bit multiply; beyond
+  // those ranges kernels with 64-bit addressing take over (the generic
+  // kernel without a K split, or the 16-row decode kernel; neither needs a
+  // workspace).
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t xbytes = ((int64_t)(p.cin - 1) * ldx + batch) * 2;
+  const bool fits32 = xbytes < lim && ldx * 2 < ((int64_t)1 << 24) && p.bytes_val_dense < lim &&
+                      p.bytes_val_24 < lim && p.bytes_idx_dense < lim && p.bytes_idx_24 < lim &&
+                      p.bytes_meta_24 < lim;
+  if (sh.path == hinm::kPathDecodeSplit && !fits32) {
+    sh.path = hinm::kPathDecode;
+    sh.splits = 1;
+    a.splits = 1;
+  }
   if (sh.path == hinm::kPathPrefill) {
-    // The prefill kernel addresses X and the packed buffers with 32-bit
-    // offsets and gathers with a 24-bit multiply; beyond those ranges the
-    // generic kernel (without a K split, so no workspace) takes over.
-    const int64_t lim = (int64_t)1 << 31;
-    const int64_t xbytes = ((int64_t)(p.cin - 1) * ldx + batch) * 2;
-    if (xbytes >= lim || ldx * 2 >= ((int64_t)1 << 24) || p.bytes_val_dense >= lim || p.bytes_val_24 >= lim ||
-        p.bytes_idx_dense >= lim || p.bytes_idx_24 >= lim || p.bytes_meta_24 >= lim) {
+    if (!fits32) {
       sh.path = hinm::kPathGeneric;
       sh.nt = 64;
       sh.n_tblocks = (int)((batch + 63) / 64);
@@ -897,14 +960,14 @@ extern "C" int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_
     const bool fast = a.x_vec && (batch % sh.nt == 0);
     unsigned* counters = static_cast<unsigned*>(workspace);
     float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + sh.ws_counter_bytes);
-    const dim3 grid(p.n_tiles * (p.tile_rows / 64) * sh.splits, sh.n_tblocks), block(256);
+    const dim3 grid(p.n_tiles * (p.tile_rows / 64) * sh.splits, sh.n_tblocks), block(384);
     switch (sh.nt * 2 + (fast ? 1 : 0)) {
-      case 33: hipLaunchKernelGGL((decode4_kernel<16, 24, true>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
-      case 32: hipLaunchKernelGGL((decode4_kernel<16, 24, false>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
-      case 65: hipLaunchKernelGGL((decode4_kernel<32, 12, true>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
-      case 64: hipLaunchKernelGGL((decode4_kernel<32, 12, false>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
-      case 129: hipLaunchKernelGGL((decode4_kernel<64, 6, true>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
-      default: hipLaunchKernelGGL((decode4_kernel<64, 6, false>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
+      case 33: hipLaunchKernelGGL((decode5_kernel<16, 24, true>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
+      case 32: hipLaunchKernelGGL((decode5_kernel<16, 24, false>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
+      case 65: hipLaunchKernelGGL((decode5_kernel<32, 12, true>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
+      case 64: hipLaunchKernelGGL((decode5_kernel<32, 12, false>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
+      case 129: hipLaunchKernelGGL((decode5_kernel<64, 6, true>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
+      default: hipLaunchKernelGGL((decode5_kernel<64, 6, false>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
     }
   } else if (sh.path == hinm::kPathDecode) {
     const dim3 grid(p.n_tiles * (p.tile_rows / 16), sh.n_tblocks), block(kDecWaves * 64);
