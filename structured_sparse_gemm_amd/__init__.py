@@ -139,10 +139,16 @@ class HinmPacked:
     idx_24: torch.Tensor      # int32 [T, n_24_pad]
 
     def struct(self) -> PackedT:
-        def ptr(t):
-            return t.data_ptr() if t.numel() else None
-        return PackedT(self.plan.raw, ptr(self.val_dense), ptr(self.idx_dense), ptr(self.val_24),
-                       ptr(self.meta_24), ptr(self.idx_24))
+        """The C view of this weight (built once; the tensors must not be replaced afterwards)."""
+        st = self.__dict__.get("_struct")
+        if st is None:
+            def ptr(t):
+                return t.data_ptr() if t.numel() else None
+            st = PackedT(self.plan.raw, ptr(self.val_dense), ptr(self.idx_dense), ptr(self.val_24),
+                         ptr(self.meta_24), ptr(self.idx_24))
+            self.__dict__["_struct"] = st
+            self.__dict__["_ws_need"] = {}
+        return st
 
     @property
     def device(self) -> torch.device:
@@ -152,7 +158,12 @@ class HinmPacked:
         return self.plan.packed_bytes
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream_ptr(device: torch.device) -> int:
+    if _raw_stream is not None:
+        return _raw_stream(device.index if device.index is not None else torch.cuda.current_device())
     return torch.cuda.current_stream(device).cuda_stream
 
 
@@ -234,27 +245,38 @@ def spmm(packed: HinmPacked, x: torch.Tensor, out: Optional[torch.Tensor] = None
 
     Asynchronous on the current stream.  ``workspace`` (uint8, device) may be
     given; otherwise a per-device buffer is reused (calls on one device that
-    use it must not overlap on different streams).
+    use it must not overlap on different streams).  The per-call host work is
+    kept to argument checks and one C call, so that small products are not
+    bound by Python.
     """
     p = packed.plan
-    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[0] != p.cin or x.device != packed.device:
+    dev = x.device
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[0] != p.cin or dev != packed.idx_24.device:
         raise ValueError(f"x must be bf16 [{p.cin}, batch] on {packed.device}")
     if x.stride(1) != 1:
         raise ValueError("x must have unit column stride")
     batch = x.shape[1]
     if out is None:
-        out = torch.empty((p.cout, batch), dtype=torch.bfloat16, device=x.device)
-    elif out.dtype != torch.bfloat16 or out.shape != (p.cout, batch) or out.stride(1) != 1 or out.device != x.device:
-        raise ValueError(f"out must be bf16 [{p.cout}, {batch}] with unit column stride on {x.device}")
-    need = spmm_workspace_bytes(p, batch)
-    if workspace is None:
-        workspace = _workspace(x.device, need)
+        out = torch.empty((p.cout, batch), dtype=torch.bfloat16, device=dev)
+    elif out.dtype != torch.bfloat16 or out.shape != (p.cout, batch) or out.stride(1) != 1 or out.device != dev:
+        raise ValueError(f"out must be bf16 [{p.cout}, {batch}] with unit column stride on {dev}")
     st = packed.struct()
-    with torch.cuda.device(x.device):
-        _check(library().hinm_spmm(ctypes.byref(st), x.data_ptr(), batch, max(x.stride(0), batch) if batch else 0,
-                                   out.data_ptr(), max(out.stride(0), batch) if batch else 0,
-                                   workspace.data_ptr() if workspace is not None else None,
-                                   workspace.numel() if workspace is not None else 0, _stream_ptr(x.device)))
+    need_cache = packed.__dict__["_ws_need"]
+    need = need_cache.get(batch)
+    if need is None:
+        need = need_cache[batch] = spmm_workspace_bytes(p, batch)
+    if workspace is None:
+        workspace = _workspace(dev, need)
+    lib = library()
+    args = (ctypes.byref(st), x.data_ptr(), batch, max(x.stride(0), batch) if batch else 0,
+            out.data_ptr(), max(out.stride(0), batch) if batch else 0,
+            workspace.data_ptr() if workspace is not None else None,
+            workspace.numel() if workspace is not None else 0, _stream_ptr(dev))
+    if dev.index is None or dev.index == torch.cuda.current_device():
+        _check(lib.hinm_spmm(*args))
+    else:
+        with torch.cuda.device(dev):
+            _check(lib.hinm_spmm(*args))
     return out
 
 

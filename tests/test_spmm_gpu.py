@@ -185,3 +185,39 @@ def test_spmm_shared_workspace_across_shapes():
                 torch.cuda.synchronize()
                 xf = synth.as_f64(x)
                 check_y(y, c.w_hat @ xf, np.abs(c.w_hat) @ np.abs(xf), f"shared ws rep {rep} batch {b}")
+
+
+def test_spmm_graph_replay():
+    """Products captured in a HIP graph (as the benchmark times the batch-16 point) give the eager
+    results on every replay, with eager work and synchronisation between replays."""
+    cases = [(Case(synth.small(256, 4096, 64, 0.75, 0.55, 1, seed=41)), 16),    # split-K decode, workspace
+             (Case(synth.small(256, 4096, 64, 0.75, 0.55, 1, seed=41)), 300),   # prefill
+             (Case(synth.small(96, 1024, 48, 0.5, 0.25, 1, seed=42)), 40)]      # generic split + reduce
+    g_in = torch.Generator().manual_seed(7)
+    xs = [torch.randn(c.w.cin, b, generator=g_in).to(torch.bfloat16).to(DEV) for c, b in cases]
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
+    eager = [hinm.spmm(c.pk, x, workspace=ws) for (c, _), x in zip(cases, xs)]
+    torch.cuda.synchronize()
+    outs = [torch.empty_like(e) for e in eager]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for (c, _), x, o in zip(cases, xs, outs):
+            hinm.spmm(c.pk, x, out=o, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for (c, _), x, o in zip(cases, xs, outs):
+            hinm.spmm(c.pk, x, out=o, workspace=ws)
+    for rep in range(4):
+        for o in outs:
+            o.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (o, e) in enumerate(zip(outs, eager)):
+            assert torch.equal(o.view(torch.int16), e.view(torch.int16)), f"replay {rep} product {i}"
+        # eager work on the same workspace between replays
+        (c, _), x = cases[0], xs[0]
+        assert torch.equal(hinm.spmm(c.pk, x, workspace=ws).view(torch.int16), eager[0].view(torch.int16))
+        torch.cuda.synchronize()
