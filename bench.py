@@ -133,7 +133,7 @@ def time_spmm(hinm, torch, rot, steps, warmup):
             "ms_p10": per[len(per) // 10], "ms_p90": per[(9 * len(per)) // 10], "wall_s": wall}
 
 
-def time_spmm_graph(hinm, torch, rot, steps, extra=4):
+def time_spmm_graph(hinm, torch, rot, steps, extra=4, out_rows=None):
     """Time of exactly `steps` products launched from one HIP graph.
 
     Product i uses rotation copy i % k.  The graph is captured on a side
@@ -146,7 +146,7 @@ def time_spmm_graph(hinm, torch, rot, steps, extra=4):
     def run():
         for i in range(steps):
             pk, x, y = rot[i]
-            hinm.spmm(pk, x, out=y, workspace=rot.ws)
+            hinm.spmm(pk, x, out=y, workspace=rot.ws, out_rows=out_rows)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -283,6 +283,25 @@ def main():
     algd = algorithmic(p, Bd)
     gbs_d = algd["bytes"] / (rd["ms_mean"] * 1e-3) / 1e9
 
+    # NEXT row: output-channel permutation fused into the write-out, and the
+    # one-time cross-layer index translation
+    out_rows = torch.from_numpy(__import__("numpy").random.default_rng(0).permutation(p.cout).astype("int32")).to(dev)
+    r_rows = time_spmm_graph(hinm, torch, rot, args.steps, extra=0, out_rows=out_rows)
+    rd_rows = time_spmm_graph(hinm, torch, rotd, steps_d, extra=0, out_rows=out_rows)
+    sigma = torch.from_numpy(__import__("numpy").random.default_rng(1).permutation(p.cin).astype("int32")).to(dev)
+    pk_t = hinm.HinmPacked(pk.plan, pk.val_dense, pk.idx_dense.clone(), pk.val_24, pk.meta_24, pk.idx_24.clone())
+    tr_ms = []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        hinm.translate_indices(pk_t, sigma)
+        tr_ms.append((time.perf_counter() - t0) * 1e3)
+    next_rows = {"what": "hinm_spmm_rows (Y row r written to out_rows[r]) next to hinm_spmm, same timing method; "
+                         "hinm_translate_indices wall time (synchronous, includes the permutation check)",
+                 "spmm_rows_batch_2048_ms": round(r_rows["ms_mean"], 5), "spmm_batch_2048_ms": round(ms, 5),
+                 "spmm_rows_batch_16_ms": round(rd_rows["ms_mean"], 5), "spmm_batch_16_ms": round(rd["ms_mean"], 5),
+                 "translate_indices_ms": [round(v, 3) for v in tr_ms]}
+
     dense = None
     if not args.no_dense:
         dense_ms = time_dense(torch, wgpu, x, max(10, args.steps // 2), 3)
@@ -328,6 +347,7 @@ def main():
                    "rotation_copies": rotd.k},
         "batch_2048_hbm_gbs": round(alg["bytes"] / (ms * 1e-3) / 1e9, 1),
         "pack_ms": [round(v, 2) for v in pack_ms],
+        "next_output_permutation": next_rows,
         "dense_comparator": dense,
         "cpu_baseline": cpu,
     }

@@ -171,6 +171,37 @@ int hinm_spmm_workspace_bytes(const hinm_plan_t* plan, int64_t batch, size_t* by
 int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_t batch, int64_t ldx,
               void* y_bf16, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
 
+/* hinm_spmm with the output-channel permutation fused into the write-out
+ * (FlexHiNM-GP notes, key design 2: the output channels of a tile are
+ * permuted before pruning, and the permutation is undone where the data
+ * moves anyway; highlights: permutation at no run-time cost).  Row r of the
+ * product (W's row order, which is the order the weight was packed in) is
+ * written to Y row out_rows[r]:  Y[out_rows[r]][n] = ((W (.) M) X)[r][n].
+ * out_rows (device) int32 [cout], 4-byte aligned, a permutation of
+ * 0..cout-1; an entry outside [0, cout) leaves nothing written for that row
+ * (the device does not check that out_rows is a permutation; rows that two
+ * entries name receive one of the two results).  All other arguments,
+ * errors and guarantees as hinm_spmm; out_rows == NULL is HINM_EINVAL. */
+int hinm_spmm_rows(const hinm_packed_t* packed, const void* x_bf16, int64_t batch, int64_t ldx, void* y_bf16,
+                   int64_t ldy, const int32_t* out_rows, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Cross-layer index translation (FlexHiNM-GP notes, key design 2: the
+ * translation between one layer's output order and the next layer's input
+ * order is folded into the HiNM index lists; key design 4: the kernel
+ * gathers X rows through those indices).  Every non-negative entry i of
+ * packed->idx_dense and packed->idx_24 becomes map[i]; pads (-1) stay.  Use
+ * map[c] = the position at which the activations hold input channel c, so
+ * that a product over activations stored in that order equals the product
+ * over activations in channel order, bit for bit.
+ * map (device) int32 [cin], 4-byte aligned, must be a permutation of
+ * 0..cin-1; it is checked on the device first and nothing is written if it
+ * is not (HINM_EPERM).  workspace (device, 256-byte aligned, >= 256 bytes).
+ * Synchronous (returns after the work on `stream` has finished).  Errors:
+ * HINM_EINVAL, HINM_EPERM, HINM_EALIGN, HINM_EWORKSPACE, HINM_EHIP,
+ * HINM_EDEVICE. */
+int hinm_translate_indices(hinm_packed_t* packed, const int32_t* map, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* Static description of a status code. */
 const char* hinm_status_str(int status);
 

@@ -311,6 +311,44 @@ def spmm(w_hat: np.ndarray, x: np.ndarray) -> np.ndarray:
     return np.asarray(w_hat, dtype=np.float64) @ np.asarray(x, dtype=np.float64)
 
 
+def scatter_rows(y: np.ndarray, out_rows: np.ndarray) -> np.ndarray:
+    """Output-channel permutation undone at write-out: result[out_rows[r]] = y[r].
+
+    FlexHiNM-GP notes, key design 2: output channels are permuted before
+    pruning, and the permutation costs nothing at run time because it is
+    applied where the data moves anyway (highlights).  ``out_rows`` must be a
+    permutation of 0..cout-1.
+    """
+    y = np.asarray(y)
+    out_rows = np.asarray(out_rows, dtype=np.int64)
+    if out_rows.shape != (y.shape[0],) or not np.array_equal(np.sort(out_rows), np.arange(y.shape[0])):
+        raise ValueError("out_rows must be a permutation of 0..cout-1")
+    res = np.empty_like(y)
+    res[out_rows] = y
+    return res
+
+
+def translate_indices(idx: np.ndarray, mapping: np.ndarray) -> np.ndarray:
+    """Cross-layer index translation: every index i >= 0 becomes mapping[i]; pads (-1) stay.
+
+    FlexHiNM-GP notes, key design 2: the translation between one layer's
+    output order and the next layer's input order is folded into the HiNM
+    indices; key design 4: the kernel gathers X rows through those indices.
+    With mapping[c] = the row at which channel c is stored, gathering through
+    the translated indices reads the same values as gathering channel rows
+    through the original ones.
+    """
+    idx = np.asarray(idx)
+    mapping = np.asarray(mapping, dtype=np.int64)
+    n = mapping.shape[0]
+    if not np.array_equal(np.sort(mapping), np.arange(n)):
+        raise ValueError("mapping must be a permutation")
+    out = idx.copy()
+    keep = idx >= 0
+    out[keep] = mapping[idx[keep]]
+    return out
+
+
 def retained_importance(d: np.ndarray, perm: np.ndarray, p: Plan,
                         s: Optional[np.ndarray] = None) -> float:
     """R_total = R_dense + R_24 for the allocation that ``p`` defines.

@@ -26,7 +26,8 @@ STATUS = {0: "HINM_OK", 1: "HINM_EINVAL", 2: "HINM_ESHAPE", 3: "HINM_EPERM", 4: 
 
 # Every symbol the C ABI exports (include/hinm.h).
 EXPORTS = ("hinm_abi_version", "hinm_plan", "hinm_pack_workspace_bytes", "hinm_pack",
-           "hinm_spmm_workspace_bytes", "hinm_spmm", "hinm_status_str", "hinm_last_error")
+           "hinm_spmm_workspace_bytes", "hinm_spmm", "hinm_spmm_rows", "hinm_translate_indices",
+           "hinm_status_str", "hinm_last_error")
 
 
 class HinmError(RuntimeError):
@@ -73,6 +74,8 @@ def library() -> ctypes.CDLL:
             "hinm_pack": ([P, VP, I64, VP, I64, VP, ctypes.POINTER(PackedT), VP, S, VP], ctypes.c_int),
             "hinm_spmm_workspace_bytes": ([P, I64, ctypes.POINTER(S)], ctypes.c_int),
             "hinm_spmm": ([ctypes.POINTER(PackedT), VP, I64, I64, VP, I64, VP, S, VP], ctypes.c_int),
+            "hinm_spmm_rows": ([ctypes.POINTER(PackedT), VP, I64, I64, VP, I64, VP, VP, S, VP], ctypes.c_int),
+            "hinm_translate_indices": ([ctypes.POINTER(PackedT), VP, VP, S, VP], ctypes.c_int),
             "hinm_status_str": ([ctypes.c_int], ctypes.c_char_p),
             "hinm_last_error": ([], ctypes.c_char_p),
         }
@@ -240,9 +243,11 @@ def _workspace(device: torch.device, nbytes: int) -> Optional[torch.Tensor]:
 
 
 def spmm(packed: HinmPacked, x: torch.Tensor, out: Optional[torch.Tensor] = None,
-         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+         workspace: Optional[torch.Tensor] = None, out_rows: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Y = (W (.) M) X: x bf16 [cin, batch] (row stride >= batch), returns bf16 [cout, batch].
 
+    With ``out_rows`` (int32 [cout] on the device, a permutation), row r of the
+    product is written to row out_rows[r] of Y (hinm_spmm_rows).
     Asynchronous on the current stream.  ``workspace`` (uint8, device) may be
     given; otherwise a per-device buffer is reused (calls on one device that
     use it must not overlap on different streams).  The per-call host work is
@@ -260,6 +265,9 @@ def spmm(packed: HinmPacked, x: torch.Tensor, out: Optional[torch.Tensor] = None
         out = torch.empty((p.cout, batch), dtype=torch.bfloat16, device=dev)
     elif out.dtype != torch.bfloat16 or out.shape != (p.cout, batch) or out.stride(1) != 1 or out.device != dev:
         raise ValueError(f"out must be bf16 [{p.cout}, {batch}] with unit column stride on {dev}")
+    if out_rows is not None and (out_rows.dtype != torch.int32 or out_rows.shape != (p.cout,)
+                                 or not out_rows.is_contiguous() or out_rows.device != dev):
+        raise ValueError(f"out_rows must be a contiguous int32 [{p.cout}] tensor on {dev}")
     st = packed.struct()
     need_cache = packed.__dict__["_ws_need"]
     need = need_cache.get(batch)
@@ -268,17 +276,38 @@ def spmm(packed: HinmPacked, x: torch.Tensor, out: Optional[torch.Tensor] = None
     if workspace is None:
         workspace = _workspace(dev, need)
     lib = library()
-    args = (ctypes.byref(st), x.data_ptr(), batch, max(x.stride(0), batch) if batch else 0,
-            out.data_ptr(), max(out.stride(0), batch) if batch else 0,
-            workspace.data_ptr() if workspace is not None else None,
-            workspace.numel() if workspace is not None else 0, _stream_ptr(dev))
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_n = workspace.numel() if workspace is not None else 0
+    ldx = max(x.stride(0), batch) if batch else 0
+    ldy = max(out.stride(0), batch) if batch else 0
+    if out_rows is None:
+        call, args = lib.hinm_spmm, (ctypes.byref(st), x.data_ptr(), batch, ldx, out.data_ptr(), ldy, ws_ptr, ws_n,
+                                     _stream_ptr(dev))
+    else:
+        call, args = lib.hinm_spmm_rows, (ctypes.byref(st), x.data_ptr(), batch, ldx, out.data_ptr(), ldy,
+                                          out_rows.data_ptr(), ws_ptr, ws_n, _stream_ptr(dev))
     if dev.index is None or dev.index == torch.cuda.current_device():
-        _check(lib.hinm_spmm(*args))
+        _check(call(*args))
     else:
         with torch.cuda.device(dev):
-            _check(lib.hinm_spmm(*args))
+            _check(call(*args))
     return out
 
 
-__all__ = ["HinmError", "HinmPacked", "Plan", "plan", "pack", "spmm", "alloc_packed", "pack_workspace_bytes",
+def translate_indices(packed: HinmPacked, mapping: torch.Tensor) -> HinmPacked:
+    """Rewrites the packed index lists in place through ``mapping`` (int32 [cin] permutation on the device):
+    index i becomes mapping[i], pads stay -1 (hinm_translate_indices).  Synchronous; returns ``packed``."""
+    p = packed.plan
+    dev = packed.idx_24.device
+    if mapping.dtype != torch.int32 or mapping.shape != (p.cin,) or not mapping.is_contiguous() or mapping.device != dev:
+        raise ValueError(f"mapping must be a contiguous int32 [{p.cin}] tensor on {dev}")
+    ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(library().hinm_translate_indices(ctypes.byref(packed.struct()), mapping.data_ptr(), ws.data_ptr(),
+                                                ws.numel(), _stream_ptr(dev)))
+    return packed
+
+
+__all__ = ["HinmError", "HinmPacked", "Plan", "plan", "pack", "spmm", "translate_indices", "alloc_packed",
+           "pack_workspace_bytes",
            "spmm_workspace_bytes", "library", "LIB_PATH", "EXPORTS"]

@@ -204,6 +204,16 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(HINM_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Cross-layer index translation: every index i >= 0 of the packed lists
+// becomes map[i]; pads (-1) stay.  map has been checked to be a permutation.
+__global__ __launch_bounds__(256) void translate_kernel(int32_t* __restrict__ idx, int64_t n,
+                                                        const int32_t* __restrict__ map) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int32_t v = idx[i];
+  if (v >= 0) idx[i] = map[v];
+}
+
 }  // namespace
 
 extern "C" int hinm_pack(const hinm_plan_t* plan, const void* w_bf16, int64_t ldw, const float* importance,
@@ -279,5 +289,47 @@ extern "C" int hinm_pack(const hinm_plan_t* plan, const void* w_bf16, int64_t ld
   if (e != hipSuccess) return hip_fail(e, "pack stage-2 launch");
   e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_fail(e, "pack stage-2");
+  return HINM_OK;
+}
+
+extern "C" int hinm_translate_indices(hinm_packed_t* packed, const int32_t* map, void* workspace,
+                                      size_t workspace_bytes, void* stream_) {
+  hinm::clear_error();
+  if (!packed || !map) return fail(HINM_EINVAL, "packed and map must be non-NULL");
+  int st = hinm::check_plan(&packed->plan);
+  if (st) return st;
+  const hinm_plan_t& p = packed->plan;
+  if (!hinm::aligned(map, 4)) return fail(HINM_EALIGN, "map is not 4-byte aligned");
+  if ((p.bytes_idx_dense > 0 && !packed->idx_dense) || (p.bytes_idx_24 > 0 && !packed->idx_24))
+    return fail(HINM_EINVAL, "index lists are NULL");
+  if (!workspace || workspace_bytes < 256)
+    return fail(HINM_EWORKSPACE, "translate workspace of %zu bytes given, 256 needed", workspace_bytes);
+  if (!hinm::aligned(workspace, 256)) return fail(HINM_EALIGN, "workspace is not 256-byte aligned");
+  st = hinm::ensure_device();
+  if (st) return st;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  int* flag = static_cast<int*>(workspace);
+  // 1. map must be a permutation of 0..cin-1 (nothing is written otherwise)
+  hipLaunchKernelGGL(zero_flag_kernel, dim3(1), dim3(64), 0, stream, flag);
+  hipLaunchKernelGGL(check_perm_kernel, dim3(1), dim3(1024), ((p.cin + 31) / 32) * 4, stream, map, p.cin, flag);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "translate check launch");
+  int hflag = 0;
+  e = hipMemcpyAsync(&hflag, flag, sizeof(int), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "translate check");
+  if (hflag & kFlagPerm) return fail(HINM_EPERM, "map is not a permutation of 0..%d", p.cin - 1);
+  // 2. rewrite both index lists in place
+  const int64_t nd = (int64_t)p.n_tiles * p.n_dense_pad, ns = (int64_t)p.n_tiles * p.n_24_pad;
+  if (nd > 0)
+    hipLaunchKernelGGL(translate_kernel, dim3((unsigned)((nd + 255) / 256)), dim3(256), 0, stream, packed->idx_dense,
+                       nd, map);
+  if (ns > 0)
+    hipLaunchKernelGGL(translate_kernel, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, stream, packed->idx_24,
+                       ns, map);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "translate launch");
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "translate");
   return HINM_OK;
 }

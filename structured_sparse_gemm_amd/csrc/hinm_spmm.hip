@@ -53,7 +53,16 @@ struct SpmmArgs {
   int x_vec;                 // 1: 16-byte aligned X rows (ldx % 8 == 0)
   int y_vec;                 // 1: 16-byte aligned Y rows (ldy % 8 == 0)
   int n_tiles;
+  const int32_t* out_rows;   // NULL, or the Y row of each product row
 };
+
+// Y row that product row r goes to: r itself, or out_rows[r]; -1 for an
+// out-of-range entry (the row is then not written).
+__device__ inline int64_t y_row(const SpmmArgs& a, int64_t r) {
+  if (!a.out_rows) return r;
+  const int64_t d = a.out_rows[r];
+  return (d >= 0 && d < a.cout) ? d : -1;
+}
 
 __device__ inline uint16_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -162,7 +171,10 @@ __global__ __launch_bounds__(kWaves * 64) void spmm_kernel(SpmmArgs a) {
     const int n = n0 + nb * 16 + (lane & 15);
     if (a.splits == 1) {
       if (n < a.batch)
-        for (int i = 0; i < 4; ++i) a.y[(grow0 + i) * a.ldy + n] = bf16_rne(acc[nb][i]);
+        for (int i = 0; i < 4; ++i) {
+          const int64_t yr = y_row(a, grow0 + i);
+          if (yr >= 0) a.y[yr * a.ldy + n] = bf16_rne(acc[nb][i]);
+        }
     } else if (n < a.batch_pad16) {
       float* dst = a.ws + ((int64_t)split * a.cout + grow0) * a.batch_pad16 + n;
       for (int i = 0; i < 4; ++i) dst[(int64_t)i * a.batch_pad16] = acc[nb][i];
@@ -172,7 +184,8 @@ __global__ __launch_bounds__(kWaves * 64) void spmm_kernel(SpmmArgs a) {
 
 // Sum of the split partials in split order, then bf16 into Y.
 __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ ws, int splits, int cout, int batch,
-                                                     int batch_pad16, uint16_t* __restrict__ y, int64_t ldy) {
+                                                     int batch_pad16, uint16_t* __restrict__ y, int64_t ldy,
+                                                     const int32_t* __restrict__ out_rows) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (int64_t)cout * batch) return;
   const int64_t row = i / batch;
@@ -181,7 +194,8 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ w
   const float* src = ws + row * batch_pad16 + n;
   float acc = 0.f;
   for (int s = 0; s < splits; ++s) acc += src[s * plane];
-  y[row * ldy + n] = bf16_rne(acc);
+  const int64_t yr = out_rows ? (int64_t)out_rows[row] : row;
+  if (yr >= 0 && yr < cout) y[yr * ldy + n] = bf16_rne(acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -328,7 +342,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode3_kernel(SpmmArgs a) {
     const int r = o / NTOK, n = o % NTOK;
     float sum = 0.f;
     for (int w = 0; w < kDecWaves; ++w) sum += red[w * 16 * NTOK + o];
-    if (n0 + n < a.batch) a.y[((int64_t)t * a.rows + rb * 16 + r) * a.ldy + n0 + n] = bf16_rne(sum);
+    const int64_t yr = y_row(a, (int64_t)t * a.rows + rb * 16 + r);
+    if (n0 + n < a.batch && yr >= 0) a.y[yr * a.ldy + n0 + n] = bf16_rne(sum);
   }
 }
 
@@ -493,7 +508,10 @@ __global__ __launch_bounds__(384) void decode5_kernel(SpmmArgs a, int splits, in
       for (int nb = 0; nb < NB; ++nb) {
         const int n = n0 + 16 * nb + i16;
         if (n < a.batch)
-          for (int e = 0; e < 4; ++e) a.y[(grow0 + e) * a.ldy + n] = bf16_rne(acc[0][nb][e]);
+          for (int e = 0; e < 4; ++e) {
+            const int64_t yr = y_row(a, grow0 + e);
+            if (yr >= 0) a.y[yr * a.ldy + n] = bf16_rne(acc[0][nb][e]);
+          }
       }
     return;
   }
@@ -538,7 +556,8 @@ __global__ __launch_bounds__(384) void decode5_kernel(SpmmArgs a, int splits, in
   for (int k = 0; k < OPT; ++k) {
     const int o = threadIdx.x + 256 * k;
     const int r = o / NTOK, n = o % NTOK;
-    if (n0 + n < a.batch) a.y[(grow_base + r) * a.ldy + n0 + n] = bf16_rne(sum[k]);
+    const int64_t yr = y_row(a, grow_base + r);
+    if (n0 + n < a.batch && yr >= 0) a.y[yr * a.ldy + n0 + n] = bf16_rne(sum[k]);
   }
   if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next call
 }
@@ -835,7 +854,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
         const int r = q / C::CPR, c = q % C::CPR;
         const int n = n0 + 8 * c;
         if (n >= a.batch) continue;
-        uint16_t* dst = a.y + ((int64_t)t * a.rows + rb * 64 + r) * a.ldy + n;
+        const int64_t yr = y_row(a, (int64_t)t * a.rows + rb * 64 + r);
+        if (yr < 0) continue;
+        uint16_t* dst = a.y + yr * a.ldy + n;
         const uint16_t* src = ys + r * C::PITCH + 8 * c;
         if (a.y_vec && n + 8 <= a.batch) {
           *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
@@ -870,9 +891,8 @@ int ensure_device() {
 
 }  // namespace hinm
 
-extern "C" int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_t batch, int64_t ldx, void* y_bf16,
-                         int64_t ldy, void* workspace, size_t workspace_bytes, void* stream_) {
-  hinm::clear_error();
+static int spmm_impl(const hinm_packed_t* packed, const void* x_bf16, int64_t batch, int64_t ldx, void* y_bf16,
+                     int64_t ldy, const int32_t* out_rows, void* workspace, size_t workspace_bytes, void* stream_) {
   if (!packed) return fail(HINM_EINVAL, "packed is NULL");
   int st = hinm::check_plan(&packed->plan);
   if (st) return st;
@@ -930,6 +950,7 @@ extern "C" int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_
   a.x_vec = hinm::aligned(x_bf16, 16) && (ldx % 8 == 0);
   a.y_vec = hinm::aligned(y_bf16, 16) && (ldy % 8 == 0);
   a.n_tiles = p.n_tiles;
+  a.out_rows = out_rows;
 
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   // The prefill and split decode kernels address X and the packed buffers
@@ -1004,10 +1025,25 @@ extern "C" int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_
     if (sh.splits > 1) {
       const int64_t n = (int64_t)p.cout * batch;
       hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a.ws, sh.splits,
-                         p.cout, (int)batch, a.batch_pad16, a.y, ldy);
+                         p.cout, (int)batch, a.batch_pad16, a.y, ldy, a.out_rows);
     }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(HINM_EHIP, "spmm launch: %s", hipGetErrorString(e));
   return HINM_OK;
+}
+
+extern "C" int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_t batch, int64_t ldx, void* y_bf16,
+                         int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
+  hinm::clear_error();
+  return spmm_impl(packed, x_bf16, batch, ldx, y_bf16, ldy, nullptr, workspace, workspace_bytes, stream);
+}
+
+extern "C" int hinm_spmm_rows(const hinm_packed_t* packed, const void* x_bf16, int64_t batch, int64_t ldx,
+                              void* y_bf16, int64_t ldy, const int32_t* out_rows, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  hinm::clear_error();
+  if (!out_rows) return fail(HINM_EINVAL, "out_rows is NULL");
+  if (!hinm::aligned(out_rows, 4)) return fail(HINM_EALIGN, "out_rows is not 4-byte aligned");
+  return spmm_impl(packed, x_bf16, batch, ldx, y_bf16, ldy, out_rows, workspace, workspace_bytes, stream);
 }

@@ -121,6 +121,31 @@ def test_spmm_host_errors(lib):
     assert call(pk=hinm.PackedT(bad, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20)) == 1
 
 
+def test_spmm_rows_and_translate_host_errors(lib):
+    """The output-row and index-translation entry points check their extra arguments on the host."""
+    p = hinm.plan(4096, 4096, 64, 0.5, 0.25)
+    pk = _fake_packed(p)
+    rows = lambda **kw: lib.hinm_spmm_rows(ctypes.byref(kw.get("pk", pk)), kw.get("x", 4096), kw.get("batch", 2048),
+                                           kw.get("ldx", 2048), kw.get("y", 4096), kw.get("ldy", 2048),
+                                           kw.get("out_rows", 1 << 20), kw.get("ws", None), kw.get("wsb", 0), None)
+    assert rows(out_rows=None) == 1
+    assert rows(out_rows=(1 << 20) + 2) == 5
+    assert rows(batch=-1) == 2                      # then everything hinm_spmm checks
+    assert rows(x=None) == 1
+    assert rows(batch=0, ldx=0, ldy=0) == 0
+    tr = lambda **kw: lib.hinm_translate_indices(ctypes.byref(kw.get("pk", pk)), kw.get("map", 1 << 20),
+                                                 kw.get("ws", 1 << 20), kw.get("wsb", 256), None)
+    assert tr(map=None) == 1
+    assert tr(map=(1 << 20) + 2) == 5
+    assert tr(ws=None) == 6
+    assert tr(wsb=255) == 6
+    assert tr(ws=(1 << 20) + 16) == 5
+    assert tr(pk=hinm.PackedT(p.raw, None, None, None, None, None)) == 1
+    bad = hinm.PlanT.from_buffer_copy(p.raw)
+    bad.n_24 += 4
+    assert tr(pk=hinm.PackedT(bad, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20)) == 1
+
+
 def test_pack_host_errors(lib):
     p = hinm.plan(128, 256, 32, 0.75, 0.5)
     wsb = hinm.pack_workspace_bytes(p)

@@ -468,3 +468,70 @@ def test_mutation_transposed_product_is_caught(monkeypatch):
     monkeypatch.setattr(oh, "spmm", lambda w, x: (np.asarray(x, np.float64).T @ np.asarray(w, np.float64).T).T[:, ::-1])
     with pytest.raises(AssertionError):
         test_gemm_brute_force()
+
+
+# --------------------------------------------------------------------------------------
+# Output-channel permutation at write-out and cross-layer index translation
+# (FlexHiNM-GP notes, key designs 2 and 4; highlights)
+# --------------------------------------------------------------------------------------
+
+def test_scatter_rows_brute_force():
+    rng = np.random.default_rng(3)
+    y = rng.standard_normal((7, 3))
+    out_rows = rng.permutation(7)
+    res = oh.scatter_rows(y, out_rows)
+    for r in range(7):
+        assert np.array_equal(res[out_rows[r]], y[r])
+    assert np.array_equal(oh.scatter_rows(y, np.arange(7)), y)
+    with pytest.raises(ValueError):
+        oh.scatter_rows(y, np.array([0, 0, 1, 2, 3, 4, 5]))
+
+
+def test_translate_indices_brute_force():
+    rng = np.random.default_rng(4)
+    mapping = rng.permutation(12)
+    idx = np.array([[3, -1, 0, 11], [7, 7, -1, -1]])
+    out = oh.translate_indices(idx, mapping)
+    for (i, j), v in np.ndenumerate(idx):
+        assert out[i, j] == (-1 if v < 0 else mapping[v])
+    with pytest.raises(ValueError):
+        oh.translate_indices(idx, np.zeros(12, dtype=np.int64))
+
+
+def test_two_layer_chain_permuted_storage():
+    """Layer A writes its rows through out_rows = sigma; layer B, whose indices are translated by
+    mapping = sigma (channel c is stored at row sigma[c]), reads the stored activations and produces
+    exactly the product over activations in channel order.  Integer-valued inputs keep every sum exact."""
+    rng = np.random.default_rng(5)
+    wa = synth.small(64, 32, 32, 0.5, 0.25, 4, 31)
+    wb = synth.small(32, 64, 32, 0.5, 0.25, 4, 32)
+    pa, packed_a, _ = run_pack(wa)
+    pb, packed_b, _ = run_pack(wb)
+    x = rng.integers(-3, 4, size=(32, 4)).astype(np.float64)
+    wa_hat = np.round(oh.unpack(packed_a, pa) * 8)      # small integers: exact float64 sums
+    ya = oh.spmm(wa_hat, x)                              # activations in channel order [64 x 4]
+    sigma = rng.permutation(64)
+    stored = oh.scatter_rows(ya, sigma)                  # row sigma[c] holds channel c
+    pk_t = dict(packed_b)
+    pk_t["idx_dense"] = oh.translate_indices(packed_b["idx_dense"], sigma)
+    pk_t["idx_24"] = oh.translate_indices(packed_b["idx_24"], sigma)
+    wb_hat = np.round(oh.unpack(packed_b, pb) * 8)
+    wb_hat_t = np.round(oh.unpack(pk_t, pb) * 8)         # columns moved to the stored rows
+    assert np.array_equal(oh.spmm(wb_hat_t, stored), oh.spmm(wb_hat, ya))
+    # the translation is not the identity, so the check above is not vacuous
+    assert not np.array_equal(wb_hat_t, wb_hat)
+
+
+def test_mutation_translate_inverse_is_caught(monkeypatch):
+    orig = oh.translate_indices
+    monkeypatch.setattr(oh, "translate_indices", lambda idx, m: orig(idx, np.argsort(m)))
+    with pytest.raises(AssertionError):
+        test_two_layer_chain_permuted_storage()
+
+
+def test_mutation_scatter_as_gather_is_caught(monkeypatch):
+    monkeypatch.setattr(oh, "scatter_rows", lambda y, r: np.asarray(y)[np.asarray(r)])
+    with pytest.raises(AssertionError):
+        test_scatter_rows_brute_force()
+    with pytest.raises(AssertionError):
+        test_two_layer_chain_permuted_storage()
