@@ -415,6 +415,20 @@ __global__ __launch_bounds__(384) void decode5_kernel(SpmmArgs a, int splits, in
   f32x4 acc[2][NB];
   for (int h = 0; h < 2; ++h)
     for (int j = 0; j < NB; ++j) acc[h][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Y rows of this thread's outputs, read now so that the write-out at the
+  // end does not wait for them: rows grow0 + e (one split) or the rows of
+  // the final reduction (several splits).
+  constexpr int OPT = 64 * NTOK / 256;
+  const int64_t grow0 = (int64_t)t * a.rows + rb * 64 + (wave & 3) * 16 + 4 * kc;
+  const int64_t grow_base = (int64_t)t * a.rows + rb * 64;
+  int64_t yrow[OPT > 4 ? OPT : 4];
+  if (threadIdx.x < 256) {
+    if (splits == 1) {
+      for (int e = 0; e < 4; ++e) yrow[e] = y_row(a, grow0 + e);
+    } else {
+      for (int k = 0; k < OPT; ++k) yrow[k] = y_row(a, grow_base + (threadIdx.x + 256 * k) / NTOK);
+    }
+  }
 
   for (int r0 = b_lo; r0 < b_hi; r0 += MAXB) {
     const int r1 = min(r0 + MAXB, b_hi);
@@ -502,16 +516,13 @@ __global__ __launch_bounds__(384) void decode5_kernel(SpmmArgs a, int splits, in
   for (int j = 0; j < NB; ++j) acc[0][j] += acc[1][j];
 
   // acc[nb][e]: tile row rb*64 + wave*16 + 4*kc + e, token 16*nb + i16.
-  const int64_t grow0 = (int64_t)t * a.rows + rb * 64 + (wave & 3) * 16 + 4 * kc;
   if (splits == 1) {
     if (!gather)
       for (int nb = 0; nb < NB; ++nb) {
         const int n = n0 + 16 * nb + i16;
         if (n < a.batch)
-          for (int e = 0; e < 4; ++e) {
-            const int64_t yr = y_row(a, grow0 + e);
-            if (yr >= 0) a.y[yr * a.ldy + n] = bf16_rne(acc[0][nb][e]);
-          }
+          for (int e = 0; e < 4; ++e)
+            if (yrow[e] >= 0) a.y[yrow[e] * a.ldy + n] = bf16_rne(acc[0][nb][e]);
       }
     return;
   }
@@ -534,8 +545,6 @@ __global__ __launch_bounds__(384) void decode5_kernel(SpmmArgs a, int splits, in
     s_last = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(splits - 1);
   __syncthreads();
   if (!s_last || threadIdx.x >= 256) return;
-  const int64_t grow_base = (int64_t)t * a.rows + rb * 64;
-  constexpr int OPT = 64 * NTOK / 256;
   const int64_t plane = (int64_t)n_tb * a.cout * NTOK;
   const float* p0 = part + ((int64_t)tb * a.cout + grow_base) * NTOK;
   float sum[OPT];
@@ -555,9 +564,8 @@ __global__ __launch_bounds__(384) void decode5_kernel(SpmmArgs a, int splits, in
   }
   for (int k = 0; k < OPT; ++k) {
     const int o = threadIdx.x + 256 * k;
-    const int r = o / NTOK, n = o % NTOK;
-    const int64_t yr = y_row(a, grow_base + r);
-    if (n0 + n < a.batch && yr >= 0) a.y[yr * a.ldy + n0 + n] = bf16_rne(sum[k]);
+    const int n = o % NTOK;
+    if (n0 + n < a.batch && yrow[k] >= 0) a.y[yrow[k] * a.ldy + n0 + n] = bf16_rne(sum[k]);
   }
   if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next call
 }
