@@ -302,6 +302,28 @@ def main():
                  "spmm_rows_batch_16_ms": round(rd_rows["ms_mean"], 5), "spmm_batch_16_ms": round(rd["ms_mean"], 5),
                  "translate_indices_ms": [round(v, 3) for v in tr_ms]}
 
+    # NEXT row: the boundary search for v_s on the device (down_proj sweep workload, t_s 0.7)
+    wb_ = synth.down_proj_sweep(0.7)
+    imp_b, perm_b = wb_.importance.to(dev), wb_.perm.to(dev)
+    hinm.boundary_search(imp_b, perm_b, 64, 0.7)
+    torch.cuda.synchronize()
+    bs_ms = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        v_b, tr_b = hinm.boundary_search(imp_b, perm_b, 64, 0.7)
+        bs_ms.append((time.perf_counter() - t0) * 1e3)
+    next_bs = {"what": "hinm_boundary_search wall time, down_proj 4096x11008 with 5% outlier columns, importance W*W, "
+                       "t_s 0.7 (synchronous: checks, scores, ranking, then one device pass and one host read per grid "
+                       "point)", "ms": [round(x, 2) for x in bs_ms], "v_s": v_b, "grid_points": len(tr_b)}
+    if not args.no_cpu:
+        import oracle.hinm as oh
+        p_b = oh.plan(wb_.cout, wb_.cin, 64, 0.7, 0.7)
+        s_b = oh.vector_scores(wb_.importance.numpy(), p_b)
+        t0 = time.perf_counter()
+        oh.retained_importance(wb_.importance.numpy(), wb_.perm.numpy(), oh.plan(wb_.cout, wb_.cin, 64, 0.7, 0.6), s_b)
+        next_bs["oracle_s_per_grid_point"] = round(time.perf_counter() - t0, 3)
+        next_bs["oracle_sample"] = "one grid point (v_s 0.6) of the same search, scores precomputed"
+
     dense = None
     if not args.no_dense:
         dense_ms = time_dense(torch, wgpu, x, max(10, args.steps // 2), 3)
@@ -348,6 +370,7 @@ def main():
         "batch_2048_hbm_gbs": round(alg["bytes"] / (ms * 1e-3) / 1e9, 1),
         "pack_ms": [round(v, 2) for v in pack_ms],
         "next_output_permutation": next_rows,
+        "next_boundary_search": next_bs,
         "dense_comparator": dense,
         "cpu_baseline": cpu,
     }

@@ -202,6 +202,38 @@ int hinm_spmm_rows(const hinm_packed_t* packed, const void* x_bf16, int64_t batc
 int hinm_translate_indices(hinm_packed_t* packed, const int32_t* map, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* Device scratch that hinm_boundary_search needs, in bytes (host only; the
+ * same for every t_s). */
+int hinm_boundary_workspace_bytes(int64_t cout, int64_t cin, int32_t tile_rows, size_t* bytes);
+
+/* Boundary search for v_s (FlexHiNM-GP notes, key design 1): with t_s fixed,
+ * the closed form leaves v_s as the only free parameter; the search starts
+ * at v_s = t_s and lowers it by `step` while the retained importance
+ *     R_total(v) = R_dense(v) + R_24(v)
+ * does not decrease, stopping at the first strict decrease.  R_dense sums
+ * the vector scores (as in hinm_pack, step 1) of the dense columns of every
+ * tile; R_24 sums, over every row and every 2:4 group (as in hinm_pack,
+ * steps 2-4, with the region counts of v), the two largest importances of
+ * the group.  Grid: v_k = t_s - step*k for k = 0, 1, ... while
+ * v_k >= max(0, 2 t_s - 1) - 1e-12, the last point clamped to that bound.
+ * The result is n_pruned / cin of the plan at the last v before the
+ * decrease (so hinm_plan reproduces the same counts from it).  Sums are
+ * float64 in a fixed order (per tile and per row on the device, then the
+ * tiles and rows in ascending order on the host): the same inputs give the
+ * same trace on every call.
+ * Inputs (device): importance fp32 [cout][ldi] (finite, >= 0), perm int32
+ * [n_tiles][cin] or NULL.  Outputs (host): *v_s_out; the first trace_cap
+ * grid points visited and their R_total in trace_v / trace_r (may be NULL
+ * when trace_cap == 0), their number in *trace_len (may be NULL).
+ * workspace (device, 256-byte aligned) of hinm_boundary_workspace_bytes.
+ * Synchronous.  Errors: HINM_EINVAL (also a non-positive step), HINM_ESHAPE,
+ * HINM_EPERM, HINM_EIMPORTANCE, HINM_EALIGN, HINM_EWORKSPACE, HINM_EHIP,
+ * HINM_EDEVICE. */
+int hinm_boundary_search(int64_t cout, int64_t cin, int32_t tile_rows, double t_s, double step,
+                         const float* importance, int64_t ldi, const int32_t* perm, void* workspace,
+                         size_t workspace_bytes, double* v_s_out, double* trace_v, double* trace_r,
+                         int32_t trace_cap, int32_t* trace_len, void* stream);
+
 /* Static description of a status code. */
 const char* hinm_status_str(int status);
 

@@ -27,7 +27,7 @@ STATUS = {0: "HINM_OK", 1: "HINM_EINVAL", 2: "HINM_ESHAPE", 3: "HINM_EPERM", 4: 
 # Every symbol the C ABI exports (include/hinm.h).
 EXPORTS = ("hinm_abi_version", "hinm_plan", "hinm_pack_workspace_bytes", "hinm_pack",
            "hinm_spmm_workspace_bytes", "hinm_spmm", "hinm_spmm_rows", "hinm_translate_indices",
-           "hinm_status_str", "hinm_last_error")
+           "hinm_boundary_workspace_bytes", "hinm_boundary_search", "hinm_status_str", "hinm_last_error")
 
 
 class HinmError(RuntimeError):
@@ -76,6 +76,10 @@ def library() -> ctypes.CDLL:
             "hinm_spmm": ([ctypes.POINTER(PackedT), VP, I64, I64, VP, I64, VP, S, VP], ctypes.c_int),
             "hinm_spmm_rows": ([ctypes.POINTER(PackedT), VP, I64, I64, VP, I64, VP, VP, S, VP], ctypes.c_int),
             "hinm_translate_indices": ([ctypes.POINTER(PackedT), VP, VP, S, VP], ctypes.c_int),
+            "hinm_boundary_workspace_bytes": ([I64, I64, I32, ctypes.POINTER(S)], ctypes.c_int),
+            "hinm_boundary_search": ([I64, I64, I32, D, D, VP, I64, VP, VP, S, ctypes.POINTER(D),
+                                      ctypes.POINTER(D), ctypes.POINTER(D), I32, ctypes.POINTER(I32), VP],
+                                     ctypes.c_int),
             "hinm_status_str": ([ctypes.c_int], ctypes.c_char_p),
             "hinm_last_error": ([], ctypes.c_char_p),
         }
@@ -308,6 +312,33 @@ def translate_indices(packed: HinmPacked, mapping: torch.Tensor) -> HinmPacked:
     return packed
 
 
-__all__ = ["HinmError", "HinmPacked", "Plan", "plan", "pack", "spmm", "translate_indices", "alloc_packed",
+def boundary_search(importance: torch.Tensor, perm: Optional[torch.Tensor], tile_rows: int, t_s: float,
+                    step: float = 0.01, trace_cap: int = 256):
+    """Device boundary search for v_s (hinm_boundary_search).  importance fp32 [cout, cin] and perm int32
+    [n_tiles, cin] (or None) on the device.  Returns (v_s, [(v, R_total), ...] of the grid points visited)."""
+    if importance.dtype != torch.float32 or importance.dim() != 2 or importance.stride(1) != 1:
+        raise ValueError("importance must be float32 [cout, cin] with unit column stride")
+    cout, cin = importance.shape
+    dev = importance.device
+    if perm is not None and (perm.dtype != torch.int32 or not perm.is_contiguous() or perm.device != dev):
+        raise ValueError("perm must be a contiguous int32 tensor on the importance's device")
+    lib = library()
+    n = ctypes.c_size_t()
+    _check(lib.hinm_boundary_workspace_bytes(cout, cin, tile_rows, ctypes.byref(n)))
+    ws = torch.empty(n.value, dtype=torch.uint8, device=dev)
+    v = ctypes.c_double()
+    tv = (ctypes.c_double * trace_cap)()
+    tr = (ctypes.c_double * trace_cap)()
+    tl = ctypes.c_int32()
+    with torch.cuda.device(dev):
+        _check(lib.hinm_boundary_search(cout, cin, tile_rows, float(t_s), float(step), importance.data_ptr(),
+                                        importance.stride(0), perm.data_ptr() if perm is not None else None,
+                                        ws.data_ptr(), ws.numel(), ctypes.byref(v), tv, tr, trace_cap,
+                                        ctypes.byref(tl), _stream_ptr(dev)))
+    k = min(tl.value, trace_cap)
+    return v.value, [(tv[i], tr[i]) for i in range(k)]
+
+
+__all__ = ["HinmError", "HinmPacked", "Plan", "plan", "pack", "spmm", "translate_indices", "boundary_search", "alloc_packed",
            "pack_workspace_bytes",
            "spmm_workspace_bytes", "library", "LIB_PATH", "EXPORTS"]

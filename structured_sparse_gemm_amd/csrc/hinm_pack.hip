@@ -4,6 +4,10 @@
 // identical to the definition) more than speed, but every kernel is a plain
 // data-parallel pass with coalesced stores.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <vector>
 #include <math.h>
 #include <stdint.h>
 
@@ -214,6 +218,85 @@ __global__ __launch_bounds__(256) void translate_kernel(int32_t* __restrict__ id
   if (v >= 0) idx[i] = map[v];
 }
 
+// ---------------------------------------------------------------------------
+// Boundary search on the device (FlexHiNM-GP notes, key design 1): the
+// column ranking does not depend on v_s, so it is computed once; each grid
+// point then only moves the two cuts, rebuilds the 2:4 groups in permuted
+// order and sums the retained importance.
+// ---------------------------------------------------------------------------
+
+// rank[t][c] = position of column c under the order (-score, column).
+__global__ __launch_bounds__(256) void rank_kernel(const double* __restrict__ s, int cin, int32_t* __restrict__ rank) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  const int t = blockIdx.y;
+  const double* st = s + (int64_t)t * cin;
+  const double sc = c < cin ? st[c] : 0.0;
+  int r = 0;
+  for (int j = 0; j < cin; ++j) {
+    const double sj = st[j];
+    r += (sj > sc) | ((sj == sc) & (j < c));
+  }
+  if (c < cin) rank[(int64_t)t * cin + c] = r;
+}
+
+__global__ __launch_bounds__(256) void cut_kernel(const int32_t* __restrict__ rank, int64_t n, int n_dense, int n_24,
+                                                  uint8_t* __restrict__ reg) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int r = rank[i];
+  reg[i] = r < n_dense ? kDense : (r < n_dense + n_24 ? kTwoFour : kPruned);
+}
+
+// Fixed-order sum of 256 per-thread values (thread 0 holds the result).
+__device__ inline double block_sum_256(double v, double* sh) {
+  sh[threadIdx.x] = v;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) sh[threadIdx.x] += sh[threadIdx.x + w];
+    __syncthreads();
+  }
+  return sh[0];
+}
+
+// R_dense of tile t: sum of the scores of its dense columns.  Thread k adds
+// columns k, k+256, ... in ascending order, then a fixed tree: the same
+// float64 value on every run.
+__global__ __launch_bounds__(256) void rdense_kernel(const double* __restrict__ s, const int32_t* __restrict__ rank,
+                                                     int cin, int n_dense, double* __restrict__ part) {
+  __shared__ double sh[256];
+  const int t = blockIdx.x;
+  double acc = 0.0;
+  for (int c = threadIdx.x; c < cin; c += 256)
+    if (rank[(int64_t)t * cin + c] < n_dense) acc += s[(int64_t)t * cin + c];
+  const double tot = block_sum_256(acc, sh);
+  if (threadIdx.x == 0) part[t] = tot;
+}
+
+// R_24 of one row of tile t: over its 2:4 groups, the two largest
+// importances of each group (the kept pair; ties do not change the sum),
+// added in float64.  Thread k takes groups k, k+256, ...; fixed tree.
+__global__ __launch_bounds__(256) void r24_kernel(const float* __restrict__ imp, int64_t ldi,
+                                                  const int32_t* __restrict__ idx_s, int n_24_pad, int groups, int rows,
+                                                  double* __restrict__ part) {
+  __shared__ double sh[256];
+  const int t = blockIdx.y, r = blockIdx.x;
+  const float* row = imp + ((int64_t)t * rows + r) * ldi;
+  const int32_t* list = idx_s + (int64_t)t * n_24_pad;
+  double acc = 0.0;
+  for (int q = threadIdx.x; q < groups; q += 256) {
+    float a[4];
+    for (int k = 0; k < 4; ++k) a[k] = row[list[4 * q + k]];
+    // two largest of four
+    float m1 = fmaxf(a[0], a[1]), n1 = fminf(a[0], a[1]);
+    float m2 = fmaxf(a[2], a[3]), n2 = fminf(a[2], a[3]);
+    const float top = fmaxf(m1, m2);
+    const float second = fmaxf(fminf(m1, m2), fmaxf(n1, n2));
+    acc += (double)top + (double)second;
+  }
+  const double tot = block_sum_256(acc, sh);
+  if (threadIdx.x == 0) part[(int64_t)t * rows + r] = tot;
+}
+
 }  // namespace
 
 extern "C" int hinm_pack(const hinm_plan_t* plan, const void* w_bf16, int64_t ldw, const float* importance,
@@ -331,5 +414,119 @@ extern "C" int hinm_translate_indices(hinm_packed_t* packed, const int32_t* map,
   if (e != hipSuccess) return hip_fail(e, "translate launch");
   e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_fail(e, "translate");
+  return HINM_OK;
+}
+
+extern "C" int hinm_boundary_workspace_bytes(int64_t cout, int64_t cin, int32_t tile_rows, size_t* bytes) {
+  hinm::clear_error();
+  if (!bytes) return fail(HINM_EINVAL, "bytes is NULL");
+  hinm_plan_t p;
+  int st = hinm_plan(cout, cin, tile_rows, 0.5, 0.5, &p);
+  if (st) return st;
+  const size_t T = (size_t)p.n_tiles, C = (size_t)p.cin, R = (size_t)p.tile_rows;
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  const size_t list = up(T * (C + 64) * 4);
+  *bytes = 256 + up(T * C * 8) + up(T * C * 4) + up(T * C) + 2 * list + up((T + T * R) * 8);
+  return HINM_OK;
+}
+
+extern "C" int hinm_boundary_search(int64_t cout, int64_t cin, int32_t tile_rows, double t_s, double step,
+                                    const float* importance, int64_t ldi, const int32_t* perm, void* workspace,
+                                    size_t workspace_bytes, double* v_s_out, double* trace_v, double* trace_r,
+                                    int32_t trace_cap, int32_t* trace_len, void* stream_) {
+  hinm::clear_error();
+  if (!importance || !v_s_out) return fail(HINM_EINVAL, "importance and v_s_out must be non-NULL");
+  if (!(step > 0.0) || !std::isfinite(step)) return fail(HINM_EINVAL, "step=%g must be a positive finite number", step);
+  if (trace_cap < 0 || (trace_cap > 0 && (!trace_v || !trace_r))) return fail(HINM_EINVAL, "bad trace arguments");
+  hinm_plan_t p0;
+  int st = hinm_plan(cout, cin, tile_rows, t_s, t_s, &p0);
+  if (st) return st;
+  if (ldi < cin) return fail(HINM_ESHAPE, "ldi=%lld < cin=%lld", (long long)ldi, (long long)cin);
+  if (!hinm::aligned(importance, 4) || (perm && !hinm::aligned(perm, 4)))
+    return fail(HINM_EALIGN, "importance and perm must be 4-byte aligned");
+  size_t need = 0;
+  hinm_boundary_workspace_bytes(cout, cin, tile_rows, &need);
+  if (!workspace || workspace_bytes < need)
+    return fail(HINM_EWORKSPACE, "boundary workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if (!hinm::aligned(workspace, 256)) return fail(HINM_EALIGN, "workspace is not 256-byte aligned");
+  st = hinm::ensure_device();
+  if (st) return st;
+
+  const int T = p0.n_tiles, C = p0.cin, R = p0.tile_rows;
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  char* ws = static_cast<char*>(workspace);
+  int* flag = reinterpret_cast<int*>(ws);
+  size_t off = 256;
+  double* scores = reinterpret_cast<double*>(ws + off);  off += up((size_t)T * C * 8);
+  int32_t* rank = reinterpret_cast<int32_t*>(ws + off);  off += up((size_t)T * C * 4);
+  uint8_t* reg = reinterpret_cast<uint8_t*>(ws + off);   off += up((size_t)T * C);
+  int32_t* idx_d = reinterpret_cast<int32_t*>(ws + off); off += up((size_t)T * (C + 64) * 4);
+  int32_t* idx_s = reinterpret_cast<int32_t*>(ws + off); off += up((size_t)T * (C + 64) * 4);
+  double* part = reinterpret_cast<double*>(ws + off);
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+
+  // checks and scores (as hinm_pack), then the ranking, once
+  hipLaunchKernelGGL(zero_flag_kernel, dim3(1), dim3(64), 0, stream, flag);
+  if (perm)
+    hipLaunchKernelGGL(check_perm_kernel, dim3(T), dim3(1024), ((C + 31) / 32) * 4, stream, perm, C, flag);
+  hipLaunchKernelGGL(scores_kernel, dim3((C + 255) / 256, T), dim3(256), 0, stream, importance, ldi, C, R, scores, flag);
+  hipLaunchKernelGGL(rank_kernel, dim3((C + 255) / 256, T), dim3(256), 0, stream, scores, C, rank);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "boundary set-up launch");
+  int hflag = 0;
+  e = hipMemcpyAsync(&hflag, flag, sizeof(int), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "boundary set-up");
+  if (hflag & kFlagPerm) return fail(HINM_EPERM, "a perm row is not a permutation of 0..%d", C - 1);
+  if (hflag & kFlagImportance) return fail(HINM_EIMPORTANCE, "importance has a negative or non-finite entry");
+
+  // grid v = t_s - step*k, k = 0, 1, ..., down to max(0, 2 t_s - 1); stop at the first strict decrease
+  const double lo = std::max(0.0, 2.0 * t_s - 1.0);
+  std::vector<double> hpart((size_t)T + (size_t)T * R);
+  double best_v = t_s, best_r = 0.0;
+  bool have = false;
+  int n_trace = 0;
+  for (int k = 0;; ++k) {
+    double v = t_s - step * k;
+    if (v < lo - 1e-12) break;
+    v = std::max(v, lo);
+    hinm_plan_t pv;
+    st = hinm_plan(cout, cin, tile_rows, t_s, v, &pv);
+    if (st) return st;
+    const int64_t n = (int64_t)T * C;
+    hipLaunchKernelGGL(cut_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, rank, n, pv.n_dense,
+                       pv.n_24, reg);
+    hipLaunchKernelGGL(compact_kernel, dim3(T), dim3(1024), 0, stream, perm, reg, C, pv.n_dense_pad, pv.n_24_pad,
+                       idx_d, idx_s);
+    hipLaunchKernelGGL(rdense_kernel, dim3(T), dim3(256), 0, stream, scores, rank, C, pv.n_dense, part);
+    if (pv.groups > 0)
+      hipLaunchKernelGGL(r24_kernel, dim3(R, T), dim3(256), 0, stream, importance, ldi, idx_s, pv.n_24_pad, pv.groups,
+                         R, part + T);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "boundary launch");
+    const size_t nbytes = ((size_t)T + (pv.groups > 0 ? (size_t)T * R : 0)) * sizeof(double);
+    e = hipMemcpyAsync(hpart.data(), part, nbytes, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "boundary step");
+    // total in a fixed order: tiles' dense sums, then rows' 2:4 sums
+    double r_tot = 0.0;
+    for (int t = 0; t < T; ++t) r_tot += hpart[t];
+    if (pv.groups > 0)
+      for (size_t i = 0; i < (size_t)T * R; ++i) r_tot += hpart[T + i];
+    if (n_trace < trace_cap) {
+      trace_v[n_trace] = v;
+      trace_r[n_trace] = r_tot;
+    }
+    ++n_trace;
+    if (have && r_tot < best_r) break;
+    best_v = v;
+    best_r = r_tot;
+    have = true;
+  }
+  hinm_plan_t pb;
+  st = hinm_plan(cout, cin, tile_rows, t_s, best_v, &pb);
+  if (st) return st;
+  *v_s_out = (double)pb.n_pruned / (double)cin;
+  if (trace_len) *trace_len = n_trace;
   return HINM_OK;
 }

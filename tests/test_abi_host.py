@@ -146,6 +146,33 @@ def test_spmm_rows_and_translate_host_errors(lib):
     assert tr(pk=hinm.PackedT(bad, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20)) == 1
 
 
+def test_boundary_search_host_errors(lib):
+    n = ctypes.c_size_t()
+    assert lib.hinm_boundary_workspace_bytes(4096, 11008, 64, ctypes.byref(n)) == 0
+    T, C = 64, 11008
+    assert n.value >= T * C * (8 + 4 + 1) + 2 * T * C * 4
+    assert lib.hinm_boundary_workspace_bytes(4096, 11007, 64, ctypes.byref(n)) == 2   # cin % 4
+    v = ctypes.c_double()
+    tv, tr, tl = (ctypes.c_double * 4)(), (ctypes.c_double * 4)(), ctypes.c_int32()
+    lib.hinm_boundary_workspace_bytes(4096, 11008, 64, ctypes.byref(n))
+    call = lambda **kw: lib.hinm_boundary_search(
+        kw.get("cout", 4096), kw.get("cin", 11008), 64, kw.get("t_s", 0.7), kw.get("step", 0.01),
+        kw.get("imp", 1 << 20), kw.get("ldi", 11008), kw.get("perm", None), kw.get("ws", 1 << 20),
+        kw.get("wsb", n.value), ctypes.byref(v), kw.get("tv", tv), kw.get("tr", tr), kw.get("cap", 4),
+        ctypes.byref(tl), None)
+    assert call(imp=None) == 1
+    assert call(step=0.0) == 1
+    assert call(step=float("nan")) == 1
+    assert call(cap=-1) == 1
+    assert call(tv=None) == 1
+    assert call(t_s=1.0) == 1
+    assert call(ldi=11000) == 2
+    assert call(imp=(1 << 20) + 2) == 5
+    assert call(ws=None) == 6
+    assert call(wsb=n.value - 1) == 6
+    assert call(ws=(1 << 20) + 16) == 5
+
+
 def test_pack_host_errors(lib):
     p = hinm.plan(128, 256, 32, 0.75, 0.5)
     wsb = hinm.pack_workspace_bytes(p)
