@@ -311,6 +311,94 @@ def spmm(w_hat: np.ndarray, x: np.ndarray) -> np.ndarray:
     return np.asarray(w_hat, dtype=np.float64) @ np.asarray(x, dtype=np.float64)
 
 
+def plan_tiles(cout: int, cin: int, tile_rows: int, t_s: float, v_s_tiles) -> List[Plan]:
+    """Per-tile region counts: the closed form of key design 1 at each tile's own v_s.
+
+    FlexHiNM-GP notes, "整体框架": the ratio of the three regions is decided
+    inside each output-channel tile.  t_s is shared, so every row of every
+    tile keeps cin - z entries; only the dense / 2:4 split moves.  Each
+    returned plan describes one tile (cout = tile_rows).
+    """
+    if tile_rows <= 0 or cout % tile_rows:
+        raise OracleError("tile_rows must divide cout")
+    v = [float(x) for x in v_s_tiles]
+    if len(v) != cout // tile_rows:
+        raise OracleError("one v_s per tile is needed")
+    return [plan(tile_rows, cin, tile_rows, t_s, vt) for vt in v]
+
+
+def pack_tiles(w_bits: np.ndarray, importance: np.ndarray, perm: Optional[np.ndarray], plans: List[Plan],
+               with_intermediates: bool = False):
+    """Pack with per-tile counts.  Tiles are independent (scores, regions,
+    index lists and 2:4 groups never cross a tile), so tile t is packed on its
+    own and the buffers of the tiles are laid end to end: the K-blocks of
+    tile t follow those of tile t-1.  ``tiles`` [T][4] holds, per tile, the
+    first dense block, n_dense, the first 2:4 block and n_24.
+    """
+    R = plans[0].tile_rows
+    T = len(plans)
+    cin = plans[0].cin
+    w_bits = np.asarray(w_bits)
+    d = np.asarray(importance, dtype=np.float32)
+    if perm is None:
+        perm = np.tile(np.arange(cin, dtype=np.int64), (T, 1))
+    perm = np.asarray(perm, dtype=np.int64)
+    parts, masks = [], []
+    tiles = np.zeros((T, 4), dtype=np.int64)
+    kd = ks = 0
+    for t, pt in enumerate(plans):
+        rows = slice(t * R, (t + 1) * R)
+        pk, inter = pack(w_bits[rows], d[rows], perm[t:t + 1], pt, with_intermediates=True)
+        parts.append(pk)
+        masks.append(inter["mask"])
+        tiles[t] = (kd, pt.n_dense, ks, pt.n_24)
+        kd += pt.n_dense_pad // KB_DENSE
+        ks += pt.n_24_pad // KB_24
+    packed = {
+        "val_dense": np.concatenate([q["val_dense"][0] for q in parts], axis=0),
+        "idx_dense": np.concatenate([q["idx_dense"][0] for q in parts], axis=0),
+        "val_24": np.concatenate([q["val_24"][0] for q in parts], axis=0),
+        "meta_24": np.concatenate([q["meta_24"][0] for q in parts], axis=0),
+        "idx_24": np.concatenate([q["idx_24"][0] for q in parts], axis=0),
+        "tiles": tiles,
+    }
+    if with_intermediates:
+        return packed, {"mask": np.concatenate(masks, axis=0)}
+    return packed
+
+
+def unpack_tiles(packed: Dict[str, np.ndarray], plans: List[Plan]) -> np.ndarray:
+    """Dense masked weight [cout][cin] (float64) from per-tile packed buffers."""
+    R, cin = plans[0].tile_rows, plans[0].cin
+    w = np.zeros((R * len(plans), cin), dtype=np.float64)
+    for t, pt in enumerate(plans):
+        kd, _, ks, _ = (int(v) for v in packed["tiles"][t])
+        nkd, nks = pt.n_dense_pad // KB_DENSE, pt.n_24_pad // KB_24
+        one = {"val_dense": packed["val_dense"][None, kd:kd + nkd],
+               "idx_dense": packed["idx_dense"][None, KB_DENSE * kd:KB_DENSE * (kd + nkd)],
+               "val_24": packed["val_24"][None, ks:ks + nks],
+               "meta_24": packed["meta_24"][None, ks:ks + nks],
+               "idx_24": packed["idx_24"][None, KB_24 * ks:KB_24 * (ks + nks)]}
+        w[t * R:(t + 1) * R] = unpack(one, pt)
+    return w
+
+
+def boundary_search_tiles(d: np.ndarray, perm: np.ndarray, cout: int, cin: int, tile_rows: int, t_s: float,
+                          step: float = 0.01) -> Tuple[List[float], List[List[Tuple[float, float]]]]:
+    """Key design 1's search run inside each tile on its own: tile t's retained
+    importance R_t(v) decides tile t's v_s (same grid and stop rule as
+    boundary_search, which is this search with one tile)."""
+    d = np.asarray(d, dtype=np.float32)
+    perm = np.asarray(perm)
+    vs, traces = [], []
+    for t in range(cout // tile_rows):
+        rows = slice(t * tile_rows, (t + 1) * tile_rows)
+        v, tr = boundary_search(d[rows], perm[t:t + 1], tile_rows, cin, tile_rows, t_s, step)
+        vs.append(v)
+        traces.append(tr)
+    return vs, traces
+
+
 def scatter_rows(y: np.ndarray, out_rows: np.ndarray) -> np.ndarray:
     """Output-channel permutation undone at write-out: result[out_rows[r]] = y[r].
 

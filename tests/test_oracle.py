@@ -535,3 +535,90 @@ def test_mutation_scatter_as_gather_is_caught(monkeypatch):
         test_scatter_rows_brute_force()
     with pytest.raises(AssertionError):
         test_two_layer_chain_permuted_storage()
+
+
+# --------------------------------------------------------------------------------------
+# Per-tile v_s (FlexHiNM-GP notes, "整体框架": region ratios decided inside each tile)
+# --------------------------------------------------------------------------------------
+
+def test_pack_tiles_equal_v_is_the_uniform_pack():
+    """With one v_s for every tile the per-tile layout is the uniform layout with the tile axis folded."""
+    w = synth.small(256, 512, 64, 0.75, 0.55, 4, 71)
+    p, packed, inter = run_pack(w)
+    plans = oh.plan_tiles(w.cout, w.cin, 64, 0.75, [0.55] * p.n_tiles)
+    pt, it = oh.pack_tiles(bits_of(w.w_bf16), w.importance.numpy(), w.perm.numpy(), plans, with_intermediates=True)
+    nkd, nks = p.n_dense_pad // 32, p.n_24_pad // 64
+    assert np.array_equal(pt["val_dense"], packed["val_dense"].reshape(-1, 64, 32))
+    assert np.array_equal(pt["idx_dense"], packed["idx_dense"].reshape(-1))
+    assert np.array_equal(pt["val_24"], packed["val_24"].reshape(-1, 64, 32))
+    assert np.array_equal(pt["meta_24"], packed["meta_24"].reshape(-1, 64))
+    assert np.array_equal(pt["idx_24"], packed["idx_24"].reshape(-1))
+    assert np.array_equal(pt["tiles"][:, 0], np.arange(p.n_tiles) * nkd)
+    assert np.array_equal(pt["tiles"][:, 2], np.arange(p.n_tiles) * nks)
+    assert np.array_equal(it["mask"], inter["mask"])
+
+
+def test_pack_tiles_invariants_random_v():
+    """Random per-tile v_s: every row keeps cin - z entries, each tile has its closed-form counts, every
+    2:4 group keeps exactly two, and the unpacked weight is W on the mask."""
+    rng = np.random.default_rng(72)
+    cout, cin, R, t_s = 192, 256, 32, 0.7
+    w = synth.small(cout, cin, R, t_s, 0.5, 3, 73)
+    lo = 2 * t_s - 1
+    v = [float(x) for x in rng.uniform(max(0.0, lo), t_s, cout // R)]
+    plans = oh.plan_tiles(cout, cin, R, t_s, v)
+    pk, inter = oh.pack_tiles(bits_of(w.w_bf16), w.importance.numpy(), w.perm.numpy(), plans,
+                              with_intermediates=True)
+    m = inter["mask"]
+    z = math.floor(t_s * cin + 0.5)
+    assert np.all(m.sum(axis=1) == cin - z)
+    assert len({(pl.n_dense, pl.n_24) for pl in plans}) > 1          # the counts really differ
+    for t, pl in enumerate(plans):
+        g = math.floor((t_s - v[t]) * cin / 2 + 0.5)
+        g = max(0, min(g, min(z, cin - z) // 2))
+        assert (pl.n_24, pl.n_pruned, pl.n_dense) == (4 * g, z - 2 * g, cin - z - 2 * g)
+        assert tuple(pk["tiles"][t, [1, 3]]) == (pl.n_dense, pl.n_24)
+        # each 2:4 group of the tile keeps exactly two per row
+        kd, _, ks, n24 = pk["tiles"][t]
+        cols = pk["idx_24"][64 * ks:64 * ks + n24].reshape(-1, 4)
+        rows = m[t * R:(t + 1) * R]
+        for grp in cols:
+            assert np.all(rows[:, grp].sum(axis=1) == 2)
+    wh = oh.unpack_tiles(pk, plans)
+    assert np.array_equal(wh, oh.masked_weight(bits_of(w.w_bf16), m))
+
+
+def test_boundary_search_tiles_single_tile_is_the_search():
+    w = synth.draw("bt1", 64, 256, 64, 0.7, None, 1, 74, n_outliers=12, importance="sq")
+    v1, tr1 = oh.boundary_search(w.importance.numpy(), w.perm.numpy(), 64, 256, 64, 0.7)
+    vt, trt = oh.boundary_search_tiles(w.importance.numpy(), w.perm.numpy(), 64, 256, 64, 0.7)
+    assert vt == [v1] and trt == [tr1]
+
+
+def test_boundary_search_tiles_stop_rule_brute_force():
+    """Each tile's v_s obeys the stop rule on its own retained importance, recomputed here by brute force
+    (every kept element summed one by one)."""
+    w = synth.draw("bt2", 96, 64, 32, 0.6, None, 1, 75, n_outliers=4, importance="sq")
+    d, perm = w.importance.numpy(), w.perm.numpy()
+    vs, traces = oh.boundary_search_tiles(d, perm, 96, 64, 32, 0.6)
+
+    def r_tile(t, v):
+        pl = oh.plan(32, 64, 32, 0.6, v)
+        _, inter = oh.pack(bits_of(w.w_bf16)[32 * t:32 * t + 32], d[32 * t:32 * t + 32], perm[t:t + 1], pl,
+                           with_intermediates=True)
+        m = inter["mask"]
+        sub = d[32 * t:32 * t + 32].astype(np.float64)
+        scores = sub.sum(axis=0)
+        dense = inter["regions"][0] == oh.DENSE
+        return math.fsum(scores[dense]) + math.fsum(sub[m & ~dense[None, :]].tolist())
+
+    for t in range(3):
+        tr = traces[t]
+        for v, r in tr:
+            assert abs(r - r_tile(t, v)) <= 1e-9 * abs(r)
+        # the trace ends at the first strict decrease (or at the end of the grid); the rule returns the
+        # point before that decrease
+        stopped = len(tr) > 1 and tr[-1][1] < tr[-2][1]
+        assert all(tr[k][1] >= tr[k - 1][1] for k in range(1, len(tr) - (1 if stopped else 0)))
+        vb = tr[-2][0] if stopped else tr[-1][0]
+        assert vs[t] == oh.plan(32, 64, 32, 0.6, vb).n_pruned / 64
