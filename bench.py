@@ -324,6 +324,56 @@ def main():
         next_bs["oracle_s_per_grid_point"] = round(time.perf_counter() - t0, 3)
         next_bs["oracle_sample"] = "one grid point (v_s 0.6) of the same search, scores precomputed"
 
+    # NEXT row: per-tile v_s (per-tile boundary search on the same weight and importance, then the
+    # per-tile layout), products timed like the uniform ones but without buffer rotation
+    t0 = time.perf_counter()
+    v_tiles, _ = hinm.boundary_search_tiles(igpu, pgpu, w.tile_rows, w.t_s)
+    search_tiles_ms = (time.perf_counter() - t0) * 1e3
+    t0 = time.perf_counter()
+    pk_tiles = hinm.pack_tiles(wgpu, igpu, w.tile_rows, w.t_s, v_tiles, pgpu)
+    pack_tiles_ms = (time.perf_counter() - t0) * 1e3
+
+    def graph_ms(fn, steps):
+        s_ = torch.cuda.Stream()
+        s_.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s_):
+            fn()
+        torch.cuda.current_stream().wait_stream(s_)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        g.replay()
+        b_.record()
+        torch.cuda.synchronize()
+        return a_.elapsed_time(b_) / steps
+
+    y_t = torch.empty(p.cout, B, dtype=torch.bfloat16, device=dev)
+    yd_t = torch.empty(p.cout, Bd, dtype=torch.bfloat16, device=dev)
+    ws_t = torch.zeros(max(1, hinm.spmm_tiles_workspace_bytes(pk_tiles.plan, Bd)), dtype=torch.uint8, device=dev)
+    kept_t = sum(int(r[1]) + int(r[3]) // 2 for r in pk_tiles.plan.tiles)       # kept entries per row, summed over tiles
+    useful_t = 2 * p.tile_rows * kept_t * B
+    next_tiles = {
+        "what": "per-tile v_s from hinm_boundary_search_tiles on this weight (importance |W|, t_s 0.75), packed by "
+                "hinm_pack_tiles, products by hinm_spmm_tiles; graph-timed like the uniform products but on one "
+                "resident copy (the uniform product on one resident copy is given for comparison)",
+        "v_s_min": round(min(v_tiles), 5), "v_s_max": round(max(v_tiles), 5),
+        "dense_blocks": pk_tiles.plan.dense_blocks, "blocks_24": pk_tiles.plan.blocks_24,
+        "uniform_dense_blocks": p.n_tiles * p.n_dense_pad // 32, "uniform_blocks_24": p.n_tiles * p.n_24_pad // 64,
+        "search_tiles_ms": round(search_tiles_ms, 2), "pack_tiles_ms": round(pack_tiles_ms, 2),
+        "spmm_tiles_batch_2048_ms": round(graph_ms(lambda: hinm.spmm(pk_tiles, x, out=y_t), 20), 5),
+        "spmm_uniform_resident_batch_2048_ms": round(graph_ms(lambda: hinm.spmm(pk, x, out=y_t), 20), 5),
+        "spmm_tiles_batch_16_ms": round(graph_ms(lambda: hinm.spmm(pk_tiles, xd, out=yd_t, workspace=ws_t), 100), 5),
+        "spmm_uniform_resident_batch_16_ms": round(graph_ms(lambda: hinm.spmm(pk, xd, out=yd_t, workspace=ws_t), 100),
+                                                   5),
+        "useful_tflops_batch_2048": None}
+    next_tiles["useful_tflops_batch_2048"] = round(useful_t / (next_tiles["spmm_tiles_batch_2048_ms"] * 1e-3) / 1e12, 2)
+
     dense = None
     if not args.no_dense:
         dense_ms = time_dense(torch, wgpu, x, max(10, args.steps // 2), 3)
@@ -371,6 +421,7 @@ def main():
         "pack_ms": [round(v, 2) for v in pack_ms],
         "next_output_permutation": next_rows,
         "next_boundary_search": next_bs,
+        "next_per_tile_v_s": next_tiles,
         "dense_comparator": dense,
         "cpu_baseline": cpu,
     }

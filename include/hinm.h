@@ -105,6 +105,48 @@ typedef struct {
   int32_t* idx_24;
 } hinm_packed_t;
 
+/* Per-tile region counts (FlexHiNM-GP notes, "整体框架": the ratio of the
+ * three regions is decided inside each output-channel tile).  t_s is shared,
+ * so every row keeps cin - z entries; each tile has its own v_s and so its
+ * own dense / 2:4 / pruned counts.  The K-blocks of the tiles are laid end
+ * to end in the packed buffers, and a tile table locates them.  Plain data,
+ * computed on the host by hinm_plan_tiles. */
+typedef struct {
+  int32_t abi_version;     /* HINM_ABI_VERSION                                        */
+  int32_t cout, cin, tile_rows, n_tiles;
+  int32_t z;               /* zeros per row, as in hinm_plan_t                        */
+  int32_t max_n_dense_pad; /* largest per-tile n_dense rounded up to HINM_KB_DENSE    */
+  int32_t max_n_24_pad;    /* largest per-tile n_24 rounded up to HINM_KB_24          */
+  int32_t dense_blocks;    /* total dense K-blocks (32 columns) over the tiles        */
+  int32_t blocks_24;       /* total 2:4 K-blocks (64 positions) over the tiles        */
+  double t_s;
+  int64_t bytes_val_dense; /* dense_blocks * tile_rows * 32 * 2                       */
+  int64_t bytes_idx_dense; /* dense_blocks * 32 * 4                                   */
+  int64_t bytes_val_24;    /* blocks_24 * tile_rows * 32 * 2                          */
+  int64_t bytes_meta_24;   /* blocks_24 * tile_rows * 8                               */
+  int64_t bytes_idx_24;    /* blocks_24 * 64 * 4                                      */
+  int64_t bytes_tiles;     /* n_tiles * 4 * 4                                         */
+} hinm_tplan_t;
+
+/* A packed weight with per-tile counts.  Buffers as in hinm_packed_t with
+ * the tile axis folded into the block axis: tile t's dense blocks are
+ * blocks tiles[t][0] .. tiles[t][0] + ceil(tiles[t][1] / 32) - 1 of
+ * val_dense [dense_blocks][tile_rows][32] and of idx_dense
+ * [dense_blocks * 32]; its 2:4 blocks start at block tiles[t][2] of val_24
+ * [blocks_24][tile_rows][32], meta_24 [blocks_24][tile_rows] and idx_24
+ * [blocks_24 * 64].  `tiles` (device, caller-owned, filled by the caller
+ * from the table hinm_plan_tiles returns) is int32 [n_tiles][4]: first
+ * dense block, n_dense, first 2:4 block, n_24. */
+typedef struct {
+  hinm_tplan_t plan;
+  const int32_t* tiles;
+  void* val_dense;
+  int32_t* idx_dense;
+  void* val_24;
+  uint64_t* meta_24;
+  int32_t* idx_24;
+} hinm_tpacked_t;
+
 /* Library ABI version (HINM_ABI_VERSION of the build). */
 int hinm_abi_version(void);
 
@@ -233,6 +275,45 @@ int hinm_boundary_search(int64_t cout, int64_t cin, int32_t tile_rows, double t_
                          const float* importance, int64_t ldi, const int32_t* perm, void* workspace,
                          size_t workspace_bytes, double* v_s_out, double* trace_v, double* trace_r,
                          int32_t trace_cap, int32_t* trace_len, void* stream);
+
+/* Per-tile plan (host only).  v_s (host) [n_tiles]: tile t's v_s, each in
+ * [max(0, 2 t_s - 1), t_s]; tile t's counts are those of hinm_plan at
+ * (t_s, v_s[t]).  out (host) receives the shared fields and the buffer
+ * sizes; tiles_out (host) int32 [n_tiles][4] the tile table (copy it to the
+ * device for hinm_pack_tiles / hinm_spmm_tiles).  Errors as hinm_plan. */
+int hinm_plan_tiles(int64_t cout, int64_t cin, int32_t tile_rows, double t_s, const double* v_s, hinm_tplan_t* out,
+                    int32_t* tiles_out);
+
+/* Device scratch for hinm_pack_tiles, in bytes (host only). */
+int hinm_pack_tiles_workspace_bytes(const hinm_tplan_t* plan, size_t* bytes);
+
+/* hinm_pack with per-tile counts: the same five steps, tile t cut at its
+ * own n_dense / n_24 (read from out->tiles).  Same inputs, guarantees and
+ * errors as hinm_pack; out holds the plan copy, the device tile table and
+ * the output buffers sized by the plan. */
+int hinm_pack_tiles(const hinm_tplan_t* plan, const void* w_bf16, int64_t ldw, const float* importance, int64_t ldi,
+                    const int32_t* perm, hinm_tpacked_t* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device scratch that hinm_spmm_tiles needs for a batch, in bytes (host only). */
+int hinm_spmm_tiles_workspace_bytes(const hinm_tplan_t* plan, int64_t batch, size_t* bytes);
+
+/* Y = (W (.) M) X for a packed weight with per-tile counts; as hinm_spmm.
+ * Each tile runs its own number of K-blocks.  Requires tile_rows % 64 == 0
+ * and buffers below 2^31 bytes (HINM_ESHAPE otherwise). */
+int hinm_spmm_tiles(const hinm_tpacked_t* packed, const void* x_bf16, int64_t batch, int64_t ldx, void* y_bf16,
+                    int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The boundary search run inside each tile on its own (FlexHiNM-GP notes,
+ * "整体框架": the region ratio is decided per tile; key design 1: the
+ * search).  Tile t follows hinm_boundary_search's grid and stop rule on its
+ * own retained importance R_t(v) = R_dense(t) + R_24(t); the grid goes on
+ * while any tile has not stopped.  Outputs (host): v_s_tiles [n_tiles]
+ * (n_pruned / cin of each tile's plan), points_tiles [n_tiles] (grid points
+ * each tile visited; may be NULL).  Other arguments, workspace and errors as
+ * hinm_boundary_search. */
+int hinm_boundary_search_tiles(int64_t cout, int64_t cin, int32_t tile_rows, double t_s, double step,
+                               const float* importance, int64_t ldi, const int32_t* perm, void* workspace,
+                               size_t workspace_bytes, double* v_s_tiles, int32_t* points_tiles, void* stream);
 
 /* Static description of a status code. */
 const char* hinm_status_str(int status);

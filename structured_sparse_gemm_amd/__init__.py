@@ -27,7 +27,9 @@ STATUS = {0: "HINM_OK", 1: "HINM_EINVAL", 2: "HINM_ESHAPE", 3: "HINM_EPERM", 4: 
 # Every symbol the C ABI exports (include/hinm.h).
 EXPORTS = ("hinm_abi_version", "hinm_plan", "hinm_pack_workspace_bytes", "hinm_pack",
            "hinm_spmm_workspace_bytes", "hinm_spmm", "hinm_spmm_rows", "hinm_translate_indices",
-           "hinm_boundary_workspace_bytes", "hinm_boundary_search", "hinm_status_str", "hinm_last_error")
+           "hinm_boundary_workspace_bytes", "hinm_boundary_search", "hinm_plan_tiles",
+           "hinm_pack_tiles_workspace_bytes", "hinm_pack_tiles", "hinm_spmm_tiles_workspace_bytes",
+           "hinm_spmm_tiles", "hinm_boundary_search_tiles", "hinm_status_str", "hinm_last_error")
 
 
 class HinmError(RuntimeError):
@@ -54,6 +56,22 @@ class PackedT(ctypes.Structure):
                 ("val_24", ctypes.c_void_p), ("meta_24", ctypes.c_void_p), ("idx_24", ctypes.c_void_p)]
 
 
+class TPlanT(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32), ("cout", ctypes.c_int32), ("cin", ctypes.c_int32),
+                ("tile_rows", ctypes.c_int32), ("n_tiles", ctypes.c_int32), ("z", ctypes.c_int32),
+                ("max_n_dense_pad", ctypes.c_int32), ("max_n_24_pad", ctypes.c_int32),
+                ("dense_blocks", ctypes.c_int32), ("blocks_24", ctypes.c_int32), ("t_s", ctypes.c_double),
+                ("bytes_val_dense", ctypes.c_int64), ("bytes_idx_dense", ctypes.c_int64),
+                ("bytes_val_24", ctypes.c_int64), ("bytes_meta_24", ctypes.c_int64),
+                ("bytes_idx_24", ctypes.c_int64), ("bytes_tiles", ctypes.c_int64)]
+
+
+class TPackedT(ctypes.Structure):
+    _fields_ = [("plan", TPlanT), ("tiles", ctypes.c_void_p), ("val_dense", ctypes.c_void_p),
+                ("idx_dense", ctypes.c_void_p), ("val_24", ctypes.c_void_p), ("meta_24", ctypes.c_void_p),
+                ("idx_24", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -77,6 +95,15 @@ def library() -> ctypes.CDLL:
             "hinm_spmm_rows": ([ctypes.POINTER(PackedT), VP, I64, I64, VP, I64, VP, VP, S, VP], ctypes.c_int),
             "hinm_translate_indices": ([ctypes.POINTER(PackedT), VP, VP, S, VP], ctypes.c_int),
             "hinm_boundary_workspace_bytes": ([I64, I64, I32, ctypes.POINTER(S)], ctypes.c_int),
+            "hinm_plan_tiles": ([I64, I64, I32, D, ctypes.POINTER(D), ctypes.POINTER(TPlanT), ctypes.POINTER(I32)],
+                                ctypes.c_int),
+            "hinm_pack_tiles_workspace_bytes": ([ctypes.POINTER(TPlanT), ctypes.POINTER(S)], ctypes.c_int),
+            "hinm_pack_tiles": ([ctypes.POINTER(TPlanT), VP, I64, VP, I64, VP, ctypes.POINTER(TPackedT), VP, S, VP],
+                                ctypes.c_int),
+            "hinm_spmm_tiles_workspace_bytes": ([ctypes.POINTER(TPlanT), I64, ctypes.POINTER(S)], ctypes.c_int),
+            "hinm_spmm_tiles": ([ctypes.POINTER(TPackedT), VP, I64, I64, VP, I64, VP, S, VP], ctypes.c_int),
+            "hinm_boundary_search_tiles": ([I64, I64, I32, D, D, VP, I64, VP, VP, S, ctypes.POINTER(D),
+                                            ctypes.POINTER(I32), VP], ctypes.c_int),
             "hinm_boundary_search": ([I64, I64, I32, D, D, VP, I64, VP, VP, S, ctypes.POINTER(D),
                                       ctypes.POINTER(D), ctypes.POINTER(D), I32, ctypes.POINTER(I32), VP],
                                      ctypes.c_int),
@@ -225,6 +252,109 @@ def pack(w: torch.Tensor, importance: torch.Tensor, tile_rows: int, t_s: float, 
     return out
 
 
+@dataclasses.dataclass
+class TilePlan:
+    """Per-tile region counts (hinm_plan_tiles): shared fields, buffer sizes and the tile table."""
+
+    raw: TPlanT = dataclasses.field(repr=False)
+    tiles: "np.ndarray"          # int32 [n_tiles, 4]: first dense block, n_dense, first 2:4 block, n_24
+    v_s: tuple
+
+    def __getattr__(self, name):
+        raw = self.__dict__.get("raw")
+        if raw is not None and name in dict(TPlanT._fields_):
+            return getattr(raw, name)
+        raise AttributeError(name)
+
+    @property
+    def packed_bytes(self) -> int:
+        r = self.raw
+        return r.bytes_val_dense + r.bytes_idx_dense + r.bytes_val_24 + r.bytes_meta_24 + r.bytes_idx_24
+
+
+def plan_tiles(cout: int, cin: int, tile_rows: int, t_s: float, v_s) -> TilePlan:
+    """Per-tile plan (host only): tile t uses v_s[t]."""
+    import numpy as np
+    v = [float(x) for x in v_s]
+    raw = TPlanT()
+    n_tiles = cout // tile_rows if tile_rows > 0 else 0
+    if len(v) != n_tiles:
+        raise ValueError(f"{n_tiles} per-tile v_s values are needed, got {len(v)}")
+    arr = (ctypes.c_double * max(1, len(v)))(*v)
+    tiles = (ctypes.c_int32 * max(1, 4 * n_tiles))()
+    _check(library().hinm_plan_tiles(cout, cin, tile_rows, float(t_s), arr, ctypes.byref(raw), tiles))
+    return TilePlan(raw=raw, tiles=np.ctypeslib.as_array(tiles)[:4 * n_tiles].reshape(n_tiles, 4).copy(),
+                    v_s=tuple(v))
+
+
+@dataclasses.dataclass
+class HinmTPacked:
+    """A packed weight with per-tile counts: the plan, the device tile table and five device buffers."""
+
+    plan: TilePlan
+    tiles: torch.Tensor       # int32 [T, 4] on the device
+    val_dense: torch.Tensor   # int16 bits of bf16 [dense_blocks, R, 32]
+    idx_dense: torch.Tensor   # int32 [dense_blocks * 32]
+    val_24: torch.Tensor      # int16 bits of bf16 [blocks_24, R, 32]
+    meta_24: torch.Tensor     # int64 bits of uint64 [blocks_24, R]
+    idx_24: torch.Tensor      # int32 [blocks_24 * 64]
+
+    def struct(self) -> TPackedT:
+        st = self.__dict__.get("_struct")
+        if st is None:
+            def ptr(t):
+                return t.data_ptr() if t.numel() else None
+            st = TPackedT(self.plan.raw, ptr(self.tiles), ptr(self.val_dense), ptr(self.idx_dense),
+                          ptr(self.val_24), ptr(self.meta_24), ptr(self.idx_24))
+            self.__dict__["_struct"] = st
+            self.__dict__["_ws_need"] = {}
+        return st
+
+    @property
+    def device(self) -> torch.device:
+        return self.tiles.device
+
+    def nbytes(self) -> int:
+        return self.plan.packed_bytes
+
+
+def pack_tiles(w: torch.Tensor, importance: torch.Tensor, tile_rows: int, t_s: float, v_s,
+               perm: Optional[torch.Tensor] = None) -> HinmTPacked:
+    """Packs a bf16 weight with one v_s per tile (hinm_pack_tiles, synchronous)."""
+    if w.dtype != torch.bfloat16 or w.dim() != 2 or not w.is_cuda:
+        raise ValueError("w must be a 2-D bf16 CUDA tensor")
+    if importance.dtype != torch.float32 or importance.shape != w.shape or importance.device != w.device:
+        raise ValueError("importance must be fp32 with the shape and device of w")
+    if w.stride(1) != 1 or importance.stride(1) != 1:
+        raise ValueError("w and importance must have unit column stride")
+    cout, cin = w.shape
+    p = plan_tiles(cout, cin, tile_rows, t_s, v_s)
+    if perm is not None:
+        if perm.dtype != torch.int32 or perm.shape != (p.n_tiles, cin) or perm.device != w.device:
+            raise ValueError(f"perm must be int32 [{p.n_tiles}, {cin}] on the device of w")
+        perm = perm.contiguous()
+    dev, R = w.device, tile_rows
+    out = HinmTPacked(p, torch.from_numpy(p.tiles).to(dev),
+                      _empty((p.dense_blocks, R, 32), torch.int16, dev), _empty((p.dense_blocks * 32,), torch.int32, dev),
+                      _empty((p.blocks_24, R, 32), torch.int16, dev), _empty((p.blocks_24, R), torch.int64, dev),
+                      _empty((p.blocks_24 * 64,), torch.int32, dev))
+    n = ctypes.c_size_t()
+    _check(library().hinm_pack_tiles_workspace_bytes(ctypes.byref(p.raw), ctypes.byref(n)))
+    ws = torch.empty(n.value, dtype=torch.uint8, device=dev)
+    st = out.struct()
+    with torch.cuda.device(dev):
+        _check(library().hinm_pack_tiles(ctypes.byref(p.raw), w.data_ptr(), w.stride(0), importance.data_ptr(),
+                                         importance.stride(0), perm.data_ptr() if perm is not None else None,
+                                         ctypes.byref(st), ws.data_ptr(), ws.numel(), _stream_ptr(dev)))
+    return out
+
+
+def spmm_tiles_workspace_bytes(p: TilePlan, batch: int) -> int:
+    n = ctypes.c_size_t()
+    _check(library().hinm_spmm_tiles_workspace_bytes(ctypes.byref(p.raw), batch, ctypes.byref(n)))
+    return n.value
+
+
 def spmm_workspace_bytes(p: Plan, batch: int) -> int:
     n = ctypes.c_size_t()
     _check(library().hinm_spmm_workspace_bytes(ctypes.byref(p.raw), batch, ctypes.byref(n)))
@@ -260,6 +390,9 @@ def spmm(packed: HinmPacked, x: torch.Tensor, out: Optional[torch.Tensor] = None
     """
     p = packed.plan
     dev = x.device
+    tiled = isinstance(packed, HinmTPacked)
+    if tiled and out_rows is not None:
+        raise ValueError("out_rows is not supported with per-tile counts")
     if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[0] != p.cin or dev != packed.idx_24.device:
         raise ValueError(f"x must be bf16 [{p.cin}, batch] on {packed.device}")
     if x.stride(1) != 1:
@@ -276,7 +409,8 @@ def spmm(packed: HinmPacked, x: torch.Tensor, out: Optional[torch.Tensor] = None
     need_cache = packed.__dict__["_ws_need"]
     need = need_cache.get(batch)
     if need is None:
-        need = need_cache[batch] = spmm_workspace_bytes(p, batch)
+        need = need_cache[batch] = (spmm_tiles_workspace_bytes(p, batch) if tiled else
+                                    spmm_workspace_bytes(p, batch))
     if workspace is None:
         workspace = _workspace(dev, need)
     lib = library()
@@ -284,7 +418,10 @@ def spmm(packed: HinmPacked, x: torch.Tensor, out: Optional[torch.Tensor] = None
     ws_n = workspace.numel() if workspace is not None else 0
     ldx = max(x.stride(0), batch) if batch else 0
     ldy = max(out.stride(0), batch) if batch else 0
-    if out_rows is None:
+    if tiled:
+        call, args = lib.hinm_spmm_tiles, (ctypes.byref(st), x.data_ptr(), batch, ldx, out.data_ptr(), ldy, ws_ptr,
+                                           ws_n, _stream_ptr(dev))
+    elif out_rows is None:
         call, args = lib.hinm_spmm, (ctypes.byref(st), x.data_ptr(), batch, ldx, out.data_ptr(), ldy, ws_ptr, ws_n,
                                      _stream_ptr(dev))
     else:
@@ -339,6 +476,30 @@ def boundary_search(importance: torch.Tensor, perm: Optional[torch.Tensor], tile
     return v.value, [(tv[i], tr[i]) for i in range(k)]
 
 
-__all__ = ["HinmError", "HinmPacked", "Plan", "plan", "pack", "spmm", "translate_indices", "boundary_search", "alloc_packed",
+def boundary_search_tiles(importance: torch.Tensor, perm: Optional[torch.Tensor], tile_rows: int, t_s: float,
+                          step: float = 0.01):
+    """Per-tile device boundary search (hinm_boundary_search_tiles).  Returns (v_s per tile, grid points per tile)."""
+    if importance.dtype != torch.float32 or importance.dim() != 2 or importance.stride(1) != 1:
+        raise ValueError("importance must be float32 [cout, cin] with unit column stride")
+    cout, cin = importance.shape
+    dev = importance.device
+    if perm is not None and (perm.dtype != torch.int32 or not perm.is_contiguous() or perm.device != dev):
+        raise ValueError("perm must be a contiguous int32 tensor on the importance's device")
+    lib = library()
+    n = ctypes.c_size_t()
+    _check(lib.hinm_boundary_workspace_bytes(cout, cin, tile_rows, ctypes.byref(n)))
+    ws = torch.empty(n.value, dtype=torch.uint8, device=dev)
+    T = cout // tile_rows
+    v = (ctypes.c_double * max(1, T))()
+    pts = (ctypes.c_int32 * max(1, T))()
+    with torch.cuda.device(dev):
+        _check(lib.hinm_boundary_search_tiles(cout, cin, tile_rows, float(t_s), float(step), importance.data_ptr(),
+                                              importance.stride(0), perm.data_ptr() if perm is not None else None,
+                                              ws.data_ptr(), ws.numel(), v, pts, _stream_ptr(dev)))
+    return [v[i] for i in range(T)], [pts[i] for i in range(T)]
+
+
+__all__ = ["HinmError", "HinmPacked", "Plan", "plan", "pack", "spmm", "translate_indices", "boundary_search", "plan_tiles", "pack_tiles", "boundary_search_tiles",
+           "HinmTPacked", "TilePlan", "spmm_tiles_workspace_bytes", "alloc_packed",
            "pack_workspace_bytes",
            "spmm_workspace_bytes", "library", "LIB_PATH", "EXPORTS"]

@@ -16,6 +16,12 @@ void clear_error();
 
 // Host-side validation of a plan handed back by a caller.
 int check_plan(const hinm_plan_t* p);
+// The same for a per-tile plan (its shared fields and buffer sizes; the
+// tile table itself lives on the device).
+int check_tplan(const hinm_tplan_t* p);
+// A hinm_plan_t carrying a per-tile plan's shape (largest per-tile pads), for
+// the launch-shape logic shared with the uniform layout.
+hinm_plan_t shape_plan(const hinm_tplan_t& p);
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 

@@ -18,6 +18,18 @@ using hinm::fail;
 namespace {
 
 constexpr uint8_t kPruned = 0, kTwoFour = 1, kDense = 2;
+
+// Where tile t's K-blocks and counts are: from the per-tile table
+// (first dense block, n_dense, first 2:4 block, n_24) when there is one,
+// else the uniform layout (every tile the same counts, tiles end to end).
+struct TileDesc {
+  int kd0, n_dense, ks0, n_24;
+};
+__device__ inline TileDesc tile_desc(const int32_t* tiles, int t, int n_dense, int n_dense_pad, int n_24,
+                                     int n_24_pad) {
+  if (tiles) return {tiles[4 * t], tiles[4 * t + 1], tiles[4 * t + 2], tiles[4 * t + 3]};
+  return {t * (n_dense_pad / 32), n_dense, t * (n_24_pad / 64), n_24};
+}
 constexpr int kFlagPerm = 1, kFlagImportance = 2;
 
 __global__ void zero_flag_kernel(int* flag) {
@@ -71,9 +83,14 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ i
 // rank is counted directly, comparing against every column of the tile; the
 // loop index is uniform across the wave, so each score is read once per wave.
 __global__ __launch_bounds__(256) void regions_kernel(const double* __restrict__ s, int cin, int n_dense,
-                                                      int n_24, uint8_t* __restrict__ reg) {
+                                                      int n_24, uint8_t* __restrict__ reg,
+                                                      const int32_t* __restrict__ tiles) {
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   const int t = blockIdx.y;
+  if (tiles) {
+    n_dense = tiles[4 * t + 1];
+    n_24 = tiles[4 * t + 3];
+  }
   const double* st = s + (int64_t)t * cin;
   const double sc = c < cin ? st[c] : 0.0;
   int rank = 0;
@@ -89,13 +106,20 @@ __global__ __launch_bounds__(256) void regions_kernel(const double* __restrict__
 // workgroup of 1024 threads per tile, chunks of 1024 positions.
 __global__ __launch_bounds__(1024) void compact_kernel(const int32_t* __restrict__ perm, const uint8_t* __restrict__ reg,
                                                        int cin, int n_dense_pad, int n_24_pad,
-                                                       int32_t* __restrict__ idx_d, int32_t* __restrict__ idx_s) {
+                                                       int32_t* __restrict__ idx_d, int32_t* __restrict__ idx_s,
+                                                       const int32_t* __restrict__ tiles) {
   __shared__ int wd[16], ws[16];
   const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
   int32_t* od = idx_d + (int64_t)t * n_dense_pad;
   int32_t* os = idx_s + (int64_t)t * n_24_pad;
+  if (tiles) {   // this tile's lists and pads
+    od = idx_d + (int64_t)tiles[4 * t] * 32;
+    os = idx_s + (int64_t)tiles[4 * t + 2] * 64;
+    n_dense_pad = (tiles[4 * t + 1] + 31) / 32 * 32;
+    n_24_pad = (tiles[4 * t + 3] + 63) / 64 * 64;
+  }
   int base_d = 0, base_s = 0;
   for (int j0 = 0; j0 < cin; j0 += 1024) {
     const int j = j0 + threadIdx.x;
@@ -139,16 +163,23 @@ __global__ __launch_bounds__(256) void encode24_kernel(const uint16_t* __restric
                                                        const float* __restrict__ imp, int64_t ldi,
                                                        const int32_t* __restrict__ idx_s, int cin, int rows,
                                                        int n_tiles, int groups, int n_24_pad,
-                                                       uint16_t* __restrict__ val_s, uint64_t* __restrict__ meta) {
-  const int nkb = n_24_pad / 64;
+                                                       uint16_t* __restrict__ val_s, uint64_t* __restrict__ meta,
+                                                       const int32_t* __restrict__ tiles) {
+  const int nkb = n_24_pad / 64;   // blocks per tile (the largest, with a tile table)
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (int64_t)n_tiles * nkb * rows) return;
   const int r = (int)(gid % rows);
   const int64_t tk = gid / rows;
   const int kb = (int)(tk % nkb);
   const int t = (int)(tk / nkb);
+  const TileDesc td = tile_desc(tiles, t, 0, 0, groups * 4, n_24_pad);
+  if (tiles) {
+    if (kb >= (td.n_24 + 63) / 64) return;
+    groups = td.n_24 / 4;
+  }
+  const int blk = td.ks0 + kb;     // this block's index in the 2:4 buffers
   const int64_t grow = (int64_t)t * rows + r;
-  const int32_t* il = idx_s + (int64_t)t * n_24_pad + kb * 64;
+  const int32_t* il = idx_s + (int64_t)blk * 64;
   uint64_t m = 0;
   uint32_t packed[16];
   for (int g = 0; g < 16; ++g) {
@@ -175,24 +206,28 @@ __global__ __launch_bounds__(256) void encode24_kernel(const uint16_t* __restric
     m |= (uint64_t)nib << (4 * g);
     packed[g] = v0 | (v1 << 16);
   }
-  uint4* dst = reinterpret_cast<uint4*>(val_s + ((int64_t)(t * nkb + kb) * rows + r) * 32);
+  uint4* dst = reinterpret_cast<uint4*>(val_s + ((int64_t)blk * rows + r) * 32);
   for (int i = 0; i < 4; ++i) dst[i] = make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
-  meta[(int64_t)(t * nkb + kb) * rows + r] = m;
+  meta[(int64_t)blk * rows + r] = m;
 }
 
 // Dense-region gather: val_d[t][kb][r][k] = W[t*R + r][idx_d[t][32 kb + k]].
 __global__ __launch_bounds__(256) void gather_dense_kernel(const uint16_t* __restrict__ w, int64_t ldw,
                                                            const int32_t* __restrict__ idx_d, int cin, int rows,
-                                                           int n_tiles, int n_dense_pad, uint16_t* __restrict__ val_d) {
-  const int nkb = n_dense_pad / 32;
+                                                           int n_tiles, int n_dense_pad, uint16_t* __restrict__ val_d,
+                                                           const int32_t* __restrict__ tiles) {
+  const int nkb = n_dense_pad / 32;   // blocks per tile (the largest, with a tile table)
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (int64_t)n_tiles * nkb * rows) return;
   const int r = (int)(gid % rows);
   const int64_t tk = gid / rows;
   const int kb = (int)(tk % nkb);
   const int t = (int)(tk / nkb);
+  const TileDesc td = tile_desc(tiles, t, 0, n_dense_pad, 0, 0);
+  if (tiles && kb >= (td.n_dense + 31) / 32) return;
+  const int blk = td.kd0 + kb;     // this block's index in the dense buffers
   const int64_t grow = (int64_t)t * rows + r;
-  const int32_t* il = idx_d + (int64_t)t * n_dense_pad + kb * 32;
+  const int32_t* il = idx_d + (int64_t)blk * 32;
   uint32_t packed[16];
   for (int k = 0; k < 32; k += 2) {
     const int c0 = il[k], c1 = il[k + 1];
@@ -200,7 +235,7 @@ __global__ __launch_bounds__(256) void gather_dense_kernel(const uint16_t* __res
     const uint32_t v1 = (c1 >= 0 && c1 < cin) ? w[grow * ldw + c1] : 0u;
     packed[k / 2] = v0 | (v1 << 16);
   }
-  uint4* dst = reinterpret_cast<uint4*>(val_d + ((int64_t)(t * nkb + kb) * rows + r) * 32);
+  uint4* dst = reinterpret_cast<uint4*>(val_d + ((int64_t)blk * rows + r) * 32);
   for (int i = 0; i < 4; ++i) dst[i] = make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
 }
 
@@ -299,38 +334,40 @@ __global__ __launch_bounds__(256) void r24_kernel(const float* __restrict__ imp,
 
 }  // namespace
 
-extern "C" int hinm_pack(const hinm_plan_t* plan, const void* w_bf16, int64_t ldw, const float* importance,
-                         int64_t ldi, const int32_t* perm, hinm_packed_t* out, void* workspace,
-                         size_t workspace_bytes, void* stream_) {
-  hinm::clear_error();
-  int st = hinm::check_plan(plan);
-  if (st) return st;
-  const hinm_plan_t& p = *plan;
-  if (!w_bf16 || !importance || !out) return fail(HINM_EINVAL, "w, importance and out must be non-NULL");
+// Shape of a pack: the uniform counts, or (with a tile table on the device)
+// the largest per-tile pads, which size the launch grids.
+struct PackShape {
+  int T, cin, R;
+  int n_dense, n_24, n_dense_pad, n_24_pad, groups;
+  int64_t bytes_val_dense, bytes_idx_dense, bytes_val_24, bytes_meta_24, bytes_idx_24;
+};
+
+static int pack_core(const PackShape& p, const int32_t* tiles, const void* w_bf16, int64_t ldw,
+                     const float* importance, int64_t ldi, const int32_t* perm, void* val_dense, int32_t* idx_dense,
+                     void* val_24, uint64_t* meta_24, int32_t* idx_24, void* workspace, size_t workspace_bytes,
+                     size_t need, void* stream_) {
+  if (!w_bf16 || !importance) return fail(HINM_EINVAL, "w and importance must be non-NULL");
   if (ldw < p.cin || ldi < p.cin)
     return fail(HINM_ESHAPE, "ldw=%lld and ldi=%lld must be >= cin=%d", (long long)ldw, (long long)ldi, p.cin);
   if (p.cin > (1 << 20)) return fail(HINM_ESHAPE, "cin=%d exceeds the 2^20 supported by the permutation check", p.cin);
   if (!hinm::aligned(w_bf16, 2) || !hinm::aligned(importance, 4) || (perm && !hinm::aligned(perm, 4)))
     return fail(HINM_EALIGN, "w must be 2-byte, importance and perm 4-byte aligned");
   struct Buf { const void* ptr; int64_t bytes; const char* name; } bufs[5] = {
-      {out->val_dense, p.bytes_val_dense, "val_dense"}, {out->idx_dense, p.bytes_idx_dense, "idx_dense"},
-      {out->val_24, p.bytes_val_24, "val_24"}, {out->meta_24, p.bytes_meta_24, "meta_24"},
-      {out->idx_24, p.bytes_idx_24, "idx_24"}};
+      {val_dense, p.bytes_val_dense, "val_dense"}, {idx_dense, p.bytes_idx_dense, "idx_dense"},
+      {val_24, p.bytes_val_24, "val_24"}, {meta_24, p.bytes_meta_24, "meta_24"},
+      {idx_24, p.bytes_idx_24, "idx_24"}};
   for (const Buf& b : bufs) {
     if (b.bytes > 0 && !b.ptr) return fail(HINM_EINVAL, "%s is NULL but needs %lld bytes", b.name, (long long)b.bytes);
     if (b.ptr && !hinm::aligned(b.ptr, 16)) return fail(HINM_EALIGN, "%s is not 16-byte aligned", b.name);
   }
-  size_t need = 0;
-  hinm_pack_workspace_bytes(plan, &need);
   if (!workspace || workspace_bytes < need)
     return fail(HINM_EWORKSPACE, "pack workspace of %zu bytes given, %zu needed", workspace_bytes, need);
   if (!hinm::aligned(workspace, 256)) return fail(HINM_EALIGN, "workspace is not 256-byte aligned");
-  st = hinm::ensure_device();
+  int st = hinm::ensure_device();
   if (st) return st;
 
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
-  out->plan = p;
-  const int T = p.n_tiles, cin = p.cin, R = p.tile_rows;
+  const int T = p.T, cin = p.cin, R = p.R;
   char* ws = static_cast<char*>(workspace);
   int* flag = reinterpret_cast<int*>(ws);
   double* scores = reinterpret_cast<double*>(ws + 256);
@@ -354,25 +391,60 @@ extern "C" int hinm_pack(const hinm_plan_t* plan, const void* w_bf16, int64_t ld
 
   // Stage 2: regions, index lists, values and metadata.
   hipLaunchKernelGGL(regions_kernel, dim3((cin + 255) / 256, T), dim3(256), 0, stream, scores, cin, p.n_dense,
-                     p.n_24, reg);
+                     p.n_24, reg, tiles);
   hipLaunchKernelGGL(compact_kernel, dim3(T), dim3(1024), 0, stream, perm, reg, cin, p.n_dense_pad, p.n_24_pad,
-                     out->idx_dense, out->idx_24);
+                     idx_dense, idx_24, tiles);
   if (p.n_24_pad > 0) {
     const int64_t n = (int64_t)T * (p.n_24_pad / 64) * R;
     hipLaunchKernelGGL(encode24_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, w, ldw, importance,
-                       ldi, out->idx_24, cin, R, T, p.groups, p.n_24_pad, static_cast<uint16_t*>(out->val_24),
-                       out->meta_24);
+                       ldi, idx_24, cin, R, T, p.groups, p.n_24_pad, static_cast<uint16_t*>(val_24), meta_24, tiles);
   }
   if (p.n_dense_pad > 0) {
     const int64_t n = (int64_t)T * (p.n_dense_pad / 32) * R;
     hipLaunchKernelGGL(gather_dense_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, w, ldw,
-                       out->idx_dense, cin, R, T, p.n_dense_pad, static_cast<uint16_t*>(out->val_dense));
+                       idx_dense, cin, R, T, p.n_dense_pad, static_cast<uint16_t*>(val_dense), tiles);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "pack stage-2 launch");
   e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_fail(e, "pack stage-2");
   return HINM_OK;
+}
+
+extern "C" int hinm_pack(const hinm_plan_t* plan, const void* w_bf16, int64_t ldw, const float* importance,
+                         int64_t ldi, const int32_t* perm, hinm_packed_t* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  hinm::clear_error();
+  int st = hinm::check_plan(plan);
+  if (st) return st;
+  if (!out) return fail(HINM_EINVAL, "out must be non-NULL");
+  const hinm_plan_t& p = *plan;
+  const PackShape ps = {p.n_tiles, p.cin, p.tile_rows, p.n_dense, p.n_24, p.n_dense_pad, p.n_24_pad, p.groups,
+                        p.bytes_val_dense, p.bytes_idx_dense, p.bytes_val_24, p.bytes_meta_24, p.bytes_idx_24};
+  size_t need = 0;
+  hinm_pack_workspace_bytes(plan, &need);
+  out->plan = p;
+  return pack_core(ps, nullptr, w_bf16, ldw, importance, ldi, perm, out->val_dense, out->idx_dense, out->val_24,
+                   out->meta_24, out->idx_24, workspace, workspace_bytes, need, stream);
+}
+
+extern "C" int hinm_pack_tiles(const hinm_tplan_t* plan, const void* w_bf16, int64_t ldw, const float* importance,
+                               int64_t ldi, const int32_t* perm, hinm_tpacked_t* out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  hinm::clear_error();
+  int st = hinm::check_tplan(plan);
+  if (st) return st;
+  if (!out) return fail(HINM_EINVAL, "out must be non-NULL");
+  if (!out->tiles) return fail(HINM_EINVAL, "out->tiles (the device tile table) is NULL");
+  if (!hinm::aligned(out->tiles, 4)) return fail(HINM_EALIGN, "out->tiles is not 4-byte aligned");
+  const hinm_tplan_t& p = *plan;
+  const PackShape ps = {p.n_tiles, p.cin, p.tile_rows, 0, 0, p.max_n_dense_pad, p.max_n_24_pad, 0,
+                        p.bytes_val_dense, p.bytes_idx_dense, p.bytes_val_24, p.bytes_meta_24, p.bytes_idx_24};
+  size_t need = 0;
+  hinm_pack_tiles_workspace_bytes(plan, &need);
+  out->plan = p;
+  return pack_core(ps, out->tiles, w_bf16, ldw, importance, ldi, perm, out->val_dense, out->idx_dense, out->val_24,
+                   out->meta_24, out->idx_24, workspace, workspace_bytes, need, stream);
 }
 
 extern "C" int hinm_translate_indices(hinm_packed_t* packed, const int32_t* map, void* workspace,
@@ -430,12 +502,15 @@ extern "C" int hinm_boundary_workspace_bytes(int64_t cout, int64_t cin, int32_t 
   return HINM_OK;
 }
 
-extern "C" int hinm_boundary_search(int64_t cout, int64_t cin, int32_t tile_rows, double t_s, double step,
-                                    const float* importance, int64_t ldi, const int32_t* perm, void* workspace,
-                                    size_t workspace_bytes, double* v_s_out, double* trace_v, double* trace_r,
-                                    int32_t trace_cap, int32_t* trace_len, void* stream_) {
-  hinm::clear_error();
-  if (!importance || !v_s_out) return fail(HINM_EINVAL, "importance and v_s_out must be non-NULL");
+// Shared by the global and the per-tile search.  Global: one v_s, R_total
+// summed over all tiles.  Per tile (v_tiles != NULL): tile t follows the same
+// rule on its own R_t(v) = R_dense(t) + sum over its rows of R_24, and the
+// grid goes on while any tile is still rising.
+static int boundary_core(int64_t cout, int64_t cin, int32_t tile_rows, double t_s, double step,
+                         const float* importance, int64_t ldi, const int32_t* perm, void* workspace,
+                         size_t workspace_bytes, double* v_s_out, double* trace_v, double* trace_r, int32_t trace_cap,
+                         int32_t* trace_len, double* v_tiles, int32_t* points_tiles, void* stream_) {
+  if (!importance) return fail(HINM_EINVAL, "importance must be non-NULL");
   if (!(step > 0.0) || !std::isfinite(step)) return fail(HINM_EINVAL, "step=%g must be a positive finite number", step);
   if (trace_cap < 0 || (trace_cap > 0 && (!trace_v || !trace_r))) return fail(HINM_EINVAL, "bad trace arguments");
   hinm_plan_t p0;
@@ -481,12 +556,13 @@ extern "C" int hinm_boundary_search(int64_t cout, int64_t cin, int32_t tile_rows
   if (hflag & kFlagImportance) return fail(HINM_EIMPORTANCE, "importance has a negative or non-finite entry");
 
   // grid v = t_s - step*k, k = 0, 1, ..., down to max(0, 2 t_s - 1); stop at the first strict decrease
+  const bool per_tile = v_tiles != nullptr;
   const double lo = std::max(0.0, 2.0 * t_s - 1.0);
   std::vector<double> hpart((size_t)T + (size_t)T * R);
-  double best_v = t_s, best_r = 0.0;
-  bool have = false;
-  int n_trace = 0;
-  for (int k = 0;; ++k) {
+  std::vector<double> best_v(per_tile ? T : 1, t_s), best_r(per_tile ? T : 1, 0.0);
+  std::vector<int> have(per_tile ? T : 1, 0), active(per_tile ? T : 1, 1), points(per_tile ? T : 1, 0);
+  int n_trace = 0, n_active = per_tile ? T : 1;
+  for (int k = 0; n_active > 0; ++k) {
     double v = t_s - step * k;
     if (v < lo - 1e-12) break;
     v = std::max(v, lo);
@@ -497,7 +573,7 @@ extern "C" int hinm_boundary_search(int64_t cout, int64_t cin, int32_t tile_rows
     hipLaunchKernelGGL(cut_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, rank, n, pv.n_dense,
                        pv.n_24, reg);
     hipLaunchKernelGGL(compact_kernel, dim3(T), dim3(1024), 0, stream, perm, reg, C, pv.n_dense_pad, pv.n_24_pad,
-                       idx_d, idx_s);
+                       idx_d, idx_s, nullptr);
     hipLaunchKernelGGL(rdense_kernel, dim3(T), dim3(256), 0, stream, scores, rank, C, pv.n_dense, part);
     if (pv.groups > 0)
       hipLaunchKernelGGL(r24_kernel, dim3(R, T), dim3(256), 0, stream, importance, ldi, idx_s, pv.n_24_pad, pv.groups,
@@ -508,25 +584,73 @@ extern "C" int hinm_boundary_search(int64_t cout, int64_t cin, int32_t tile_rows
     e = hipMemcpyAsync(hpart.data(), part, nbytes, hipMemcpyDeviceToHost, stream);
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return hip_fail(e, "boundary step");
-    // total in a fixed order: tiles' dense sums, then rows' 2:4 sums
-    double r_tot = 0.0;
-    for (int t = 0; t < T; ++t) r_tot += hpart[t];
-    if (pv.groups > 0)
-      for (size_t i = 0; i < (size_t)T * R; ++i) r_tot += hpart[T + i];
-    if (n_trace < trace_cap) {
-      trace_v[n_trace] = v;
-      trace_r[n_trace] = r_tot;
+    // totals in a fixed order: per tile its dense sum, then its rows' 2:4 sums
+    std::vector<double> r_tile(T);
+    for (int t = 0; t < T; ++t) {
+      double r = hpart[t];
+      if (pv.groups > 0)
+        for (int i = 0; i < R; ++i) r += hpart[T + (size_t)t * R + i];
+      r_tile[t] = r;
     }
-    ++n_trace;
-    if (have && r_tot < best_r) break;
-    best_v = v;
-    best_r = r_tot;
-    have = true;
+    auto visit = [&](int u, double r) {
+      ++points[u];
+      if (have[u] && r < best_r[u]) {
+        active[u] = 0;
+        --n_active;
+        return;
+      }
+      best_v[u] = v;
+      best_r[u] = r;
+      have[u] = 1;
+    };
+    if (per_tile) {
+      for (int t = 0; t < T; ++t)
+        if (active[t]) visit(t, r_tile[t]);
+    } else {
+      double r_tot = 0.0;
+      for (int t = 0; t < T; ++t) r_tot += hpart[t];
+      if (pv.groups > 0)
+        for (size_t i = 0; i < (size_t)T * R; ++i) r_tot += hpart[T + i];
+      if (n_trace < trace_cap) {
+        trace_v[n_trace] = v;
+        trace_r[n_trace] = r_tot;
+      }
+      ++n_trace;
+      visit(0, r_tot);
+    }
   }
-  hinm_plan_t pb;
-  st = hinm_plan(cout, cin, tile_rows, t_s, best_v, &pb);
-  if (st) return st;
-  *v_s_out = (double)pb.n_pruned / (double)cin;
+  for (size_t u = 0; u < best_v.size(); ++u) {
+    hinm_plan_t pb;
+    st = hinm_plan(cout, cin, tile_rows, t_s, best_v[u], &pb);
+    if (st) return st;
+    const double vs = (double)pb.n_pruned / (double)cin;
+    if (per_tile) {
+      v_tiles[u] = vs;
+      if (points_tiles) points_tiles[u] = points[u];
+    } else {
+      *v_s_out = vs;
+    }
+  }
   if (trace_len) *trace_len = n_trace;
   return HINM_OK;
+}
+
+extern "C" int hinm_boundary_search(int64_t cout, int64_t cin, int32_t tile_rows, double t_s, double step,
+                                    const float* importance, int64_t ldi, const int32_t* perm, void* workspace,
+                                    size_t workspace_bytes, double* v_s_out, double* trace_v, double* trace_r,
+                                    int32_t trace_cap, int32_t* trace_len, void* stream) {
+  hinm::clear_error();
+  if (!v_s_out) return fail(HINM_EINVAL, "v_s_out must be non-NULL");
+  return boundary_core(cout, cin, tile_rows, t_s, step, importance, ldi, perm, workspace, workspace_bytes, v_s_out,
+                       trace_v, trace_r, trace_cap, trace_len, nullptr, nullptr, stream);
+}
+
+extern "C" int hinm_boundary_search_tiles(int64_t cout, int64_t cin, int32_t tile_rows, double t_s, double step,
+                                          const float* importance, int64_t ldi, const int32_t* perm,
+                                          void* workspace, size_t workspace_bytes, double* v_s_tiles,
+                                          int32_t* points_tiles, void* stream) {
+  hinm::clear_error();
+  if (!v_s_tiles) return fail(HINM_EINVAL, "v_s_tiles must be non-NULL");
+  return boundary_core(cout, cin, tile_rows, t_s, step, importance, ldi, perm, workspace, workspace_bytes, nullptr,
+                       nullptr, nullptr, 0, nullptr, v_s_tiles, points_tiles, stream);
 }

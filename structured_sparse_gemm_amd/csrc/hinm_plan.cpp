@@ -34,6 +34,48 @@ int check_plan(const hinm_plan_t* p) {
   return HINM_OK;
 }
 
+int check_tplan(const hinm_tplan_t* p) {
+  if (!p) return fail(HINM_EINVAL, "plan is NULL");
+  if (p->abi_version != HINM_ABI_VERSION)
+    return fail(HINM_EINVAL, "plan has abi_version %d, library is %d", p->abi_version, HINM_ABI_VERSION);
+  hinm_plan_t q;
+  int st = hinm_plan(p->cout, p->cin, p->tile_rows, p->t_s, p->t_s, &q);
+  if (st != HINM_OK) return st;
+  const int64_t R = p->tile_rows, cin_pad_d = (int64_t)(p->cin + 31) / 32 * 32, cin_pad_s = (int64_t)(p->cin + 63) / 64 * 64;
+  bool ok = p->n_tiles == q.n_tiles && p->z == q.z && p->max_n_dense_pad >= 0 && p->max_n_dense_pad <= cin_pad_d &&
+            p->max_n_dense_pad % HINM_KB_DENSE == 0 && p->max_n_24_pad >= 0 && p->max_n_24_pad <= cin_pad_s &&
+            p->max_n_24_pad % HINM_KB_24 == 0 && p->dense_blocks >= 0 && p->blocks_24 >= 0 &&
+            (int64_t)p->dense_blocks <= (int64_t)p->n_tiles * (p->max_n_dense_pad / HINM_KB_DENSE) &&
+            (int64_t)p->blocks_24 <= (int64_t)p->n_tiles * (p->max_n_24_pad / HINM_KB_24);
+  ok = ok && p->bytes_val_dense == (int64_t)p->dense_blocks * R * 64 && p->bytes_idx_dense == (int64_t)p->dense_blocks * 128 &&
+       p->bytes_val_24 == (int64_t)p->blocks_24 * R * 64 && p->bytes_meta_24 == (int64_t)p->blocks_24 * R * 8 &&
+       p->bytes_idx_24 == (int64_t)p->blocks_24 * 256 && p->bytes_tiles == (int64_t)p->n_tiles * 16;
+  if (!ok) return fail(HINM_EINVAL, "per-tile plan fields are not consistent (use hinm_plan_tiles)");
+  return HINM_OK;
+}
+
+hinm_plan_t shape_plan(const hinm_tplan_t& p) {
+  hinm_plan_t q;
+  memset(&q, 0, sizeof(q));
+  q.abi_version = p.abi_version;
+  q.cout = p.cout;
+  q.cin = p.cin;
+  q.tile_rows = p.tile_rows;
+  q.n_tiles = p.n_tiles;
+  q.z = p.z;
+  q.n_dense_pad = p.max_n_dense_pad;
+  q.n_24_pad = p.max_n_24_pad;
+  q.kb_dense = HINM_KB_DENSE;
+  q.kb_24 = HINM_KB_24;
+  q.t_s = p.t_s;
+  q.bytes_val_dense = p.bytes_val_dense;
+  q.bytes_idx_dense = p.bytes_idx_dense;
+  q.bytes_val_24 = p.bytes_val_24;
+  q.bytes_meta_24 = p.bytes_meta_24;
+  q.bytes_idx_24 = p.bytes_idx_24;
+  return q;
+}
+
 }  // namespace hinm
 
 using hinm::fail;
@@ -203,5 +245,79 @@ extern "C" int hinm_spmm_workspace_bytes(const hinm_plan_t* plan, int64_t batch,
   if (!bytes) return fail(HINM_EINVAL, "bytes is NULL");
   if (batch < 0) return fail(HINM_ESHAPE, "batch=%lld is negative", (long long)batch);
   *bytes = batch == 0 ? 0 : (size_t)hinm::spmm_shape(plan, batch).ws_bytes;
+  return HINM_OK;
+}
+
+// Per-tile counts (FlexHiNM-GP notes, "整体框架": region ratios decided in
+// each tile): tile t gets the counts of hinm_plan at (t_s, v_s[t]); the
+// tiles' K-blocks are laid end to end.
+extern "C" int hinm_plan_tiles(int64_t cout, int64_t cin, int32_t tile_rows, double t_s, const double* v_s,
+                               hinm_tplan_t* out, int32_t* tiles) {
+  hinm::clear_error();
+  if (!v_s || !out || !tiles) return fail(HINM_EINVAL, "v_s, out and tiles_out must be non-NULL");
+  hinm_plan_t p0;
+  int st = hinm_plan(cout, cin, tile_rows, t_s, t_s, &p0);
+  if (st) return st;
+  int64_t kd = 0, ks = 0;
+  int32_t maxd = 0, maxs = 0;
+  for (int t = 0; t < p0.n_tiles; ++t) {
+    hinm_plan_t pt;
+    st = hinm_plan(cout, cin, tile_rows, t_s, v_s[t], &pt);
+    if (st) {
+      char msg[256];
+      snprintf(msg, sizeof(msg), "%s", hinm_last_error());
+      return fail(st, "tile %d: %s", t, msg);
+    }
+    tiles[4 * t + 0] = (int32_t)kd;
+    tiles[4 * t + 1] = pt.n_dense;
+    tiles[4 * t + 2] = (int32_t)ks;
+    tiles[4 * t + 3] = pt.n_24;
+    kd += pt.n_dense_pad / HINM_KB_DENSE;
+    ks += pt.n_24_pad / HINM_KB_24;
+    maxd = pt.n_dense_pad > maxd ? pt.n_dense_pad : maxd;
+    maxs = pt.n_24_pad > maxs ? pt.n_24_pad : maxs;
+    if (kd > INT32_MAX || ks > INT32_MAX) return fail(HINM_ESHAPE, "too many K-blocks");
+  }
+  hinm_tplan_t& o = *out;
+  memset(&o, 0, sizeof(o));
+  o.abi_version = HINM_ABI_VERSION;
+  o.cout = p0.cout;
+  o.cin = p0.cin;
+  o.tile_rows = p0.tile_rows;
+  o.n_tiles = p0.n_tiles;
+  o.z = p0.z;
+  o.max_n_dense_pad = maxd;
+  o.max_n_24_pad = maxs;
+  o.dense_blocks = (int32_t)kd;
+  o.blocks_24 = (int32_t)ks;
+  o.t_s = t_s;
+  const int64_t R = p0.tile_rows;
+  o.bytes_val_dense = kd * R * 64;
+  o.bytes_idx_dense = kd * 128;
+  o.bytes_val_24 = ks * R * 64;
+  o.bytes_meta_24 = ks * R * 8;
+  o.bytes_idx_24 = ks * 256;
+  o.bytes_tiles = (int64_t)p0.n_tiles * 16;
+  return HINM_OK;
+}
+
+extern "C" int hinm_pack_tiles_workspace_bytes(const hinm_tplan_t* plan, size_t* bytes) {
+  hinm::clear_error();
+  int st = hinm::check_tplan(plan);
+  if (st) return st;
+  if (!bytes) return fail(HINM_EINVAL, "bytes is NULL");
+  const size_t tc = (size_t)plan->n_tiles * plan->cin;
+  *bytes = 256 + tc * 8 + (tc + 255) / 256 * 256;
+  return HINM_OK;
+}
+
+extern "C" int hinm_spmm_tiles_workspace_bytes(const hinm_tplan_t* plan, int64_t batch, size_t* bytes) {
+  hinm::clear_error();
+  int st = hinm::check_tplan(plan);
+  if (st) return st;
+  if (!bytes) return fail(HINM_EINVAL, "bytes is NULL");
+  if (batch < 0) return fail(HINM_ESHAPE, "batch=%lld is negative", (long long)batch);
+  const hinm_plan_t q = hinm::shape_plan(*plan);
+  *bytes = batch == 0 ? 0 : (size_t)hinm::spmm_shape(&q, batch).ws_bytes;
   return HINM_OK;
 }

@@ -54,7 +54,20 @@ struct SpmmArgs {
   int y_vec;                 // 1: 16-byte aligned Y rows (ldy % 8 == 0)
   int n_tiles;
   const int32_t* out_rows;   // NULL, or the Y row of each product row
+  const int32_t* tiles;      // NULL (uniform counts), or [n_tiles][4]: first dense block, n_dense,
+                             // first 2:4 block, n_24 of each tile
+  int kd_total, ks_total;    // dense and 2:4 K-blocks over all tiles
 };
+
+// Tile t's K-blocks: first dense block and count, first 2:4 block and count.
+struct TileK {
+  int kd0, nbd, ks0, nbs;
+};
+__device__ inline TileK tile_k(const SpmmArgs& a, int t) {
+  if (a.tiles)
+    return {a.tiles[4 * t], (a.tiles[4 * t + 1] + 31) / 32, a.tiles[4 * t + 2], (a.tiles[4 * t + 3] + 63) / 64};
+  return {t * a.nkb_d, a.nkb_d, t * a.nkb_s, a.nkb_s};
+}
 
 // Y row that product row r goes to: r itself, or out_rows[r]; -1 for an
 // out-of-range entry (the row is then not written).
@@ -400,16 +413,17 @@ __global__ __launch_bounds__(384) void decode5_kernel(SpmmArgs a, int splits, in
   const int tb = blockIdx.y;
   const int n0 = tb * NTOK;
   const int row = rb * 64 + (wave & 3) * 16 + (lane & 15);   // tile row of this lane's A fragment
-  const int nblk = a.nkb_d + a.nkb_s;
+  const TileK tk = tile_k(a, t);
+  const int nblk = tk.nbd + tk.nbs;
   const int b_lo = (int)((int64_t)split * nblk / splits), b_hi = (int)((int64_t)(split + 1) * nblk / splits);
 
   BufRes res;
   res.x = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, (int)(uint32_t)(((int64_t)(a.cin - 1) * a.ldx + a.batch) * 2), kBufferWord3);
-  res.vd = __builtin_amdgcn_make_buffer_rsrc((void*)a.val_d, (short)0, (int)((uint32_t)a.n_tiles * a.nkb_d * a.rows * 64u), kBufferWord3);
-  res.vs = __builtin_amdgcn_make_buffer_rsrc((void*)a.val_s, (short)0, (int)((uint32_t)a.n_tiles * a.nkb_s * a.rows * 64u), kBufferWord3);
-  res.meta = __builtin_amdgcn_make_buffer_rsrc((void*)a.meta, (short)0, (int)((uint32_t)a.n_tiles * a.nkb_s * a.rows * 8u), kBufferWord3);
-  res.id = __builtin_amdgcn_make_buffer_rsrc((void*)a.idx_d, (short)0, (int)((uint32_t)a.n_tiles * a.nkb_d * 32u * 4u), kBufferWord3);
-  res.is = __builtin_amdgcn_make_buffer_rsrc((void*)a.idx_s, (short)0, (int)((uint32_t)a.n_tiles * a.nkb_s * 64u * 4u), kBufferWord3);
+  res.vd = __builtin_amdgcn_make_buffer_rsrc((void*)a.val_d, (short)0, (int)((uint32_t)a.kd_total * a.rows * 64u), kBufferWord3);
+  res.vs = __builtin_amdgcn_make_buffer_rsrc((void*)a.val_s, (short)0, (int)((uint32_t)a.ks_total * a.rows * 64u), kBufferWord3);
+  res.meta = __builtin_amdgcn_make_buffer_rsrc((void*)a.meta, (short)0, (int)((uint32_t)a.ks_total * a.rows * 8u), kBufferWord3);
+  res.id = __builtin_amdgcn_make_buffer_rsrc((void*)a.idx_d, (short)0, (int)((uint32_t)a.kd_total * 32u * 4u), kBufferWord3);
+  res.is = __builtin_amdgcn_make_buffer_rsrc((void*)a.idx_s, (short)0, (int)((uint32_t)a.ks_total * 64u * 4u), kBufferWord3);
   res.ldx_bytes = (uint32_t)a.ldx * 2u;
 
   f32x4 acc[2][NB];
@@ -434,7 +448,7 @@ __global__ __launch_bounds__(384) void decode5_kernel(SpmmArgs a, int splits, in
     const int r1 = min(r0 + MAXB, b_hi);
     const int nbr = r1 - r0;
     // dense blocks come first in the block order
-    const int nd_r = max(0, min(r1, a.nkb_d) - r0);
+    const int nd_r = max(0, min(r1, tk.nbd) - r0);
     if (gather) {
       // Gather thread gt takes 16-byte chunk gt % CPR of LDS positions
       // gt / CPR + PPJ * j; position p is slot p % 64 of block p / 64, so the
@@ -444,8 +458,8 @@ __global__ __launch_bounds__(384) void decode5_kernel(SpmmArgs a, int splits, in
       const int gt = threadIdx.x - 256;
       const int pofs = gt / CPR;
       const uint32_t xcol = (uint32_t)(n0 + 8 * (gt % CPR)) * 2u;
-      const uint32_t dbase = (uint32_t)(t * a.nkb_d + r0) * 32u;
-      const uint32_t sbase = (uint32_t)(t * a.nkb_s + max(0, r0 - a.nkb_d)) * 64u;
+      const uint32_t dbase = (uint32_t)(tk.kd0 + r0) * 32u;
+      const uint32_t sbase = (uint32_t)(tk.ks0 + max(0, r0 - tk.nbd)) * 64u;
       int cidx[MAXCH];
 #pragma unroll
       for (int j = 0; j < MAXCH; ++j) {
@@ -483,9 +497,9 @@ __global__ __launch_bounds__(384) void decode5_kernel(SpmmArgs a, int splits, in
 #pragma unroll
       for (int j = 0; j < MAXB; ++j) {
         const int b = r0 + min(j, nbr - 1);
-        const bool dense = b < a.nkb_d;
-        const uint32_t brow = dense ? (uint32_t)((t * a.nkb_d + b) * a.rows + row)
-                                    : (uint32_t)((t * a.nkb_s + (b - a.nkb_d)) * a.rows + row);
+        const bool dense = b < tk.nbd;
+        const uint32_t brow = dense ? (uint32_t)((tk.kd0 + b) * a.rows + row)
+                                    : (uint32_t)((tk.ks0 + (b - tk.nbd)) * a.rows + row);
         av[j] = __builtin_amdgcn_raw_buffer_load_b128(dense ? res.vd : res.vs, brow * 64u + 16u * kc, 0, 0);
         mv[j] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(res.meta, dense ? kOob : brow * 8u, 0, 0));
       }
@@ -624,13 +638,12 @@ struct PrefillA {
 //     into a small LDS array.
 template <int NT, bool FAST, bool DENSE>
 __device__ inline void prefill_phase(const SpmmArgs& a, const BufRes& res, uint16_t* xs0, uint16_t* xs1,
-                                     uint32_t* ms0, uint32_t* ms1, int t, int rb, int n0,
+                                     uint32_t* ms0, uint32_t* ms1, int kbase, int nb, int rb, int n0,
                                      f32x16 (&acc)[2][PrefillCfg<NT>::NTB]) {
   using C = PrefillCfg<NT>;
   constexpr int KPOS = DENSE ? 32 : 64;       // positions per block
   constexpr int PPT = KPOS / C::PG;           // gathered rows per thread
   constexpr int WP = KPOS / 4;                // positions per wave
-  const int nb = DENSE ? a.nkb_d : a.nkb_s;
   if (nb == 0) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -656,7 +669,7 @@ __device__ inline void prefill_phase(const SpmmArgs& a, const BufRes& res, uint1
   const uint32_t ipos = (uint32_t)(wave * WP + (lane % WP));
   auto load_idx = [&](int b) -> int {
     b = min(b, nb - 1);
-    const uint32_t off = ((uint32_t)(t * nb + b) * KPOS + ipos) * 4u;
+    const uint32_t off = ((uint32_t)(kbase + b) * KPOS + ipos) * 4u;
     return (int)__builtin_amdgcn_raw_buffer_load_b32(rid, off, 0, 0);
   };
   auto spread_idx = [&](int iw, int (&ci)[PPT]) {
@@ -684,7 +697,7 @@ __device__ inline void prefill_phase(const SpmmArgs& a, const BufRes& res, uint1
   };
   auto load_a = [&](int b, PrefillA& st) {
     b = min(b, nb - 1);
-    const uint32_t blk = (uint32_t)(t * nb + b) * (uint32_t)a.rows + vrow;
+    const uint32_t blk = (uint32_t)(kbase + b) * (uint32_t)a.rows + vrow;
     st.v = __builtin_amdgcn_raw_buffer_load_b128(rv, blk * 64u + 16u * threadIdx.x, 0, 0);
     if constexpr (!DENSE)
       st.m = __builtin_amdgcn_raw_buffer_load_b32(res.meta, threadIdx.x < 128 ? blk * 8u + 4u * threadIdx.x : kOob,
@@ -803,8 +816,9 @@ template <int NT, bool FAST>
 __device__ inline void prefill_body(const SpmmArgs& a, const BufRes& res, uint16_t* xs0, uint16_t* xs1,
                                     uint32_t* ms0, uint32_t* ms1, int t, int rb, int n0,
                                     f32x16 (&acc)[2][PrefillCfg<NT>::NTB]) {
-  prefill_phase<NT, FAST, true>(a, res, xs0, xs1, ms0, ms1, t, rb, n0, acc);
-  prefill_phase<NT, FAST, false>(a, res, xs0, xs1, ms0, ms1, t, rb, n0, acc);
+  const TileK tk = tile_k(a, t);
+  prefill_phase<NT, FAST, true>(a, res, xs0, xs1, ms0, ms1, tk.kd0, tk.nbd, rb, n0, acc);
+  prefill_phase<NT, FAST, false>(a, res, xs0, xs1, ms0, ms1, tk.ks0, tk.nbs, rb, n0, acc);
 }
 
 // Persistent launch: gridDim.x = 8 * per_xcd workgroups, workgroup L runs on
@@ -827,12 +841,35 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
   BufRes res;
   const uint32_t xbytes = (uint32_t)(((int64_t)(a.cin - 1) * a.ldx + a.batch) * 2);
   res.x = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, (int)xbytes, kBufferWord3);
-  res.vd = __builtin_amdgcn_make_buffer_rsrc((void*)a.val_d, (short)0, (int)((uint32_t)a.n_tiles * a.nkb_d * a.rows * 64u), kBufferWord3);
-  res.vs = __builtin_amdgcn_make_buffer_rsrc((void*)a.val_s, (short)0, (int)((uint32_t)a.n_tiles * a.nkb_s * a.rows * 64u), kBufferWord3);
-  res.meta = __builtin_amdgcn_make_buffer_rsrc((void*)a.meta, (short)0, (int)((uint32_t)a.n_tiles * a.nkb_s * a.rows * 8u), kBufferWord3);
-  res.id = __builtin_amdgcn_make_buffer_rsrc((void*)a.idx_d, (short)0, (int)((uint32_t)a.n_tiles * a.nkb_d * 32u * 4u), kBufferWord3);
-  res.is = __builtin_amdgcn_make_buffer_rsrc((void*)a.idx_s, (short)0, (int)((uint32_t)a.n_tiles * a.nkb_s * 64u * 4u), kBufferWord3);
+  res.vd = __builtin_amdgcn_make_buffer_rsrc((void*)a.val_d, (short)0, (int)((uint32_t)a.kd_total * a.rows * 64u), kBufferWord3);
+  res.vs = __builtin_amdgcn_make_buffer_rsrc((void*)a.val_s, (short)0, (int)((uint32_t)a.ks_total * a.rows * 64u), kBufferWord3);
+  res.meta = __builtin_amdgcn_make_buffer_rsrc((void*)a.meta, (short)0, (int)((uint32_t)a.ks_total * a.rows * 8u), kBufferWord3);
+  res.id = __builtin_amdgcn_make_buffer_rsrc((void*)a.idx_d, (short)0, (int)((uint32_t)a.kd_total * 32u * 4u), kBufferWord3);
+  res.is = __builtin_amdgcn_make_buffer_rsrc((void*)a.idx_s, (short)0, (int)((uint32_t)a.ks_total * 64u * 4u), kBufferWord3);
   res.ldx_bytes = (uint32_t)a.ldx * 2u;
+
+  // Per-tile counts: tiles differ in K-blocks, so each token block takes the
+  // tiles in order of cost (dense + 2:4 blocks, largest first, ties by tile),
+  // alternating direction from one token block to the next.  A workgroup
+  // slot that meets a costly tile in one token block then meets a cheap one
+  // in the next (tiles past the table's LDS room keep their natural order).
+  constexpr int kMaxOrdered = 1024;
+  __shared__ int16_t order[kMaxOrdered];
+  const bool ordered = a.tiles != nullptr && a.n_tiles <= kMaxOrdered;
+  if (ordered) {
+    for (int t = threadIdx.x; t < a.n_tiles; t += 256) {
+      const TileK k = tile_k(a, t);
+      const int c = k.nbd + k.nbs;
+      int r = 0;
+      for (int u = 0; u < a.n_tiles; ++u) {
+        const TileK ku = tile_k(a, u);
+        const int cu = ku.nbd + ku.nbs;
+        r += (cu > c) | ((cu == c) & (u < t));
+      }
+      order[r] = (int16_t)t;
+    }
+    __syncthreads();
+  }
 
   const int items = n_tb * n_tr;
   const int i_lo = (int)((int64_t)xcd * items / 8), i_hi = (int)((int64_t)(xcd + 1) * items / 8);
@@ -840,7 +877,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
     {
       const int tb = it / n_tr, trb = it % n_tr;
       const int n0 = tb * NT;
-      const int t = trb / nrb, rb = trb % nrb;
+      int t = trb / nrb;
+      const int rb = trb % nrb;
+      if (ordered) t = order[(tb & 1) ? a.n_tiles - 1 - t : t];
       f32x16 acc[2][C::NTB];
       for (int r = 0; r < 2; ++r)
         for (int j = 0; j < C::NTB; ++j)
@@ -899,12 +938,25 @@ int ensure_device() {
 
 }  // namespace hinm
 
-static int spmm_impl(const hinm_packed_t* packed, const void* x_bf16, int64_t batch, int64_t ldx, void* y_bf16,
-                     int64_t ldy, const int32_t* out_rows, void* workspace, size_t workspace_bytes, void* stream_) {
-  if (!packed) return fail(HINM_EINVAL, "packed is NULL");
-  int st = hinm::check_plan(&packed->plan);
-  if (st) return st;
-  const hinm_plan_t& p = packed->plan;
+// The packed buffers of either layout: the uniform one (tiles == NULL, block
+// counts from the plan) or the per-tile one (a device tile table).
+struct PackedView {
+  const void* val_dense;
+  const int32_t* idx_dense;
+  const void* val_24;
+  const uint64_t* meta_24;
+  const int32_t* idx_24;
+  const int32_t* tiles;
+  int kd_total, ks_total;
+};
+
+// `p` has been validated by the caller (for the per-tile layout it carries
+// the largest per-tile pads and the buffer totals).
+static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const void* x_bf16, int64_t batch,
+                     int64_t ldx, void* y_bf16, int64_t ldy, const int32_t* out_rows, void* workspace,
+                     size_t workspace_bytes, void* stream_) {
+  const PackedView* packed = &packed_v;
+  int st = HINM_OK;
   if (batch < 0) return fail(HINM_ESHAPE, "batch=%lld is negative", (long long)batch);
   if (batch > (1 << 24)) return fail(HINM_ESHAPE, "batch=%lld exceeds 2^24", (long long)batch);
   if (ldx < batch || ldy < batch)
@@ -959,6 +1011,9 @@ static int spmm_impl(const hinm_packed_t* packed, const void* x_bf16, int64_t ba
   a.y_vec = hinm::aligned(y_bf16, 16) && (ldy % 8 == 0);
   a.n_tiles = p.n_tiles;
   a.out_rows = out_rows;
+  a.tiles = packed->tiles;
+  a.kd_total = packed->kd_total;
+  a.ks_total = packed->ks_total;
 
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   // The prefill and split decode kernels address X and the packed buffers
@@ -976,6 +1031,8 @@ static int spmm_impl(const hinm_packed_t* packed, const void* x_bf16, int64_t ba
     sh.splits = 1;
     a.splits = 1;
   }
+  if (packed->tiles && !((sh.path == hinm::kPathPrefill || sh.path == hinm::kPathDecodeSplit) && fits32))
+    return fail(HINM_ESHAPE, "the per-tile layout needs tile_rows %% 64 == 0 and buffers below 2^31 bytes");
   if (sh.path == hinm::kPathPrefill) {
     if (!fits32) {
       sh.path = hinm::kPathGeneric;
@@ -1041,17 +1098,46 @@ static int spmm_impl(const hinm_packed_t* packed, const void* x_bf16, int64_t ba
   return HINM_OK;
 }
 
+static PackedView uniform_view(const hinm_packed_t& k) {
+  const hinm_plan_t& p = k.plan;
+  return {k.val_dense, k.idx_dense, k.val_24, k.meta_24, k.idx_24, nullptr,
+          p.n_tiles * (p.n_dense_pad / HINM_KB_DENSE), p.n_tiles * (p.n_24_pad / HINM_KB_24)};
+}
+
 extern "C" int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_t batch, int64_t ldx, void* y_bf16,
                          int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
   hinm::clear_error();
-  return spmm_impl(packed, x_bf16, batch, ldx, y_bf16, ldy, nullptr, workspace, workspace_bytes, stream);
+  if (!packed) return fail(HINM_EINVAL, "packed is NULL");
+  int st = hinm::check_plan(&packed->plan);
+  if (st) return st;
+  return spmm_impl(packed->plan, uniform_view(*packed), x_bf16, batch, ldx, y_bf16, ldy, nullptr, workspace,
+                   workspace_bytes, stream);
+}
+
+extern "C" int hinm_spmm_tiles(const hinm_tpacked_t* packed, const void* x_bf16, int64_t batch, int64_t ldx,
+                               void* y_bf16, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
+  hinm::clear_error();
+  if (!packed) return fail(HINM_EINVAL, "packed is NULL");
+  int st = hinm::check_tplan(&packed->plan);
+  if (st) return st;
+  if (!packed->tiles) return fail(HINM_EINVAL, "the tile table is NULL");
+  if (!hinm::aligned(packed->tiles, 4)) return fail(HINM_EALIGN, "the tile table is not 4-byte aligned");
+  const hinm_tplan_t& p = packed->plan;
+  const PackedView v = {packed->val_dense, packed->idx_dense, packed->val_24, packed->meta_24, packed->idx_24,
+                        packed->tiles, p.dense_blocks, p.blocks_24};
+  return spmm_impl(hinm::shape_plan(p), v, x_bf16, batch, ldx, y_bf16, ldy, nullptr, workspace, workspace_bytes,
+                   stream);
 }
 
 extern "C" int hinm_spmm_rows(const hinm_packed_t* packed, const void* x_bf16, int64_t batch, int64_t ldx,
                               void* y_bf16, int64_t ldy, const int32_t* out_rows, void* workspace,
                               size_t workspace_bytes, void* stream) {
   hinm::clear_error();
+  if (!packed) return fail(HINM_EINVAL, "packed is NULL");
+  int st = hinm::check_plan(&packed->plan);
+  if (st) return st;
   if (!out_rows) return fail(HINM_EINVAL, "out_rows is NULL");
   if (!hinm::aligned(out_rows, 4)) return fail(HINM_EALIGN, "out_rows is not 4-byte aligned");
-  return spmm_impl(packed, x_bf16, batch, ldx, y_bf16, ldy, out_rows, workspace, workspace_bytes, stream);
+  return spmm_impl(packed->plan, uniform_view(*packed), x_bf16, batch, ldx, y_bf16, ldy, out_rows, workspace,
+                   workspace_bytes, stream);
 }

@@ -199,3 +199,59 @@ def test_workspace_sizes(lib):
         assert hinm.spmm_workspace_bytes(p, b) % 4 == 0
     p = hinm.plan(96, 4096, 48, 0.75, 0.55)
     assert hinm.spmm_workspace_bytes(p, 200) % 256 == 0
+
+
+def test_plan_tiles_matches_oracle():
+    """Per-tile counts and block offsets equal the oracle's per-tile plan, on random shapes and v_s."""
+    import oracle.hinm as oh
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        R = int(rng.choice([16, 32, 64]))
+        T = int(rng.integers(1, 9))
+        cin = 4 * int(rng.integers(1, 600))
+        t_s = float(rng.uniform(0, 0.95))
+        lo = max(0.0, 2 * t_s - 1)
+        v = [float(x) for x in rng.uniform(lo, t_s, T)]
+        tp = hinm.plan_tiles(T * R, cin, R, t_s, v)
+        plans = oh.plan_tiles(T * R, cin, R, t_s, v)
+        kd = ks = 0
+        for t, pl in enumerate(plans):
+            assert tuple(tp.tiles[t]) == (kd, pl.n_dense, ks, pl.n_24)
+            kd += pl.n_dense_pad // 32
+            ks += pl.n_24_pad // 64
+        assert (tp.dense_blocks, tp.blocks_24) == (kd, ks)
+        assert tp.max_n_dense_pad == max(pl.n_dense_pad for pl in plans)
+        assert tp.max_n_24_pad == max(pl.n_24_pad for pl in plans)
+        assert tp.z == plans[0].z
+        assert tp.bytes_val_24 == ks * R * 64 and tp.bytes_meta_24 == ks * R * 8 and tp.bytes_idx_dense == kd * 128
+
+
+def test_tiles_host_errors(lib):
+    v = (ctypes.c_double * 4)(0.5, 0.55, 0.6, 0.8)          # 0.8 > t_s
+    raw, tiles = hinm.TPlanT(), (ctypes.c_int32 * 16)()
+    assert lib.hinm_plan_tiles(256, 512, 64, 0.75, v, ctypes.byref(raw), tiles) == 1
+    assert b"tile 3" in lib.hinm_last_error()
+    assert lib.hinm_plan_tiles(256, 512, 64, 0.75, None, ctypes.byref(raw), tiles) == 1
+    tp = hinm.plan_tiles(256, 512, 64, 0.75, [0.5, 0.55, 0.6, 0.7])
+    n = ctypes.c_size_t()
+    assert lib.hinm_pack_tiles_workspace_bytes(ctypes.byref(tp.raw), ctypes.byref(n)) == 0
+    assert n.value >= 4 * 512 * 9
+    assert lib.hinm_spmm_tiles_workspace_bytes(ctypes.byref(tp.raw), 2048, ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.hinm_spmm_tiles_workspace_bytes(ctypes.byref(tp.raw), 16, ctypes.byref(n)) == 0
+    bad = hinm.TPlanT.from_buffer_copy(tp.raw)
+    bad.blocks_24 += 1                                      # sizes no longer consistent
+    assert lib.hinm_pack_tiles_workspace_bytes(ctypes.byref(bad), ctypes.byref(n)) == 1
+    bad = hinm.TPlanT.from_buffer_copy(tp.raw)
+    bad.z += 1
+    assert lib.hinm_spmm_tiles_workspace_bytes(ctypes.byref(bad), 16, ctypes.byref(n)) == 1
+    pk = hinm.TPackedT(tp.raw, None, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20)
+    call = lambda **kw: lib.hinm_spmm_tiles(ctypes.byref(kw.get("pk", pk)), 1 << 20, kw.get("batch", 16), 16,
+                                            1 << 20, 16, kw.get("ws", 1 << 20), 1 << 24, None)
+    assert call() == 1                                      # no tile table
+    pk2 = hinm.TPackedT(tp.raw, (1 << 20) + 2, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20)
+    assert call(pk=pk2) == 5
+    pk3 = hinm.TPackedT(tp.raw, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20)
+    assert call(pk=pk3, batch=-1) == 2
+    out = hinm.TPackedT(tp.raw, None, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20)
+    assert lib.hinm_pack_tiles(ctypes.byref(tp.raw), 1 << 20, 512, 1 << 20, 512, None, ctypes.byref(out),
+                               1 << 20, 1 << 24, None) == 1
