@@ -346,22 +346,27 @@ def main():
                 fn()
         g.replay()
         torch.cuda.synchronize()
-        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a_.record()
-        g.replay()
-        b_.record()
-        torch.cuda.synchronize()
-        return a_.elapsed_time(b_) / steps
+        times = []
+        for _ in range(5):            # median of five replays: single replays vary by several percent
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record()
+            g.replay()
+            b_.record()
+            torch.cuda.synchronize()
+            times.append(a_.elapsed_time(b_) / steps)
+        return sorted(times)[2]
 
     y_t = torch.empty(p.cout, B, dtype=torch.bfloat16, device=dev)
     yd_t = torch.empty(p.cout, Bd, dtype=torch.bfloat16, device=dev)
     ws_t = torch.zeros(max(1, hinm.spmm_tiles_workspace_bytes(pk_tiles.plan, Bd)), dtype=torch.uint8, device=dev)
+    costs = [(int(r[1]) + 31) // 32 + 2 * ((int(r[3]) + 63) // 64) for r in pk_tiles.plan.tiles]
     kept_t = sum(int(r[1]) + int(r[3]) // 2 for r in pk_tiles.plan.tiles)       # kept entries per row, summed over tiles
     useful_t = 2 * p.tile_rows * kept_t * B
     next_tiles = {
         "what": "per-tile v_s from hinm_boundary_search_tiles on this weight (importance |W|, t_s 0.75), packed by "
-                "hinm_pack_tiles, products by hinm_spmm_tiles; graph-timed like the uniform products but on one "
-                "resident copy (the uniform product on one resident copy is given for comparison)",
+                "hinm_pack_tiles, products by hinm_spmm_tiles; graph-timed (median of five replays) on one resident "
+                "copy, beside the uniform product timed the same way; tile cost = dense blocks + 2 x 2:4 blocks "
+                "(X rows gathered / 32)",
         "v_s_min": round(min(v_tiles), 5), "v_s_max": round(max(v_tiles), 5),
         "dense_blocks": pk_tiles.plan.dense_blocks, "blocks_24": pk_tiles.plan.blocks_24,
         "uniform_dense_blocks": p.n_tiles * p.n_dense_pad // 32, "uniform_blocks_24": p.n_tiles * p.n_24_pad // 64,
@@ -371,6 +376,8 @@ def main():
         "spmm_tiles_batch_16_ms": round(graph_ms(lambda: hinm.spmm(pk_tiles, xd, out=yd_t, workspace=ws_t), 100), 5),
         "spmm_uniform_resident_batch_16_ms": round(graph_ms(lambda: hinm.spmm(pk, xd, out=yd_t, workspace=ws_t), 100),
                                                    5),
+        "tile_cost_min": int(min(costs)), "tile_cost_mean": round(sum(costs) / len(costs), 2),
+        "tile_cost_max": int(max(costs)),
         "useful_tflops_batch_2048": None}
     next_tiles["useful_tflops_batch_2048"] = round(useful_t / (next_tiles["spmm_tiles_batch_2048_ms"] * 1e-3) / 1e12, 2)
 

@@ -208,6 +208,14 @@ int hinm_spmm_workspace_bytes(const hinm_plan_t* plan, int64_t batch, size_t* by
  * batch == 0 is a no-op.  Asynchronous on `stream`; no host synchronisation.
  * Partial sums of a split reduction dimension are added in split order, so
  * the same inputs give bitwise-identical Y on every call.
+ * Launch-shape overrides, read from the environment at each call (for
+ * tuning; unset gives the defaults): HINM_PREFILL_NT = 128 | 256 (token
+ * block of the batch > 64 kernel), HINM_PREFILL_PER_XCD = n > 0 (its
+ * persistent workgroups per XCD, default 64), HINM_DECODE_WGS = n > 0
+ * (about how many workgroups the batch <= 64 kernel splits K over, default
+ * 256; this changes the split count and so may change the last bits of Y),
+ * HINM_DECODE_PATH = rows16 (the 16-row batch <= 64 kernel without a K
+ * split).  The workspace size asked for must come from the same settings.
  * Errors (host-side checks only): HINM_EINVAL, HINM_ESHAPE, HINM_EALIGN,
  * HINM_EWORKSPACE, HINM_EHIP (launch failure). */
 int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_t batch, int64_t ldx,

@@ -848,22 +848,32 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
   res.is = __builtin_amdgcn_make_buffer_rsrc((void*)a.idx_s, (short)0, (int)((uint32_t)a.ks_total * 64u * 4u), kBufferWord3);
   res.ldx_bytes = (uint32_t)a.ldx * 2u;
 
-  // Per-tile counts: tiles differ in K-blocks, so each token block takes the
-  // tiles in order of cost (dense + 2:4 blocks, largest first, ties by tile),
-  // alternating direction from one token block to the next.  A workgroup
-  // slot that meets a costly tile in one token block then meets a cheap one
-  // in the next (tiles past the table's LDS room keep their natural order).
+  // Per-tile counts: every tile runs the same number of K-block steps (its
+  // kept entries per row are fixed by t_s), but a 2:4 block gathers 64 X rows
+  // against a dense block's 32, so a tile costs n_dense_blocks + 2 n_24_blocks.
+  // When workgroups take more than one item each, every token block takes the
+  // tiles largest cost first (ties by tile), alternating direction from one
+  // token block to the next, so a slot that meets a costly tile in one token
+  // block meets a cheap one in the next.  With one item per workgroup the
+  // order cannot change the finish time and is skipped; tiles past the
+  // order's LDS room keep their natural order.  The costs are staged in the
+  // second X buffer, which no item has used yet.
+  const int items = n_tb * n_tr;
   constexpr int kMaxOrdered = 1024;
   __shared__ int16_t order[kMaxOrdered];
-  const bool ordered = a.tiles != nullptr && a.n_tiles <= kMaxOrdered;
+  const bool ordered = a.tiles != nullptr && a.n_tiles <= kMaxOrdered && items > (int)gridDim.x;
   if (ordered) {
+    int16_t* cost = reinterpret_cast<int16_t*>(xs[1]);
     for (int t = threadIdx.x; t < a.n_tiles; t += 256) {
       const TileK k = tile_k(a, t);
-      const int c = k.nbd + k.nbs;
+      cost[t] = (int16_t)(k.nbd + 2 * k.nbs);
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < a.n_tiles; t += 256) {
+      const int c = cost[t];
       int r = 0;
       for (int u = 0; u < a.n_tiles; ++u) {
-        const TileK ku = tile_k(a, u);
-        const int cu = ku.nbd + ku.nbs;
+        const int cu = cost[u];
         r += (cu > c) | ((cu == c) & (u < t));
       }
       order[r] = (int16_t)t;
@@ -871,7 +881,6 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
     __syncthreads();
   }
 
-  const int items = n_tb * n_tr;
   const int i_lo = (int)((int64_t)xcd * items / 8), i_hi = (int)((int64_t)(xcd + 1) * items / 8);
   for (int it = i_lo + slot; it < i_hi; it += per_xcd) {
     {

@@ -91,6 +91,25 @@ def test_spmm_tiles_vs_oracle(batch):
     check_y(y, oh.spmm(wh, xf), np.abs(wh) @ np.abs(xf), f"spmm_tiles batch {batch}")
 
 
+@pytest.mark.parametrize("per_xcd", ["1", "3"])
+def test_spmm_tiles_cost_ordered_schedule(monkeypatch, per_xcd):
+    """Few persistent workgroups, so each takes several (token block, tile) items in cost order: same bits
+    as the launch with one item per workgroup, and within the bar of the oracle."""
+    w = synth.small(640, 2048, 64, 0.75, 0.55, 1, seed=88)
+    v = random_v(w.cout // 64, 0.75, 88)
+    pk, plans, ref, inter = pack_both(w, v)
+    x = torch.randn(w.cin, 1100, generator=torch.Generator().manual_seed(88)).to(torch.bfloat16)
+    y_one = hinm.spmm(pk, x.to(DEV))
+    monkeypatch.setenv("HINM_PREFILL_PER_XCD", per_xcd)
+    print(f"[tiles]   cost-ordered schedule, {per_xcd} workgroups per XCD", flush=True)
+    y_few = hinm.spmm(pk, x.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(y_one.view(torch.int16), y_few.view(torch.int16))
+    wh = oh.masked_weight(bits_of(w.w_bf16), inter["mask"])
+    xf = synth.as_f64(x)
+    check_y(y_few, oh.spmm(wh, xf), np.abs(wh) @ np.abs(xf), f"cost-ordered, {per_xcd} per XCD")
+
+
 def test_spmm_tiles_needs_64_row_tiles():
     w = synth.small(96, 256, 32, 0.75, 0.55, 1, seed=87)
     pk = hinm.pack_tiles(w.w_bf16.to(DEV), w.importance.to(DEV), 32, 0.75, random_v(3, 0.75, 87), w.perm.to(DEV))
