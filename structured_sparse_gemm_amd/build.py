@@ -14,8 +14,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhinm.so")
 SOURCES = ("hinm_plan.cpp", "hinm_pack.hip", "hinm_spmm.hip")
 ARCH = "gfx950"
-# Packed-fp32 VALU forms are kept off for every kernel of this library.
-DEVICE_FLAGS = ("-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops")
+# Packed-fp32 VALU forms are kept off for every kernel of this library.  MFMA
+# accumulators stay in ordinary VGPRs: with one wave per SIMD the compiler
+# would otherwise park them in AGPRs and copy them at every loop back edge.
+DEVICE_FLAGS = ("-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form=1")
 
 
 def _hipcc() -> str:

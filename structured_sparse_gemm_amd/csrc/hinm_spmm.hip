@@ -52,6 +52,7 @@ struct SpmmArgs {
   int n_rblocks, splits, n_kunits;
   int x_vec;                 // 1: 16-byte aligned X rows (ldx % 8 == 0)
   int y_vec;                 // 1: 16-byte aligned Y rows (ldy % 8 == 0)
+  int x_lds;                 // 1: the batch > 64 kernel loads X rows straight into LDS (needs x_vec)
   int n_tiles;
   const int32_t* out_rows;   // NULL, or the Y row of each product row
   const int32_t* tiles;      // NULL (uniform counts), or [n_tiles][4]: first dense block, n_dense,
@@ -812,13 +813,229 @@ __device__ inline void prefill_phase(const SpmmArgs& a, const BufRes& res, uint1
   if (b + 2 < nb) step(std::integral_constant<int, 2>{}, b + 2);
 }
 
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// s_waitcnt with only the vector-memory count: vmcnt(n), nothing else.
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// A buffer load whose 16 bytes per lane go straight to LDS: lane l's bytes
+// land at lds + 16 l (an offset past the buffer writes zeros).
+__device__ inline void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_u8*)lds, 16, off, 0, 0, 0);
+}
+
+__device__ inline v4i16 tr_read_b(const uint8_t* lds) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds_u8*)lds);
+}
+
+// prefill_phase with the X rows loaded straight into LDS (X rows 16-byte
+// aligned).  The gathered rows never pass through VGPRs: each wave issues
+// its share of block b + 1's rows into the other tile at the start of step
+// b, multiplies block b, stores the packed values of b + 1 (loaded DA blocks
+// earlier through VGPRs), waits for its own row loads and meets the other
+// waves at the barrier.
+//
+// Tile layout (bytes): X rows, 64 positions x 2 NT bytes, the 16-byte chunk c
+// of position p at chunk c ^ 4 (p % 4) (a 32-lane half of a transpose read
+// then covers every bank once); packed values at 128 NT, 64 rows x 64 bytes,
+// chunk q of row r at q ^ (r / 4 % 4).  X load j of a wave brings 64 / CPR
+// consecutive positions starting at wave * RPW + j * 64 / CPR, lane l taking
+// chunk l % CPR of position + l / CPR.
+template <int NT, bool DENSE>
+__device__ inline void prefill_phase_lds(const SpmmArgs& a, const BufRes& res, uint16_t* xs0, uint16_t* xs1,
+                                         uint32_t* ms0, uint32_t* ms1, int kbase, int nb, int rb, int n0,
+                                         f32x16 (&acc)[2][PrefillCfg<NT>::NTB]) {
+  using C = PrefillCfg<NT>;
+  constexpr int KPOS = DENSE ? 32 : 64;       // positions per block
+  constexpr int RPW = KPOS / 4;               // positions per wave
+  constexpr int XROW = 2 * NT;                // bytes per X row in LDS
+  constexpr int CPR = NT / 8;                 // 16-byte chunks per row
+  constexpr int RPL = 64 / CPR;               // positions per X load
+  constexpr int NJ = RPW / RPL;               // X loads per wave per block
+  constexpr int AOFS = 64 * XROW;             // packed values
+  constexpr int PA = DENSE ? 2 : 3;           // loads a step issues after its X loads
+  static_assert(AOFS + 64 * 64 <= 64 * C::PITCH * 2, "tile size");
+  if (nb == 0) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tok_w = wave * C::TW;
+  const int g = lane >> 4, i = lane & 15;
+  const int kcb = g >> 1;                     // B-operand K chunk (0..1)
+  const int kca = lane >> 5;                  // A-operand K chunk (0..1)
+  const int q = lane / CPR, sl = lane % CPR;
+  const __amdgpu_buffer_rsrc_t rid = DENSE ? res.id : res.is;
+  const __amdgpu_buffer_rsrc_t rv = DENSE ? res.vd : res.vs;
+  const uint32_t vrow = (uint32_t)rb * 64u;
+  const uint32_t xcol = (uint32_t)n0 * 2u;
+  uint32_t xch[NJ];                           // this lane's source chunk of X load j, in bytes
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) xch[j] = 16u * (uint32_t)(sl ^ (4 * ((j * RPL + q) & 3)));
+  const int arow = threadIdx.x >> 2;          // packed-value row this thread stores
+  const int aofs = AOFS + arow * 64 + 16 * ((threadIdx.x & 3) ^ ((arow >> 2) & 3));
+
+  // Indices: lane l < RPW of the wave loads the index of position
+  // wave * RPW + l; X load j of lane l needs the one of position
+  // j * RPL + l / CPR, taken with v_readlane and selects.
+  const uint32_t ipos = (uint32_t)(wave * RPW + (lane % RPW));
+  auto load_idx = [&](int b) -> int {
+    b = min(b, nb - 1);
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(rid, ((uint32_t)(kbase + b) * KPOS + ipos) * 4u, 0, 0);
+  };
+  auto spread_idx = [&](int iw, int (&ci)[NJ]) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      int c = __builtin_amdgcn_readlane(iw, j * RPL);
+#pragma unroll
+      for (int u = 1; u < RPL; ++u) {
+        const int m = -(int)(q == u);
+        c = (c & ~m) | (__builtin_amdgcn_readlane(iw, j * RPL + u) & m);
+      }
+      ci[j] = c;
+    }
+  };
+  auto load_x = [&](const int (&ci)[NJ], uint16_t* xs) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const uint32_t off = ci[j] < 0 ? kOob : __umul24((uint32_t)ci[j], res.ldx_bytes) + xcol + xch[j];
+      load_lds16(res.x, reinterpret_cast<uint8_t*>(xs) + (wave * RPW + j * RPL) * XROW, off);
+    }
+  };
+  auto load_a = [&](int b, PrefillA& st) {
+    b = min(b, nb - 1);
+    const uint32_t blk = (uint32_t)(kbase + b) * (uint32_t)a.rows + vrow;
+    st.v = __builtin_amdgcn_raw_buffer_load_b128(rv, blk * 64u + 16u * threadIdx.x, 0, 0);
+    if constexpr (!DENSE)
+      st.m = __builtin_amdgcn_raw_buffer_load_b32(res.meta, threadIdx.x < 128 ? blk * 8u + 4u * threadIdx.x : kOob,
+                                                  0, 0);
+  };
+  auto store_a = [&](uint16_t* xs, uint32_t* ms, const PrefillA& st) {
+    *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(xs) + aofs) = st.v;
+    if constexpr (!DENSE)
+      if (threadIdx.x < 128) ms[threadIdx.x] = st.m;
+  };
+  // B operand: lane (g, i) reads 4 tokens of position p (p % 4 == i / 4) at
+  // token tok_w + 16 (g % 2) + 4 (i % 4) + 32 j.
+  const uint32_t cb0 = (uint32_t)(tok_w / 8 + 2 * (g & 1) + ((i >> 1) & 1));
+  const uint32_t bsw = (uint32_t)(4 * ((i >> 2) & 3));
+  auto compute = [&](const uint16_t* xt, const uint32_t* ms) {
+    const uint8_t* xb = reinterpret_cast<const uint8_t*>(xt);
+    u32x4 av[4];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int row = 32 * r + (lane & 31);
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        av[2 * r + s] = *reinterpret_cast<const u32x4*>(xb + AOFS + row * 64 + 16 * ((2 * s + kca) ^ ((row >> 2) & 3)));
+    }
+    if constexpr (DENSE) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {               // two K steps of 16 columns
+#pragma unroll
+        for (int j = 0; j < C::NTB; ++j) {
+          const uint8_t* base = xb + 16u * ((cb0 + 4u * j) ^ bsw) + 8u * (i & 1) + (16 * s + 8 * kcb + (i >> 2)) * XROW;
+          const v4i16 b0 = tr_read_b(base);
+          const v4i16 b1 = tr_read_b(base + 4 * XROW);
+          const bf16x8 B = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int r = 0; r < 2; ++r)
+            acc[r][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[2 * r + s]), B,
+                                                                acc[r][j], 0, 0, 0);
+        }
+      }
+    } else {
+      const uint64_t* mt = reinterpret_cast<const uint64_t*>(ms);
+      const uint64_t mv[2] = {mt[lane & 31], mt[32 + (lane & 31)]};
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {               // two K steps of 32 positions
+        int sidx[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) sidx[r] = (int)((mv[r] >> (32 * s + 16 * kca)) & 0xffffull);
+#pragma unroll
+        for (int j = 0; j < C::NTB; ++j) {
+          const uint8_t* base = xb + 16u * ((cb0 + 4u * j) ^ bsw) + 8u * (i & 1) + (32 * s + 8 * kcb + (i >> 2)) * XROW;
+          const v4i16 b0 = tr_read_b(base);
+          const v4i16 b1 = tr_read_b(base + 4 * XROW);
+          const v4i16 b2 = tr_read_b(base + 16 * XROW);
+          const v4i16 b3 = tr_read_b(base + 20 * XROW);
+          const bf16x16 B = __builtin_bit_cast(
+              bf16x16, __builtin_shufflevector(__builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7),
+                                               __builtin_shufflevector(b2, b3, 0, 1, 2, 3, 4, 5, 6, 7), 0, 1, 2, 3,
+                                               4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15));
+#pragma unroll
+          for (int r = 0; r < 2; ++r)
+            acc[r][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(bf16x8, av[2 * r + s]), B,
+                                                                  acc[r][j], sidx[r], 0, 0);
+        }
+      }
+    }
+  };
+
+  __syncthreads();                   // the LDS tiles may still be read by the previous phase
+  // Register sets: packed values of DA blocks (A[b % DA]) and the index
+  // words of blocks bb+2 and bb+3.  At block bb: issue the X rows of bb+1
+  // into the other tile, the indices of bb+3 and the values of bb+DA;
+  // multiply bb; store the values of bb+1; spread the indices of bb+2; wait
+  // for this wave's rows of bb+1; barrier.
+  constexpr int DA = C::DA;
+  PrefillA A[DA];
+  int Iw[2];
+  int CI[NJ];
+  uint16_t* const tile[2] = {xs0, xs1};
+  uint32_t* const mtile[2] = {ms0, ms1};
+  Iw[0] = load_idx(0);
+  Iw[1] = load_idx(1);
+#pragma unroll
+  for (int d = 0; d < DA; ++d) load_a(d, A[d]);
+  spread_idx(Iw[0], CI);
+  load_x(CI, tile[0]);
+  spread_idx(Iw[1], CI);
+  Iw[0] = load_idx(2);
+  store_a(tile[0], mtile[0], A[0]);
+  wait_vm<1>();                      // the X rows of block 0 (only the index load of block 2 is younger)
+  __syncthreads();
+  auto step = [&](auto kc, int bb) {
+    constexpr int k = decltype(kc)::value;
+    if (bb + 1 < nb) load_x(CI, tile[(k + 1) % 2]);   // X(bb+1)
+    Iw[(k + 1) % 2] = load_idx(bb + 3);
+    load_a(bb + DA, A[k % DA]);
+    compute(tile[k % 2], mtile[k % 2]);
+    store_a(tile[(k + 1) % 2], mtile[(k + 1) % 2], A[(k + 1) % DA]);
+    spread_idx(Iw[k % 2], CI);        // indices of bb+2
+    wait_vm<PA>();                    // this wave's X rows of bb+1 are in LDS
+    __syncthreads();
+  };
+  int b = 0;
+  for (; b + 4 <= nb; b += 4) {
+    step(std::integral_constant<int, 0>{}, b);
+    step(std::integral_constant<int, 1>{}, b + 1);
+    step(std::integral_constant<int, 2>{}, b + 2);
+    step(std::integral_constant<int, 3>{}, b + 3);
+  }
+  if (b < nb) step(std::integral_constant<int, 0>{}, b);
+  if (b + 1 < nb) step(std::integral_constant<int, 1>{}, b + 1);
+  if (b + 2 < nb) step(std::integral_constant<int, 2>{}, b + 2);
+}
+
 template <int NT, bool FAST>
 __device__ inline void prefill_body(const SpmmArgs& a, const BufRes& res, uint16_t* xs0, uint16_t* xs1,
                                     uint32_t* ms0, uint32_t* ms1, int t, int rb, int n0,
                                     f32x16 (&acc)[2][PrefillCfg<NT>::NTB]) {
   const TileK tk = tile_k(a, t);
-  prefill_phase<NT, FAST, true>(a, res, xs0, xs1, ms0, ms1, tk.kd0, tk.nbd, rb, n0, acc);
-  prefill_phase<NT, FAST, false>(a, res, xs0, xs1, ms0, ms1, tk.ks0, tk.nbs, rb, n0, acc);
+  if constexpr (NT == 256) {
+    if (a.x_lds) {
+      prefill_phase_lds<NT, true>(a, res, xs0, xs1, ms0, ms1, tk.kd0, tk.nbd, rb, n0, acc);
+      prefill_phase_lds<NT, false>(a, res, xs0, xs1, ms0, ms1, tk.ks0, tk.nbs, rb, n0, acc);
+      return;
+    }
+  }
+  {
+    prefill_phase<NT, FAST, true>(a, res, xs0, xs1, ms0, ms1, tk.kd0, tk.nbd, rb, n0, acc);
+    prefill_phase<NT, FAST, false>(a, res, xs0, xs1, ms0, ms1, tk.ks0, tk.nbs, rb, n0, acc);
+  }
 }
 
 // Persistent launch: gridDim.x = 8 * per_xcd workgroups, workgroup L runs on
@@ -829,8 +1046,12 @@ __device__ inline void prefill_body(const SpmmArgs& a, const BufRes& res, uint16
 template <int NT>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
   using C = PrefillCfg<NT>;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][64 * C::PITCH];
-  __shared__ __attribute__((aligned(16))) uint32_t ms[2][128];
+  __shared__ __attribute__((aligned(16))) uint16_t xs_a[64 * C::PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t xs_b[64 * C::PITCH];
+  __shared__ __attribute__((aligned(16))) uint32_t ms_a[128];
+  __shared__ __attribute__((aligned(16))) uint32_t ms_b[128];
+  uint16_t* const xs[2] = {xs_a, xs_b};   // separate LDS objects: loads into one tile never
+  uint32_t* const ms[2] = {ms_a, ms_b};   // hold up reads of the other
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nrb = a.rows / 64;
@@ -1017,6 +1238,13 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
   a.splits = sh.splits;
   a.n_kunits = sh.n_kunits;
   a.x_vec = hinm::aligned(x_bf16, 16) && (ldx % 8 == 0);
+  {
+    // At 256-token blocks X rows go straight into LDS when they are 16-byte
+    // aligned (the register-staged gather stays selectable for comparison);
+    // at 128-token blocks the register-staged gather measured faster.
+    const char* pp = getenv("HINM_PREFILL_PATH");
+    a.x_lds = a.x_vec && !(pp && strcmp(pp, "staged") == 0);
+  }
   a.y_vec = hinm::aligned(y_bf16, 16) && (ldy % 8 == 0);
   a.n_tiles = p.n_tiles;
   a.out_rows = out_rows;
