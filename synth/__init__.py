@@ -141,3 +141,17 @@ def small(cout: int, cin: int, tile_rows: int, t_s: float, v_s: float, batch: in
           **kw) -> Workload:
     """A small workload of the same distribution, for tests."""
     return draw(f"small_{cout}x{cin}", cout, cin, tile_rows, t_s, v_s, batch, seed, **kw)
+
+
+def gyro_draws(seed: int, rounds: int, n_tiles: int, groups: int, n_clusters: int):
+    """Random draws of the gyro permutation, made by the caller and given to both sides:
+    sample uint8 [rounds][n_tiles][groups] (the position taken out of each 2:4 group) and
+    init int32 [rounds][n_tiles][n_clusters] (distinct groups whose drawn vectors start the centroids)."""
+    rng = np.random.default_rng(seed)
+    sample = rng.integers(0, 4, size=(rounds, n_tiles, groups), dtype=np.uint8)
+    init = np.zeros((rounds, n_tiles, n_clusters), dtype=np.int32)
+    for r in range(rounds):
+        for t in range(n_tiles):
+            if n_clusters:
+                init[r, t] = rng.choice(groups, n_clusters, replace=False)
+    return sample, init

@@ -622,3 +622,159 @@ def test_boundary_search_tiles_stop_rule_brute_force():
         assert all(tr[k][1] >= tr[k - 1][1] for k in range(1, len(tr) - (1 if stopped else 0)))
         vb = tr[-2][0] if stopped else tr[-1][0]
         assert vs[t] == oh.plan(32, 64, 32, 0.6, vb).n_pruned / 64
+
+
+# ---------------------------------------------------------------------------
+# In-tile input-channel gyro permutation (oracle/gyro.py)
+# ---------------------------------------------------------------------------
+import itertools
+
+import oracle.gyro as og
+
+
+def test_hungarian_brute_force_and_library():
+    rng = np.random.default_rng(70)
+    for n in range(1, 7):
+        for _ in range(5):
+            c = rng.random((n, n))
+            col = og.hungarian(c)
+            assert sorted(col.tolist()) == list(range(n))
+            best = min(sum(c[i, pi[i]] for i in range(n)) for pi in itertools.permutations(range(n)))
+            assert abs(sum(c[i, col[i]] for i in range(n)) - best) <= 1e-12
+    from scipy.optimize import linear_sum_assignment
+    for n in (17, 40):
+        c = rng.random((n, n))
+        r, k = linear_sum_assignment(c)
+        col = og.hungarian(c)
+        assert abs(c[np.arange(n), col].sum() - c[r, k].sum()) <= 1e-9
+
+
+def test_hungarian_ties_lowest_column():
+    # all costs equal: every assignment is optimal; the rule gives row i -> column i
+    assert og.hungarian(np.ones((4, 4))).tolist() == [0, 1, 2, 3]
+
+
+def test_balanced_kmeans_recovers_blobs():
+    rng = np.random.default_rng(71)
+    n, size, dim = 5, 6, 8
+    centers = rng.normal(0, 100, (n, dim))
+    pts = np.concatenate([centers[k] + rng.normal(0, 0.1, (size, dim)) for k in range(n)])
+    perm = rng.permutation(n * size)
+    pts = pts[perm]
+    truth = (perm // size)
+    init = np.array([np.nonzero(truth == k)[0][0] for k in range(n)])
+    caps = og.capacities(n * size, n)
+    label = og.balanced_kmeans(pts, init, 4, caps)
+    assert np.bincount(label, minlength=n).tolist() == caps.tolist()
+    assert np.array_equal(label, truth)
+
+
+def test_balanced_kmeans_capacities_hold():
+    rng = np.random.default_rng(72)
+    for g, s in ((10, 3), (23, 4), (7, 7), (9, 1)):
+        pts = rng.random((g, 5))
+        n = og.n_clusters(g, s)
+        caps = og.capacities(g, n)
+        assert caps.sum() == g and caps.max() - caps.min() <= 1
+        label = og.balanced_kmeans(pts, rng.choice(g, n, replace=False), 3, caps)
+        assert np.bincount(label, minlength=n).tolist() == caps.tolist()
+
+
+def test_pair_cost_is_what_the_24_selection_drops():
+    """The group cost equals the importance the pack's own 2:4 selection leaves out (select24 is an
+    argsort-based path, not pair_cost)."""
+    rng = np.random.default_rng(73)
+    p = oh.plan(64, 96, 32, 0.75, 0.5)
+    d = rng.random((64, 96)).astype(np.float32)
+    perm = np.stack([rng.permutation(96) for _ in range(2)])
+    reg = oh.regions(oh.vector_scores(d, p), p)
+    _, idx_s = oh.index_lists(reg, perm, p)
+    sel = oh.select24(d, idx_s, p)
+    for t in range(2):
+        rows = slice(32 * t, 32 * t + 32)
+        cols = idx_s[t, :p.n_24].reshape(p.groups, 4)
+        a = d[rows][:, cols.reshape(-1)].reshape(32, p.groups, 4).astype(np.float64)
+        kept = np.take_along_axis(a, sel[rows], axis=-1).sum(axis=-1)
+        dropped = (a.sum(axis=-1) - kept).sum(axis=0)
+        assert np.allclose(og.group_costs(d[rows], cols), dropped, rtol=1e-12, atol=1e-12)
+
+
+def _gyro_case(seed, cout=128, cin=96, R=32, t=0.75, v=0.5, rounds=3, s=3, iters=2):
+    rng = np.random.default_rng(seed)
+    d = (rng.random((cout, cin)) ** 3).astype(np.float32)
+    p = oh.plan(cout, cin, R, t, v)
+    perm = np.stack([rng.permutation(cin) for _ in range(p.n_tiles)])
+    n = og.n_clusters(p.groups, s)
+    sample, init = synth.gyro_draws(seed, rounds, p.n_tiles, p.groups, n)
+    new, trace = og.gyro_permutation(d, perm, p, rounds, s, iters, sample, init)
+    return d, p, perm, new, trace
+
+
+def test_gyro_rounds_never_raise_the_cost_and_keep_the_regions():
+    for seed in range(4):
+        d, p, perm, new, trace = _gyro_case(80 + seed)
+        assert np.all(np.diff(trace, axis=0) <= 0)
+        assert np.any(trace[-1] < trace[0])
+        reg = oh.regions(oh.vector_scores(d, p), p)
+        for t in range(p.n_tiles):
+            assert sorted(new[t].tolist()) == list(range(p.cin))
+            fixed = reg[t][perm[t]] != oh.TWO_FOUR
+            assert np.array_equal(new[t][fixed], perm[t][fixed])           # dense and pruned stay put
+            assert sorted(new[t][~fixed].tolist()) == sorted(perm[t][~fixed].tolist())
+
+
+def test_gyro_trace_is_the_retained_importance_gain():
+    """R_24 after minus R_24 before equals the pruning cost removed (retained_importance is the boundary
+    search's objective, computed through the pack's select24)."""
+    d, p, perm, new, trace = _gyro_case(85)
+    gain = oh.retained_importance(d, new, p) - oh.retained_importance(d, perm, p)
+    assert gain >= 0
+    assert abs(gain - (trace[0].sum() - trace[-1].sum())) <= 1e-9 * max(1.0, trace[0].sum())
+
+
+def test_gyro_one_cluster_round_is_the_brute_force_optimum():
+    """One cluster holding every group: the round's cost is the least over all ways of putting the drawn
+    columns back (brute force over G! assignments)."""
+    rng = np.random.default_rng(86)
+    d_tile = (rng.random((16, 20)) ** 2).astype(np.float32)
+    cols = rng.permutation(20)[:16].reshape(4, 4)
+    sample = rng.integers(0, 4, 4)
+    new = og.gyro_round(d_tile, cols, sample, np.array([0]), cluster_size=8, iters=2)
+    drawn = cols[np.arange(4), sample]
+    best = np.inf
+    for pi in itertools.permutations(range(4)):
+        c = cols.copy()
+        for j in range(4):
+            c[j, sample[j]] = drawn[pi[j]]
+        best = min(best, og.total_cost(og.group_costs(d_tile, c)))
+    assert abs(og.total_cost(og.group_costs(d_tile, new)) - best) <= 1e-12
+
+
+def test_gyro_no_24_region_is_a_no_op():
+    rng = np.random.default_rng(87)
+    d = rng.random((64, 64)).astype(np.float32)
+    p = oh.plan(64, 64, 32, 0.75, 0.75)
+    perm = np.stack([rng.permutation(64) for _ in range(2)])
+    new, trace = og.gyro_permutation(d, perm, p, 2, 4, 2, np.zeros((2, 2, 0), np.uint8), np.zeros((2, 2, 0), np.int32))
+    assert np.array_equal(new, perm) and not trace.any()
+
+
+def test_mutation_gyro_largest_two_is_caught(monkeypatch):
+    """A cost that drops the two largest instead of the two smallest fails the select24 pin."""
+    def wrong(vals):
+        s = np.sort(np.asarray(vals, dtype=np.float32), axis=-1)
+        per_row = s[..., 2].astype(np.float64) + s[..., 3].astype(np.float64)
+        acc = np.zeros(per_row.shape[:-1])
+        for r in range(per_row.shape[-1]):
+            acc = acc + per_row[..., r]
+        return acc
+    monkeypatch.setattr(og, "pair_cost", wrong)
+    with pytest.raises(AssertionError):
+        test_pair_cost_is_what_the_24_selection_drops()
+
+
+def test_mutation_gyro_maximising_assignment_is_caught(monkeypatch):
+    orig = og.hungarian
+    monkeypatch.setattr(og, "hungarian", lambda c: orig(-np.asarray(c)))
+    with pytest.raises(AssertionError):
+        test_gyro_one_cluster_round_is_the_brute_force_optimum()
