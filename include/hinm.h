@@ -325,6 +325,46 @@ int hinm_boundary_search_tiles(int64_t cout, int64_t cin, int32_t tile_rows, dou
                                const float* importance, int64_t ldi, const int32_t* perm, void* workspace,
                                size_t workspace_bytes, double* v_s_tiles, int32_t* points_tiles, void* stream);
 
+/* In-tile input-channel gyro permutation (FlexHiNM-GP notes, key design 2:
+ * channels are reordered so that important weights land where the structure
+ * keeps them; the in-tile input step is rounds of drawing vectors from each
+ * tile, a balanced K-means of them and a Hungarian assignment on a pruning
+ * cost matrix).  It rewrites perm so that the 2:4 groups of plan's regions
+ * drop less importance; the dense and pruned sets and their positions in
+ * perm do not change.  One round, per tile, with G = plan->groups 2:4 groups
+ * (group q = entries 4q..4q+3 of the tile's 2:4 list in perm order):
+ *   1. the column at position sample[r][t][q] (0..3) of every group q is
+ *      taken out, leaving a hole;
+ *   2. its importance vector (float64 over the tile's rows) is clustered
+ *      into N = ceil(G / cluster_size) clusters of sizes floor(G / N) or one
+ *      more (the first G mod N clusters), centroids starting at the vectors
+ *      of groups init[r][t][0..N-1] (distinct); each of kmeans_iters
+ *      assignment steps gives every vector the cluster of the first
+ *      (squared distance, group, cluster) triple in increasing order whose
+ *      cluster has room, and centroids move to their members' mean between
+ *      steps;
+ *   3. inside every cluster the drawn columns go back into its holes by a
+ *      minimum-cost assignment (Hungarian algorithm, lowest column index on
+ *      equal reduced costs), the cost of a group being its pruning cost: per
+ *      row the two smallest of its four importances, over the tile's rows.
+ * No round raises a tile's pruning cost (putting every column back is one
+ * assignment).  Distances, centroids and costs are float64 sums in a fixed
+ * order, so the result is a function of the inputs alone.
+ * importance (device) fp32 [cout][ldi] as for hinm_pack; perm (device) int32
+ * [n_tiles][cin], in/out, each row a permutation of 0..cin-1 (checked on the
+ * device, HINM_EPERM).  sample (host) uint8 [rounds][n_tiles][G]; init
+ * (host) int32 [rounds][n_tiles][N]; both may be NULL when rounds == 0 or
+ * G == 0.  cost_trace (host) float64 [rounds + 1][n_tiles] or NULL: the
+ * pruning cost of every tile before the first round and after each round.
+ * workspace (device, 256-byte aligned) of hinm_gyro_workspace_bytes.
+ * Synchronous on `stream`.  Errors: HINM_EINVAL (counts, sample or init out
+ * of range), HINM_ESHAPE, HINM_EALIGN, HINM_EPERM, HINM_EIMPORTANCE,
+ * HINM_EWORKSPACE, HINM_EHIP. */
+int hinm_gyro_workspace_bytes(const hinm_plan_t* plan, int32_t cluster_size, size_t* bytes);
+int hinm_gyro_permute(const hinm_plan_t* plan, const float* importance, int64_t ldi, int32_t* perm, int32_t rounds,
+                      int32_t cluster_size, int32_t kmeans_iters, const uint8_t* sample, const int32_t* init,
+                      double* cost_trace, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* hinm_status_str(int status);
 

@@ -15,6 +15,7 @@ import dataclasses
 import os
 from typing import Optional
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -29,7 +30,8 @@ EXPORTS = ("hinm_abi_version", "hinm_plan", "hinm_pack_workspace_bytes", "hinm_p
            "hinm_spmm_workspace_bytes", "hinm_spmm", "hinm_spmm_rows", "hinm_translate_indices",
            "hinm_boundary_workspace_bytes", "hinm_boundary_search", "hinm_plan_tiles",
            "hinm_pack_tiles_workspace_bytes", "hinm_pack_tiles", "hinm_spmm_tiles_workspace_bytes",
-           "hinm_spmm_tiles", "hinm_boundary_search_tiles", "hinm_status_str", "hinm_last_error")
+           "hinm_spmm_tiles", "hinm_boundary_search_tiles", "hinm_gyro_workspace_bytes", "hinm_gyro_permute",
+           "hinm_status_str", "hinm_last_error")
 
 
 class HinmError(RuntimeError):
@@ -107,6 +109,9 @@ def library() -> ctypes.CDLL:
             "hinm_boundary_search": ([I64, I64, I32, D, D, VP, I64, VP, VP, S, ctypes.POINTER(D),
                                       ctypes.POINTER(D), ctypes.POINTER(D), I32, ctypes.POINTER(I32), VP],
                                      ctypes.c_int),
+            "hinm_gyro_workspace_bytes": ([P, I32, ctypes.POINTER(S)], ctypes.c_int),
+            "hinm_gyro_permute": ([P, VP, I64, VP, I32, I32, I32, VP, VP, ctypes.POINTER(D), VP, S, VP],
+                                  ctypes.c_int),
             "hinm_status_str": ([ctypes.c_int], ctypes.c_char_p),
             "hinm_last_error": ([], ctypes.c_char_p),
         }
@@ -474,6 +479,39 @@ def boundary_search(importance: torch.Tensor, perm: Optional[torch.Tensor], tile
                                         ctypes.byref(tl), _stream_ptr(dev)))
     k = min(tl.value, trace_cap)
     return v.value, [(tv[i], tr[i]) for i in range(k)]
+
+
+def gyro_permute(importance: torch.Tensor, perm: torch.Tensor, tile_rows: int, t_s: float, v_s: float,
+                 rounds: int, cluster_size: int, kmeans_iters: int, sample, init):
+    """In-tile input-channel gyro permutation (hinm_gyro_permute), synchronous.
+
+    importance fp32 [cout, cin] and perm int32 [n_tiles, cin] on the device; sample uint8
+    [rounds, n_tiles, groups] and init int32 [rounds, n_tiles, n_clusters] (numpy, host).
+    Returns (new perm tensor, cost trace float64 numpy [rounds + 1, n_tiles]); perm is not modified.
+    """
+    if importance.dtype != torch.float32 or importance.dim() != 2 or importance.stride(1) != 1:
+        raise ValueError("importance must be float32 [cout, cin] with unit column stride")
+    cout, cin = importance.shape
+    dev = importance.device
+    p = plan(cout, cin, tile_rows, t_s, v_s)
+    if perm.dtype != torch.int32 or perm.shape != (p.n_tiles, cin) or perm.device != dev:
+        raise ValueError(f"perm must be int32 [{p.n_tiles}, {cin}] on the importance's device")
+    out = perm.clone().contiguous()
+    sample = np.ascontiguousarray(sample, dtype=np.uint8)
+    init = np.ascontiguousarray(init, dtype=np.int32)
+    lib = library()
+    n = ctypes.c_size_t()
+    _check(lib.hinm_gyro_workspace_bytes(ctypes.byref(p.raw), int(cluster_size), ctypes.byref(n)))
+    ws = torch.empty(max(1, n.value), dtype=torch.uint8, device=dev)
+    trace = np.zeros((rounds + 1, p.n_tiles), dtype=np.float64)
+    with torch.cuda.device(dev):
+        _check(lib.hinm_gyro_permute(ctypes.byref(p.raw), importance.data_ptr(), importance.stride(0),
+                                     out.data_ptr(), int(rounds), int(cluster_size), int(kmeans_iters),
+                                     sample.ctypes.data if sample.size else None,
+                                     init.ctypes.data if init.size else None,
+                                     trace.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), ws.data_ptr(),
+                                     ws.numel(), _stream_ptr(dev)))
+    return out, trace
 
 
 def boundary_search_tiles(importance: torch.Tensor, perm: Optional[torch.Tensor], tile_rows: int, t_s: float,

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhinm.so")
-SOURCES = ("hinm_plan.cpp", "hinm_pack.hip", "hinm_spmm.hip")
+SOURCES = ("hinm_plan.cpp", "hinm_pack.hip", "hinm_spmm.hip", "hinm_gyro.hip")
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are kept off for every kernel of this library.  MFMA
 # accumulators stay in ordinary VGPRs: with one wave per SIMD the compiler

@@ -53,4 +53,15 @@ int ensure_device();
 
 }  // namespace hinm
 
+#ifdef __HIP__
+#include <hip/hip_runtime.h>
+namespace hinm {
+// The perm and importance checks, scores, regions and index lists of a pack
+// (its first stages) into caller buffers; ws is laid out as the pack
+// workspace (hinm_pack_workspace_bytes).  Synchronous.
+int region_lists(const hinm_plan_t& p, const float* importance, int64_t ldi, const int32_t* perm, int32_t* idx_dense,
+                 int32_t* idx_24, void* ws, hipStream_t stream);
+}  // namespace hinm
+#endif
+
 #endif  // HINM_INTERNAL_H_

@@ -411,6 +411,42 @@ static int pack_core(const PackShape& p, const int32_t* tiles, const void* w_bf1
   return HINM_OK;
 }
 
+namespace hinm {
+
+// The checks, scores, regions and index lists of a pack (its first stages)
+// into caller buffers, for entry points that need the lists without the
+// values.  ws is laid out as the pack workspace; synchronous.
+int region_lists(const hinm_plan_t& p, const float* importance, int64_t ldi, const int32_t* perm, int32_t* idx_dense,
+                 int32_t* idx_24, void* ws_, hipStream_t stream) {
+  const int T = p.n_tiles, cin = p.cin, R = p.tile_rows;
+  char* ws = static_cast<char*>(ws_);
+  int* flag = reinterpret_cast<int*>(ws);
+  double* scores = reinterpret_cast<double*>(ws + 256);
+  uint8_t* reg = reinterpret_cast<uint8_t*>(ws + 256 + (size_t)T * cin * 8);
+  hipLaunchKernelGGL(zero_flag_kernel, dim3(1), dim3(64), 0, stream, flag);
+  if (perm)
+    hipLaunchKernelGGL(check_perm_kernel, dim3(T), dim3(1024), ((cin + 31) / 32) * 4, stream, perm, cin, flag);
+  hipLaunchKernelGGL(scores_kernel, dim3((cin + 255) / 256, T), dim3(256), 0, stream, importance, ldi, cin, R,
+                     scores, flag);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "region lists launch");
+  int hflag = 0;
+  e = hipMemcpyAsync(&hflag, flag, sizeof(int), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "region lists");
+  if (hflag & kFlagPerm) return fail(HINM_EPERM, "a perm row is not a permutation of 0..%d", cin - 1);
+  if (hflag & kFlagImportance) return fail(HINM_EIMPORTANCE, "importance has a negative or non-finite entry");
+  hipLaunchKernelGGL(regions_kernel, dim3((cin + 255) / 256, T), dim3(256), 0, stream, scores, cin, p.n_dense,
+                     p.n_24, reg, nullptr);
+  hipLaunchKernelGGL(compact_kernel, dim3(T), dim3(1024), 0, stream, perm, reg, cin, p.n_dense_pad, p.n_24_pad,
+                     idx_dense, idx_24, nullptr);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "region lists launch");
+  return HINM_OK;
+}
+
+}  // namespace hinm
+
 extern "C" int hinm_pack(const hinm_plan_t* plan, const void* w_bf16, int64_t ldw, const float* importance,
                          int64_t ldi, const int32_t* perm, hinm_packed_t* out, void* workspace,
                          size_t workspace_bytes, void* stream) {

@@ -255,3 +255,45 @@ def test_tiles_host_errors(lib):
     out = hinm.TPackedT(tp.raw, None, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20)
     assert lib.hinm_pack_tiles(ctypes.byref(tp.raw), 1 << 20, 512, 1 << 20, 512, None, ctypes.byref(out),
                                1 << 20, 1 << 24, None) == 1
+
+
+def test_gyro_host_errors(lib):
+    p = hinm.plan(128, 256, 32, 0.75, 0.5)          # 32 groups per tile, 4 tiles
+    n = ctypes.c_size_t()
+    assert lib.hinm_gyro_workspace_bytes(ctypes.byref(p.raw), 0, ctypes.byref(n)) == 1
+    assert lib.hinm_gyro_workspace_bytes(ctypes.byref(p.raw), 8, ctypes.byref(n)) == 0
+    G, T, N, rounds = p.groups, p.n_tiles, 4, 2           # N = ceil(32 / 8)
+    assert G == 32 and T == 4
+    sample = np.zeros((rounds, T, G), np.uint8)
+    init = np.tile(np.arange(N, dtype=np.int32), (rounds, T, 1))
+    trace = (ctypes.c_double * ((rounds + 1) * T))()
+
+    def call(**kw):
+        s = kw.get("sample", sample)
+        i = kw.get("init", init)
+        return lib.hinm_gyro_permute(ctypes.byref(p.raw), kw.get("imp", 1 << 20), kw.get("ldi", 256),
+                                     kw.get("perm", 1 << 21), kw.get("rounds", rounds), kw.get("cs", 8),
+                                     kw.get("iters", 2), s.ctypes.data if s is not None else None,
+                                     i.ctypes.data if i is not None else None, trace, kw.get("ws", 1 << 22),
+                                     kw.get("wsb", n.value), None)
+    assert call(ws=None) == 6                        # the valid draws pass every check before the workspace one
+    assert call(imp=None) == 1
+    assert call(perm=None) == 1
+    assert call(rounds=-1) == 1
+    assert call(cs=0) == 1
+    assert call(iters=0) == 1
+    assert call(sample=None) == 1
+    bad = sample.copy()
+    bad[1, 2, 5] = 4
+    assert call(sample=bad) == 1                     # a position outside 0..3
+    dup = init.copy()
+    dup[0, 1, 2] = dup[0, 1, 0]
+    assert call(init=dup) == 1                       # centroids must start at distinct groups
+    oob = init.copy()
+    oob[1, 3, 1] = G
+    assert call(init=oob) == 1
+    assert call(ldi=255) == 2
+    assert call(imp=(1 << 20) + 2) == 5
+    assert call(ws=None) == 6
+    assert call(wsb=n.value - 1) == 6
+    assert call(ws=(1 << 22) + 16) == 5
