@@ -387,6 +387,40 @@ def main():
         "useful_tflops_batch_2048": None}
     next_tiles["useful_tflops_batch_2048"] = round(useful_t / (next_tiles["spmm_tiles_batch_2048_ms"] * 1e-3) / 1e12, 2)
 
+    # NEXT row: the in-tile input-channel gyro permutation on this weight (importance |W|, the bench's
+    # regions), wall time per round; the oracle's round on a sample of tiles beside it
+    g_rounds, g_cs, g_it = 2, 32, 5
+    n_cl = -(-p.groups // g_cs)
+    g_sample, g_init = synth.gyro_draws(11, g_rounds, p.n_tiles, p.groups, n_cl)
+    hinm.gyro_permute(igpu, pgpu, p.tile_rows, p.t_s, p.v_s, 0, g_cs, g_it, g_sample[:0], g_init[:0])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g_perm, g_trace = hinm.gyro_permute(igpu, pgpu, p.tile_rows, p.t_s, p.v_s, g_rounds, g_cs, g_it, g_sample, g_init)
+    torch.cuda.synchronize()
+    g_s = time.perf_counter() - t0
+    tot24 = float(w.importance.numpy().astype("float64").sum())   # context for the cost: all importance
+    next_gyro = {"what": f"hinm_gyro_permute on down_proj 4096x11008, importance |W|, t_s 0.75, v_s 0.55: "
+                         f"{p.groups} 2:4 groups per tile, {g_rounds} rounds, clusters of {g_cs} ({n_cl} per tile), "
+                         f"{g_it} K-means steps; wall time (synchronous, includes the region lists)",
+                 "s_total": round(g_s, 3), "s_per_round": round(g_s / g_rounds, 3),
+                 "pruning_cost_before": round(float(g_trace[0].sum()), 3),
+                 "pruning_cost_after": round(float(g_trace[-1].sum()), 3),
+                 "cost_removed_frac": round(float(1 - g_trace[-1].sum() / g_trace[0].sum()), 5),
+                 "total_importance": round(tot24, 3)}
+    if not args.no_cpu:
+        import oracle.gyro as og
+        import oracle.hinm as oh
+        dd = w.importance.numpy()
+        op = oh.plan(w.cout, w.cin, w.tile_rows, w.t_s, w.v_s)
+        reg = oh.regions(oh.vector_scores(dd, op), op)
+        _, idx_s = oh.index_lists(reg, w.perm.numpy().astype("int64"), op)
+        t0 = time.perf_counter()
+        for t in range(2):
+            og.gyro_round(dd[t * 64:(t + 1) * 64], idx_s[t, :op.n_24].reshape(op.groups, 4).astype("int64"),
+                          g_sample[0, t].astype("int64"), g_init[0, t].astype("int64"), g_cs, g_it)
+        next_gyro["oracle_s_per_round_all_tiles"] = round((time.perf_counter() - t0) / 2 * p.n_tiles, 2)
+        next_gyro["oracle_sample"] = "one round on tiles 0 and 1, scaled to all tiles"
+
     dense = None
     if not args.no_dense:
         dense_ms = time_dense(torch, wgpu, x, max(10, args.steps // 2), 3)
@@ -437,6 +471,7 @@ def main():
         "next_output_permutation": next_rows,
         "next_boundary_search": next_bs,
         "next_per_tile_v_s": next_tiles,
+        "next_gyro_permutation": next_gyro,
         "dense_comparator": dense,
         "cpu_baseline": cpu,
     }

@@ -15,7 +15,9 @@
 #include <algorithm>
 #include <cmath>
 #include <limits>
+#include <functional>
 #include <numeric>
+#include <thread>
 #include <vector>
 #include <stdint.h>
 #include <string.h>
@@ -206,23 +208,67 @@ void hungarian(const double* a, int n, int* col) {
 }
 
 // Every point to the cluster of the first (distance, point, cluster) triple
-// in increasing order that still has room.
+// in increasing order that still has room.  Scanning the sorted G x N
+// triples is done with a heap holding, for every unassigned point, its
+// smallest triple not yet looked at: the heap's minimum is then always the
+// next triple of the full scan that concerns an unassigned point, so the
+// decisions are the same.
 void balanced_assign(const double* dist, int G, int N, const std::vector<int>& caps, int* label) {
-  std::vector<int64_t> e((size_t)G * N);
-  std::iota(e.begin(), e.end(), (int64_t)0);
-  std::sort(e.begin(), e.end(), [&](int64_t x, int64_t y) {
-    if (dist[x] != dist[y]) return dist[x] < dist[y];
-    return x < y;   // x = q N + k: point first, then cluster
-  });
+  struct Key {
+    double d;
+    int q, k;
+    bool operator>(const Key& o) const {
+      if (d != o.d) return d > o.d;
+      if (q != o.q) return q > o.q;
+      return k > o.k;
+    }
+  };
+  std::vector<int> order((size_t)G * N);        // clusters of each point by (distance, cluster)
+  std::vector<int> next(G, 0);
+  for (int q = 0; q < G; ++q) {
+    int* o = order.data() + (size_t)q * N;
+    const double* dq = dist + (size_t)q * N;
+    std::iota(o, o + N, 0);
+    std::sort(o, o + N, [&](int a, int b) { return dq[a] != dq[b] ? dq[a] < dq[b] : a < b; });
+  }
+  std::vector<Key> heap;
+  heap.reserve(G);
+  for (int q = 0; q < G; ++q) {
+    const int k = order[(size_t)q * N];
+    heap.push_back({dist[(size_t)q * N + k], q, k});
+  }
+  std::make_heap(heap.begin(), heap.end(), std::greater<Key>());
   std::vector<int> room(caps);
   for (int q = 0; q < G; ++q) label[q] = -1;
-  for (int64_t x : e) {
-    const int q = (int)(x / N), k = (int)(x % N);
-    if (label[q] < 0 && room[k] > 0) {
-      label[q] = k;
-      --room[k];
+  while (!heap.empty()) {
+    std::pop_heap(heap.begin(), heap.end(), std::greater<Key>());
+    const Key top = heap.back();
+    heap.pop_back();
+    if (room[top.k] > 0) {
+      label[top.q] = top.k;
+      --room[top.k];
+    } else if (++next[top.q] < N) {
+      const int k = order[(size_t)top.q * N + next[top.q]];
+      heap.push_back({dist[(size_t)top.q * N + k], top.q, k});
+      std::push_heap(heap.begin(), heap.end(), std::greater<Key>());
     }
   }
+}
+
+// f(t) for t in [0, T) on up to 16 host threads.
+template <class F>
+void for_tiles(int T, F f) {
+  const int nt = std::max(1, std::min<int>({T, 16, (int)std::thread::hardware_concurrency()}));
+  if (nt <= 1) {
+    for (int t = 0; t < T; ++t) f(t);
+    return;
+  }
+  std::vector<std::thread> th;
+  for (int w = 0; w < nt; ++w)
+    th.emplace_back([&, w] {
+      for (int t = w; t < T; t += nt) f(t);
+    });
+  for (auto& x : th) x.join();
 }
 
 struct GyroShape {
@@ -392,7 +438,6 @@ extern "C" int hinm_gyro_permute(const hinm_plan_t* plan, const float* importanc
   std::vector<int32_t> drawn((size_t)T * G), label((size_t)T * G), memb((size_t)T * G), moff((size_t)T * (N + 1));
   std::vector<int64_t> coff((size_t)T * (N + 1));
   std::vector<double> dist((size_t)T * G * N), cost((size_t)T * N * s.cap_max * s.cap_max);
-  std::vector<int> col_of(s.cap_max);
   for (int r = 0; r < rounds; ++r) {
     // 1. one drawn column per group
     for (int t = 0; t < T; ++t)
@@ -415,7 +460,9 @@ extern "C" int hinm_gyro_permute(const hinm_plan_t* plan, const float* importanc
       e = hipMemcpyAsync(dist.data(), d_dist, dist.size() * 8, hipMemcpyDeviceToHost, stream);
       if (e == hipSuccess) e = hipStreamSynchronize(stream);
       if (e != hipSuccess) return hip_fail(e, "gyro distances");
-      for (int t = 0; t < T; ++t) balanced_assign(dist.data() + (size_t)t * G * N, G, N, caps, label.data() + (size_t)t * G);
+      for_tiles(T, [&](int t) {
+        balanced_assign(dist.data() + (size_t)t * G * N, G, N, caps, label.data() + (size_t)t * G);
+      });
       if (it + 1 < kmeans_iters) {
         e = hipMemcpyAsync(d_label, label.data(), label.size() * 4, hipMemcpyHostToDevice, stream);
         if (e != hipSuccess) return hip_fail(e, "gyro upload");
@@ -448,9 +495,10 @@ extern "C" int hinm_gyro_permute(const hinm_plan_t* plan, const float* importanc
     if (e == hipSuccess) e = hipMemcpyAsync(cost.data(), d_cost, cost.size() * 8, hipMemcpyDeviceToHost, stream);
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return hip_fail(e, "gyro costs");
-    for (int t = 0; t < T; ++t) {
+    for_tiles(T, [&](int t) {
       const int32_t* mo = moff.data() + (size_t)t * (N + 1);
       const int64_t* co = coff.data() + (size_t)t * (N + 1);
+      std::vector<int> col_of(s.cap_max);
       for (int k = 0; k < N; ++k) {
         const int m = mo[k + 1] - mo[k];
         const int32_t* mem = memb.data() + (size_t)t * G + mo[k];
@@ -463,7 +511,7 @@ extern "C" int hinm_gyro_permute(const hinm_plan_t* plan, const float* importanc
           gcost[tqj] = c[(size_t)i * m + j];
         }
       }
-    }
+    });
     e = hipMemcpyAsync(d_cols, cols.data(), cols.size() * 4, hipMemcpyHostToDevice, stream);
     if (e != hipSuccess) return hip_fail(e, "gyro upload");
     if (cost_trace) sum_costs(cost_trace + (size_t)(r + 1) * T);
