@@ -90,3 +90,13 @@ def test_gyro_rejects_a_bad_perm():
         hinm.gyro_permute(torch.from_numpy(d).to(DEV), torch.from_numpy(perm).to(DEV), 32, 0.75, 0.5, 1, 4, 2,
                           sample, init)
     assert e.value.name == "HINM_EPERM"
+
+
+def test_gyro_full_width_tiles_match_oracle():
+    """Two tiles of the down_proj width (cin 11008, 1101 groups per tile, clusters of 32): bit-exact."""
+    d, p, perm = case(128, 11008, 64, 0.75, 0.55, seed=12, power=1)
+    got, tr, want, tr_ref = run_both(d, p, perm, 1, 32, 3, seed=12)
+    assert p.groups == 1101
+    assert np.array_equal(got, want)
+    assert np.array_equal(tr, tr_ref)
+    assert np.all(tr[1] < tr[0])
