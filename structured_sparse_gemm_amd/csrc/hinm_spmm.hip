@@ -376,11 +376,14 @@ struct BufRes {
 // Decode kernel with split K and specialised waves (batch <= 64, tile_rows %
 // 64 == 0).  Workgroup = 64 rows of one tile x NTOK tokens x one K range;
 // waves 0-3 own 16 rows each, waves 4-5 gather X.  The index -> X-row chain
-// is the latency-critical part, so the gather waves issue it first; once
-// their X loads are on their way (one barrier), the four row waves put every
-// packed-value load of their K range in flight at once.  The two roles sit
-// in different waves, so the X rows never wait behind the packed values in
-// a wave's in-order load queue.
+// is the latency-critical part, so the gather waves issue it first and the
+// row waves send only a few packed-value loads ahead of it; once the X loads
+// are on their way (one barrier) the row waves keep a fixed number of
+// blocks in flight ahead of their multiplies.  The two roles sit in
+// different waves, so the X rows never wait behind the packed values in a
+// wave's in-order load queue.  A K range longer than one LDS round is
+// processed in rounds, each role issuing the next round's loads as soon as
+// its registers are free.
 //
 // Every block, dense or 2:4, takes 64 LDS positions and one
 // v_smfmac_f32_16x16x64_bf16: a dense block's 32 columns sit at positions
@@ -392,6 +395,21 @@ struct BufRes {
 // alternate between two accumulators so consecutive SMFMACs do not wait on
 // each other.
 // ---------------------------------------------------------------------------
+// LDS layout of the gathered X rows in the split decode kernel: position p
+// holds its NB = NTOK/16 groups of 16 tokens as 32-byte granules, granule g
+// at granule index xs_gran<NB>(p, g) (a bijection on every 64 positions).
+// One ds_read_b64_tr_b16 of a B operand reads granule nb of the 16
+// positions 8*kc + q + i (kc 0..3, i 0..3, q 0 or 4, plus 32 for the upper
+// half); in the plain layout those land on half of the 64 banks (a quarter
+// at NB = 4), so each half-wave took 2 to 4 passes.  The swizzle spreads
+// each half-wave over all 64 banks.
+template <int NB>
+__device__ inline int xs_gran(int p, int g) {
+  if constexpr (NB == 1) return p ^ (((p >> 3) & 1) << 2);
+  else if constexpr (NB == 2) return 2 * p + (g ^ ((p >> 3) & 1));
+  else return 4 * p + (g ^ (((p >> 1) & 1) | (((p >> 3) & 1) << 1)));
+}
+
 template <int NTOK, int MAXB, bool FAST>
 __global__ __launch_bounds__(384) void decode5_kernel(SpmmArgs a, int splits, int n_tb, float* __restrict__ part,
                                                       unsigned* __restrict__ counters) {
@@ -400,6 +418,8 @@ __global__ __launch_bounds__(384) void decode5_kernel(SpmmArgs a, int splits, in
   constexpr int GT = 128;                      // gather threads
   constexpr int MAXCH = MAXP * CPR / GT;       // X chunks per gather thread per round
   constexpr int NB = NTOK / 16;
+  constexpr int DPF = MAXB < 8 ? MAXB : 8;   // packed-value blocks in flight ahead of the multiplies
+  constexpr int P0 = DPF < 4 ? DPF : 4;       // of which issued before the first X gathers
   __shared__ __attribute__((aligned(16))) uint16_t xs[MAXP * NTOK];
   __shared__ int s_last;
 
@@ -438,27 +458,55 @@ __global__ __launch_bounds__(384) void decode5_kernel(SpmmArgs a, int splits, in
   const int64_t grow_base = (int64_t)t * a.rows + rb * 64;
   int64_t yrow[OPT > 4 ? OPT : 4];
   if (threadIdx.x < 256) {
-    if (splits == 1) {
-      for (int e = 0; e < 4; ++e) yrow[e] = y_row(a, grow0 + e);
-    } else {
-      for (int k = 0; k < OPT; ++k) yrow[k] = y_row(a, grow_base + (threadIdx.x + 256 * k) / NTOK);
+    constexpr int NR = OPT > 4 ? OPT : 4;
+    const int nr = splits == 1 ? 4 : OPT;
+    for (int k = 0; k < NR; ++k) yrow[k] = splits == 1 ? grow0 + k : grow_base + (threadIdx.x + 256 * k) / NTOK;
+    if (a.out_rows) {
+      // all the row-map loads first, then one wait
+      int32_t d[NR];
+#pragma unroll
+      for (int k = 0; k < NR; ++k) d[k] = a.out_rows[k < nr ? yrow[k] : yrow[0]];
+#pragma unroll
+      for (int k = 0; k < NR; ++k) yrow[k] = (d[k] >= 0 && d[k] < a.cout) ? d[k] : -1;
     }
   }
 
-  for (int r0 = b_lo; r0 < b_hi; r0 += MAXB) {
-    const int r1 = min(r0 + MAXB, b_hi);
-    const int nbr = r1 - r0;
-    // dense blocks come first in the block order
-    const int nd_r = max(0, min(r1, tk.nbd) - r0);
-    if (gather) {
-      // Gather thread gt takes 16-byte chunk gt % CPR of LDS positions
-      // gt / CPR + PPJ * j; position p is slot p % 64 of block p / 64, so the
-      // block of step j is a compile-time constant and the dense / 2:4
-      // choice is uniform.  Buffer loads: an out-of-range offset reads zero.
-      constexpr int PPJ = GT / CPR;
-      const int gt = threadIdx.x - 256;
-      const int pofs = gt / CPR;
-      const uint32_t xcol = (uint32_t)(n0 + 8 * (gt % CPR)) * 2u;
+  // Rounds of up to MAXB blocks.  Each role issues the loads of round r + 1
+  // as soon as it is done with the registers of round r - the gather waves
+  // right after their LDS store, the row waves right after their multiplies
+  // - so the next round's load latency hides behind this round's work.  Two
+  // barriers a round: X rows are in LDS; the row waves are done with them.
+  const int nrounds = (b_hi - b_lo + MAXB - 1) / MAXB;
+  if (gather) {
+    // Gather thread gt takes 16-byte chunk gt % CPR of LDS positions
+    // gt / CPR + PPJ * j; position p is slot p % 64 of block p / 64, so the
+    // block of step j is a compile-time constant and the dense / 2:4 choice
+    // is uniform.  Buffer loads: an out-of-range offset reads zero.
+    constexpr int PPJ = GT / CPR;
+    const int gt = threadIdx.x - 256;
+    const int pofs = gt / CPR;
+    // Tokens of this lane's chunk inside the batch.  A ragged batch or rows
+    // that are not 16-byte aligned still take one 16-byte load per chunk
+    // (buffer loads serve 2-byte aligned addresses).  The tokens past the
+    // batch - the next row's, or zeros past the buffer - reach only output
+    // columns that are never written.  A chunk wholly past the batch gets a
+    // column offset past every buffer, so it reads zeros and costs nothing.
+    const int vt = FAST ? 8 : min(8, a.batch - (n0 + 8 * (gt % CPR)));
+    const uint32_t xcol = vt > 0 ? (uint32_t)(n0 + 8 * (gt % CPR)) * 2u : 0x80000000u;
+    // The buffer ends with the last token of the last X row, and its range
+    // check zeroes every dword that crosses that end: with an odd number of
+    // tokens left, the last row's partial chunk would lose its last token.
+    // That chunk is loaded from one token earlier, so that its dwords end
+    // with the buffer, and shifted back at the LDS store.  A tile's index
+    // lists name every X row at most once, so a lane meets that row at most
+    // once a round.
+    const int fixrow = (!FAST && vt > 0 && vt < 8 && (vt & 1)) ? a.cin - 1 : -2;
+    u32x4 xr[MAXCH];
+    int fix_j = -1;
+    auto issue = [&](int r0) {
+      const int r1 = min(r0 + MAXB, b_hi);
+      const int nbr = r1 - r0;
+      const int nd_r = max(0, min(r1, tk.nbd) - r0);   // dense blocks come first in the block order
       const uint32_t dbase = (uint32_t)(tk.kd0 + r0) * 32u;
       const uint32_t sbase = (uint32_t)(tk.ks0 + max(0, r0 - tk.nbd)) * 64u;
       int cidx[MAXCH];
@@ -472,52 +520,99 @@ __global__ __launch_bounds__(384) void decode5_kernel(SpmmArgs a, int splits, in
         const __amdgpu_buffer_rsrc_t r = dense ? res.id : res.is;
         cidx[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(r, blk < nbr ? li * 4u : kOob, 0, 0);
       }
-      u32x4 xr[MAXCH];
+      fix_j = -1;
 #pragma unroll
       for (int j = 0; j < MAXCH; ++j) {
         const int blk = (PPJ * j) >> 6;
         const int ci = blk < nbr ? cidx[j] : -1;       // rows past the K range read as zeros
+        const uint32_t off = ci < 0 ? kOob : __umul24((uint32_t)ci, res.ldx_bytes) + xcol;
         if constexpr (FAST) {
-          const uint32_t off = ci < 0 ? kOob : __umul24((uint32_t)ci, res.ldx_bytes) + xcol;
           xr[j] = __builtin_amdgcn_raw_buffer_load_b128(res.x, off, 0, 0);
         } else {
-          xr[j] = load_x_chunk(a, ci, n0 + 8 * (gt % CPR));
+          const bool fix = ci == fixrow;
+          xr[j] = __builtin_amdgcn_raw_buffer_load_b128(res.x, fix ? off - 2u : off, 0, 0);
+          fix_j = fix ? j : fix_j;
         }
       }
-      __syncthreads();   // the X gathers are on their way: let the packed values go
+    };
+    if (nrounds > 0) issue(b_lo);
+    __syncthreads();   // the first X gathers are on their way: let the packed values go
+    for (int r = 0; r < nrounds; ++r) {
+      if (!FAST && __builtin_amdgcn_ballot_w64(fix_j >= 0) != 0) {
+        // a wave that holds the last row's shifted chunk
 #pragma unroll
-      for (int j = 0; j < MAXCH; ++j) *reinterpret_cast<u32x4*>(xs + 8 * (gt + GT * j)) = xr[j];
+        for (int j = 0; j < MAXCH; ++j) {
+          const uint32_t d0 = xr[j][0], d1 = xr[j][1], d2 = xr[j][2], d3 = xr[j][3];
+          const bool sh = j == fix_j;
+          *reinterpret_cast<u32x4*>(xs + xs_gran<NB>(pofs + PPJ * j, (gt % CPR) >> 1) * 16 + 8 * (gt & 1)) =
+              u32x4{sh ? __builtin_amdgcn_alignbyte(d1, d0, 2) : d0, sh ? __builtin_amdgcn_alignbyte(d2, d1, 2) : d1,
+                    sh ? __builtin_amdgcn_alignbyte(d3, d2, 2) : d2, sh ? d3 >> 16 : d3};
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < MAXCH; ++j)
+          *reinterpret_cast<u32x4*>(xs + xs_gran<NB>(pofs + PPJ * j, (gt % CPR) >> 1) * 16 + 8 * (gt & 1)) = xr[j];
+      }
+      if (r + 1 < nrounds) issue(b_lo + (r + 1) * MAXB);
       __syncthreads();   // X rows are in LDS
       __syncthreads();   // the row waves are done with them
-    } else {
-      // Each branch holds its own barriers (the condition is uniform per
-      // wave), so the two roles keep disjoint register sets.
-      u32x4 av[MAXB];
-      uint64_t mv[MAXB];
-      __syncthreads();   // wait until the X gathers are issued
+    }
+  } else {
+    // Each role holds its own barriers (the condition is uniform per wave),
+    // so the two roles keep disjoint register sets.
+    u32x4 av[MAXB];
+    uint64_t mv[MAXB];
+    // Loads of block r0 + j into slot j; a block past this split's range
+    // reads zeros (its X rows are zeros too).
+    auto issue_blk = [&](int r0, int j) {
+      const int b = r0 + j;
+      const bool dense = b < tk.nbd;
+      const uint32_t brow = dense ? (uint32_t)((tk.kd0 + b) * a.rows + row)
+                                  : (uint32_t)((tk.ks0 + (b - tk.nbd)) * a.rows + row);
+      av[j] = __builtin_amdgcn_raw_buffer_load_b128(dense ? res.vd : res.vs, b < b_hi ? brow * 64u + 16u * kc : kOob,
+                                                    0, 0);
+      mv[j] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(res.meta, dense || b >= b_hi ? kOob
+                                                                                                       : brow * 8u, 0, 0));
+    };
+    // This lane's transpose-read offsets within a block: positions
+    // 8*kc + i16/4 + {0, 4, 32, 36}, token group nb, tokens 4*(i16 % 4)...
+    int ro[4][NB];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        ro[k][nb] = xs_gran<NB>(8 * kc + (i16 >> 2) + 4 * (k & 1) + 32 * (k >> 1), nb) * 16 + 4 * (i16 & 3);
+    // DPF blocks in flight ahead of the multiplies: a wave that queued all
+    // of a round's loads at once would stall in issue, behind the memory
+    // system's back-pressure, before it could multiply the first block.
+    // Only P0 of them go out before the first X gathers: the index slices
+    // those gathers wait for are tiny next to the packed values and would
+    // otherwise queue behind them.
+#pragma unroll
+    for (int j = 0; j < P0; ++j) issue_blk(b_lo, j);
+    __syncthreads();   // wait until the first X gathers are issued
+#pragma unroll
+    for (int j = P0; j < DPF; ++j) issue_blk(b_lo, j);
+    for (int r = 0; r < nrounds; ++r) {
+      const int r0 = b_lo + r * MAXB;
+      const int nd_r = max(0, min(min(r0 + MAXB, b_hi), tk.nbd) - r0);
+      // Nothing that reads the packed values may move above the barrier:
+      // waiting for them there would hold back the whole workgroup.
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();   // X rows are in LDS
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < MAXB; ++j) {
-        const int b = r0 + min(j, nbr - 1);
-        const bool dense = b < tk.nbd;
-        const uint32_t brow = dense ? (uint32_t)((tk.kd0 + b) * a.rows + row)
-                                    : (uint32_t)((tk.ks0 + (b - tk.nbd)) * a.rows + row);
-        av[j] = __builtin_amdgcn_raw_buffer_load_b128(dense ? res.vd : res.vs, brow * 64u + 16u * kc, 0, 0);
-        mv[j] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(res.meta, dense ? kOob : brow * 8u, 0, 0));
-      }
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < MAXB; ++j) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        const bf16x8 A = __builtin_bit_cast(bf16x8, j < nbr ? av[j] : z);
+        if (j + DPF < MAXB) issue_blk(r0, j + DPF);
+        const bf16x8 A = __builtin_bit_cast(bf16x8, av[j]);
         const int sidx = j < nd_r ? 0x4444 : (int)((mv[j] >> (16 * kc)) & 0xffffull);
-        const uint16_t* xb = xs + (64 * j) * NTOK;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          const uint16_t* base = xb + 16 * nb + 4 * (i16 & 3);
-          const v4i16 b0 = tr_read(base + (8 * kc + 0 + (i16 >> 2)) * NTOK);
-          const v4i16 b1 = tr_read(base + (8 * kc + 4 + (i16 >> 2)) * NTOK);
-          const v4i16 b2 = tr_read(base + (32 + 8 * kc + 0 + (i16 >> 2)) * NTOK);
-          const v4i16 b3 = tr_read(base + (32 + 8 * kc + 4 + (i16 >> 2)) * NTOK);
+          const uint16_t* base = xs + (64 * j) * NTOK;   // the swizzle maps blocks of 64 positions onto themselves
+          const v4i16 b0 = tr_read(base + ro[0][nb]);
+          const v4i16 b1 = tr_read(base + ro[1][nb]);
+          const v4i16 b2 = tr_read(base + ro[2][nb]);
+          const v4i16 b3 = tr_read(base + ro[3][nb]);
           const bf16x16 B = __builtin_bit_cast(
               bf16x16, __builtin_shufflevector(__builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7),
                                                __builtin_shufflevector(b2, b3, 0, 1, 2, 3, 4, 5, 6, 7), 0, 1, 2,
@@ -525,6 +620,9 @@ __global__ __launch_bounds__(384) void decode5_kernel(SpmmArgs a, int splits, in
           acc[j & 1][nb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(A, B, acc[j & 1][nb], sidx, 0, 0);
         }
       }
+      // the next round's first blocks (zeros after the last round)
+#pragma unroll
+      for (int j = 0; j < DPF; ++j) issue_blk(r0 + MAXB, j);
       __syncthreads();   // the next round overwrites xs
     }
   }
@@ -1254,13 +1352,13 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
 
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   // The prefill and split decode kernels address X and the packed buffers
-  // with 32-bit buffer offsets and gather with a 24-bit multiply; beyond
-  // those ranges kernels with 64-bit addressing take over (the generic
-  // kernel without a K split, or the 16-row decode kernel; neither needs a
-  // workspace).
-  const int64_t lim = (int64_t)1 << 31;
+  // with 32-bit buffer offsets and gather with a 24-bit multiply (row index
+  // and row pitch in bytes both below 2^24); beyond those ranges kernels
+  // with 64-bit addressing take over (the generic kernel without a K split,
+  // or the 16-row decode kernel; neither needs a workspace).
+  const int64_t lim = (int64_t)1 << 31, lim24 = (int64_t)1 << 24;
   const int64_t xbytes = ((int64_t)(p.cin - 1) * ldx + batch) * 2;
-  const bool fits32 = xbytes < lim && ldx * 2 < ((int64_t)1 << 24) && p.bytes_val_dense < lim &&
+  const bool fits32 = xbytes < lim && ldx * 2 < lim24 && p.cin <= lim24 && p.bytes_val_dense < lim &&
                       p.bytes_val_24 < lim && p.bytes_idx_dense < lim && p.bytes_idx_24 < lim &&
                       p.bytes_meta_24 < lim;
   if (sh.path == hinm::kPathDecodeSplit && !fits32) {

@@ -221,3 +221,30 @@ def test_spmm_graph_replay():
         (c, _), x = cases[0], xs[0]
         assert torch.equal(hinm.spmm(c.pk, x, workspace=ws).view(torch.int16), eager[0].view(torch.int16))
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("unaligned", [False, True])
+def test_spmm_last_x_row_odd_batches(unaligned):
+    """The last input channel kept in every tile (its importance raised), at
+    odd and ragged batches: the gather's 16-byte loads of that row end past
+    the X buffer, so its tokens must come back whole.  Unaligned: X starts 2
+    bytes past a 16-byte boundary."""
+    w = synth.small(128, 264, 64, 0.6, 0.35, 1, seed=21)
+    w.importance[:, -1] = w.importance.max() * 4.0
+    c = Case(w)
+    assert (c.w_hat[:, -1] != 0).all()                                 # kept (dense) in every tile
+    for b in (1, 3, 5, 7, 9, 13, 17, 23, 33, 47, 63):
+        g = torch.Generator().manual_seed(b)
+        x = torch.randn(264, b, generator=g).to(torch.bfloat16)
+        x[-1] = torch.linspace(1.0, 2.0, b).to(torch.bfloat16)         # never zero: a lost token shows
+        if unaligned:
+            buf = torch.empty(264 * b + 1, dtype=torch.bfloat16, device=DEV)
+            buf[1:].copy_(x.reshape(-1).to(DEV))
+            xd = buf[1:].view(264, b)
+        else:
+            xd = x.to(DEV)
+        print(f"[spmm]   last row, batch={b} unaligned={unaligned}", flush=True)
+        y = hinm.spmm(c.pk, xd)
+        torch.cuda.synchronize()
+        xf = synth.as_f64(x)
+        check_y(y, c.w_hat @ xf, np.abs(c.w_hat) @ np.abs(xf), f"last row batch {b}")
