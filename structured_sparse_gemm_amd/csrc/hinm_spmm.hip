@@ -387,10 +387,10 @@ struct BufRes {
 //
 // Every block, dense or 2:4, takes 64 LDS positions and one
 // v_smfmac_f32_16x16x64_bf16: a dense block's 32 columns sit at positions
-// 4q and 4q+1 of its groups (column 2q+e at position 4q+e) and use the fixed
-// index pattern 0x4 (positions 0 and 1 of every group), which is exactly the
-// dense product because the A operand of a dense block is its 32 values in
-// order.  The multiply loop is then the same straight-line code for every
+// 4q and 4q+1 of its groups (column 2q+e at position 4q+e; positions 4q+2
+// and 4q+3 hold zeros) and use the fixed index pattern 0x4 (positions 0 and
+// 1 of every group), which is exactly the dense product because the A
+// operand of a dense block is its 32 values in order.  The multiply loop is then the same straight-line code for every
 // block: blocks past the K range get zero values and zero X rows, and blocks
 // alternate between two accumulators so consecutive SMFMACs do not wait on
 // each other.
@@ -518,13 +518,16 @@ __global__ __launch_bounds__(384) void decode5_kernel(SpmmArgs a, int splits, in
         const uint32_t li = dense ? dbase + 32u * blk + 2u * (slot >> 2) + (slot & 1)
                                   : sbase + 64u * (blk - nd_r) + slot;
         const __amdgpu_buffer_rsrc_t r = dense ? res.id : res.is;
-        cidx[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(r, blk < nbr ? li * 4u : kOob, 0, 0);
+        // rows past the K range and a dense block's positions 4q+2, 4q+3
+        // (never selected by its index pattern) read as zeros
+        const bool ok = blk < nbr && !(dense && (slot & 2));
+        const int v = (int)__builtin_amdgcn_raw_buffer_load_b32(r, ok ? li * 4u : kOob, 0, 0);
+        cidx[j] = ok ? v : -1;
       }
       fix_j = -1;
 #pragma unroll
       for (int j = 0; j < MAXCH; ++j) {
-        const int blk = (PPJ * j) >> 6;
-        const int ci = blk < nbr ? cidx[j] : -1;       // rows past the K range read as zeros
+        const int ci = cidx[j];
         const uint32_t off = ci < 0 ? kOob : __umul24((uint32_t)ci, res.ldx_bytes) + xcol;
         if constexpr (FAST) {
           xr[j] = __builtin_amdgcn_raw_buffer_load_b128(res.x, off, 0, 0);
