@@ -248,3 +248,25 @@ def test_spmm_last_x_row_odd_batches(unaligned):
         torch.cuda.synchronize()
         xf = synth.as_f64(x)
         check_y(y, c.w_hat @ xf, np.abs(c.w_hat) @ np.abs(xf), f"last row batch {b}")
+
+
+@pytest.mark.parametrize("unaligned", [False, True])
+def test_spmm_decode_ragged_full_width(unaligned):
+    """Split-K decode at q_proj's full 4096x4096 shape (4 K splits): ragged batches in every token-block size,
+    X contiguous (rows 16-byte aligned only at multiples of 8 tokens) or starting 2 bytes past a 16-byte
+    boundary; every output row checked."""
+    c = Case(synth.q_proj(batch=16))
+    for b in (1, 7, 8, 13, 24, 33, 47, 64):
+        g = torch.Generator().manual_seed(300 + b)
+        x = torch.randn(c.w.cin, b, generator=g).to(torch.bfloat16)
+        if unaligned:
+            buf = torch.empty(c.w.cin * b + 1, dtype=torch.bfloat16, device=DEV)
+            buf[1:].copy_(x.reshape(-1).to(DEV))
+            xd = buf[1:].view(c.w.cin, b)
+        else:
+            xd = x.to(DEV)
+        print(f"[spmm]   full-width decode batch={b} unaligned={unaligned}", flush=True)
+        y = hinm.spmm(c.pk, xd)
+        torch.cuda.synchronize()
+        xf = synth.as_f64(x)
+        check_y(y, oh.spmm(c.w_hat, xf), np.abs(c.w_hat) @ np.abs(xf), f"q_proj batch {b}")
