@@ -758,7 +758,16 @@ __device__ inline void prefill_phase(const SpmmArgs& a, const BufRes& res, uint1
   const int pbase = (threadIdx.x / C::CPR) * PPT;          // first of this thread's PPT positions
   constexpr int G = 64 / C::CPR;              // position groups per wave
   const int grp = lane / C::CPR;
-  const uint32_t xcol = (uint32_t)(n0 + 8 * cnk) * 2u;
+  // Without FAST (unaligned X rows or the batch's last token block): one
+  // 16-byte load per chunk all the same (buffer loads take 2-byte-aligned
+  // offsets); a chunk wholly past the batch reads zeros, tokens past the
+  // batch inside a chunk reach only unwritten output columns, and the last X
+  // row's partial chunk with an odd token count is loaded one token early
+  // (the buffer's range check zeroes every dword crossing its end) and
+  // shifted back at the LDS store.
+  const int vt = FAST ? 8 : min(8, a.batch - (n0 + 8 * cnk));
+  const uint32_t xcol = vt > 0 ? (uint32_t)(n0 + 8 * cnk) * 2u : 0x80000000u;
+  const int fixrow = (!FAST && vt > 0 && vt < 8 && (vt & 1)) ? a.cin - 1 : -2;
   const __amdgpu_buffer_rsrc_t rid = DENSE ? res.id : res.is;
   const __amdgpu_buffer_rsrc_t rv = DENSE ? res.vd : res.vs;
   const uint32_t vrow = (uint32_t)rb * 64u;
@@ -786,14 +795,18 @@ __device__ inline void prefill_phase(const SpmmArgs& a, const BufRes& res, uint1
       ci[j] = c;
     }
   };
-  auto load_x = [&](const int (&ci)[PPT], u32x4 (&st)[PPT]) {
+  int fixm[2] = {0, 0};                       // per register set: loads j that were shifted
+  auto load_x = [&](const int (&ci)[PPT], u32x4 (&st)[PPT], int& fm) {
+    fm = 0;
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
+      const uint32_t off = ci[j] < 0 ? kOob : __umul24((uint32_t)ci[j], res.ldx_bytes) + xcol;
       if constexpr (FAST) {
-        const uint32_t off = ci[j] < 0 ? kOob : __umul24((uint32_t)ci[j], res.ldx_bytes) + xcol;
         st[j] = __builtin_amdgcn_raw_buffer_load_b128(res.x, off, 0, 0);
       } else {
-        st[j] = load_x_chunk(a, ci[j], n0 + 8 * cnk);
+        const bool fix = ci[j] == fixrow;
+        st[j] = __builtin_amdgcn_raw_buffer_load_b128(res.x, fix ? off - 2u : off, 0, 0);
+        fm |= fix ? 1 << j : 0;
       }
     }
   };
@@ -805,9 +818,18 @@ __device__ inline void prefill_phase(const SpmmArgs& a, const BufRes& res, uint1
       st.m = __builtin_amdgcn_raw_buffer_load_b32(res.meta, threadIdx.x < 128 ? blk * 8u + 4u * threadIdx.x : kOob,
                                                   0, 0);
   };
-  auto store = [&](uint16_t* xs, uint32_t* ms, const u32x4 (&x)[PPT], const PrefillA& st) {
+  auto store = [&](uint16_t* xs, uint32_t* ms, const u32x4 (&x)[PPT], int fm, const PrefillA& st) {
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) *reinterpret_cast<u32x4*>(xs + (pbase + j) * C::PITCH + 8 * cnk) = x[j];
+    for (int j = 0; j < PPT; ++j) {
+      u32x4 v = x[j];
+      if constexpr (!FAST) {                      // shift the last X row's partial chunk (selects, no branch)
+        const bool sh = (fm >> j) & 1;
+        const uint32_t d0 = x[j][0], d1 = x[j][1], d2 = x[j][2], d3 = x[j][3];
+        v = u32x4{sh ? __builtin_amdgcn_alignbyte(d1, d0, 2) : d0, sh ? __builtin_amdgcn_alignbyte(d2, d1, 2) : d1,
+                  sh ? __builtin_amdgcn_alignbyte(d3, d2, 2) : d2, sh ? d3 >> 16 : d3};
+      }
+      *reinterpret_cast<u32x4*>(xs + (pbase + j) * C::PITCH + 8 * cnk) = v;
+    }
     *reinterpret_cast<u32x4*>(xs + acol) = st.v;
     if constexpr (!DENSE)
       if (threadIdx.x < 128) ms[threadIdx.x] = st.m;
@@ -882,23 +904,23 @@ __device__ inline void prefill_phase(const SpmmArgs& a, const BufRes& res, uint1
   Iw[0] = load_idx(0);
   Iw[1] = load_idx(1);
   spread_idx(Iw[0], CI);
-  load_x(CI, X[0]);
+  load_x(CI, X[0], fixm[0]);
   spread_idx(Iw[1], CI);
-  load_x(CI, X[1]);
+  load_x(CI, X[1], fixm[1]);
   Iw[0] = load_idx(2);
   Iw[1] = load_idx(3);
 #pragma unroll
   for (int d = 0; d < DA; ++d) load_a(d, A[d]);
   spread_idx(Iw[0], CI);
-  store(tile[0], mtile[0], X[0], A[0]);
+  store(tile[0], mtile[0], X[0], fixm[0], A[0]);
   __syncthreads();
   auto step = [&](auto kc, int bb) {
     constexpr int k = decltype(kc)::value;
-    load_x(CI, X[k % 2]);             // X(bb+2)
+    load_x(CI, X[k % 2], fixm[k % 2]); // X(bb+2)
     Iw[k % 2] = load_idx(bb + 4);
     load_a(bb + DA, A[k % DA]);
     compute(tile[k % 2], mtile[k % 2]);
-    store(tile[(k + 1) % 2], mtile[(k + 1) % 2], X[(k + 1) % 2], A[(k + 1) % DA]);
+    store(tile[(k + 1) % 2], mtile[(k + 1) % 2], X[(k + 1) % 2], fixm[(k + 1) % 2], A[(k + 1) % DA]);
     spread_idx(Iw[(k + 1) % 2], CI);  // indices of bb+3
     __syncthreads();
   };
@@ -933,8 +955,9 @@ __device__ inline v4i16 tr_read_b(const uint8_t* lds) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds_u8*)lds);
 }
 
-// prefill_phase with the X rows loaded straight into LDS (X rows 16-byte
-// aligned).  The gathered rows never pass through VGPRs: each wave issues
+// prefill_phase with the X rows loaded straight into LDS (buffer loads into
+// LDS take 2-byte-aligned addresses, so any X layout).  The gathered rows
+// never pass through VGPRs: each wave issues
 // its share of block b + 1's rows into the other tile at the start of step
 // b, multiplies block b, stores the packed values of b + 1 (loaded DA blocks
 // earlier through VGPRs), waits for its own row loads and meets the other
@@ -946,7 +969,16 @@ __device__ inline v4i16 tr_read_b(const uint8_t* lds) {
 // chunk q of row r at q ^ (r / 4 % 4).  X load j of a wave brings 64 / CPR
 // consecutive positions starting at wave * RPW + j * 64 / CPR, lane l taking
 // chunk l % CPR of position + l / CPR.
-template <int NT, bool DENSE>
+//
+// TAIL (1 or 2: the token block ends past the batch): chunks wholly past the
+// batch read zeros (no traffic); tokens past the batch inside a chunk reach
+// only output columns that are never written.  The buffer ends with the last
+// token of the last X row and its range check zeroes every dword that
+// crosses that end, so with an odd batch (TAIL 2) the last row's partial
+// chunk with an odd token count is loaded one token early and shifted back
+// in LDS once it has landed (a tile names each X row at most once).  The
+// shift is a branch, which is kept out of the other instantiations.
+template <int NT, bool DENSE, int TAIL>
 __device__ inline void prefill_phase_lds(const SpmmArgs& a, const BufRes& res, uint16_t* xs0, uint16_t* xs1,
                                          uint32_t* ms0, uint32_t* ms1, int kbase, int nb, int rb, int n0,
                                          f32x16 (&acc)[2][PrefillCfg<NT>::NTB]) {
@@ -998,11 +1030,38 @@ __device__ inline void prefill_phase_lds(const SpmmArgs& a, const BufRes& res, u
       ci[j] = c;
     }
   };
+  int fixm = 0;                               // TAIL: loads j of the last issue that were shifted
   auto load_x = [&](const int (&ci)[NJ], uint16_t* xs) {
+    fixm = 0;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const uint32_t off = ci[j] < 0 ? kOob : __umul24((uint32_t)ci[j], res.ldx_bytes) + xcol + xch[j];
+      uint32_t off = ci[j] < 0 ? kOob : __umul24((uint32_t)ci[j], res.ldx_bytes) + xcol + xch[j];
+      if constexpr (TAIL != 0) {
+        const int vt = a.batch - (n0 + (int)(xch[j] >> 1));   // tokens of the chunk inside the batch
+        off = vt <= 0 ? kOob : off;
+        if constexpr (TAIL == 2) {
+          const bool fix = ci[j] == a.cin - 1 && vt > 0 && vt < 8 && (vt & 1);
+          off = fix ? off - 2u : off;
+          fixm |= fix ? 1 << j : 0;
+        }
+      }
       load_lds16(res.x, reinterpret_cast<uint8_t*>(xs) + (wave * RPW + j * RPL) * XROW, off);
+    }
+  };
+  // TAIL, after this wave's loads have landed: shift the marked chunks back by one token
+  auto fix_x = [&](uint16_t* xs) {
+    if constexpr (TAIL == 2) {
+      if (__builtin_amdgcn_ballot_w64(fixm != 0) != 0) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          if (fixm & (1 << j)) {
+            u32x4* p = reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(xs) + (wave * RPW + j * RPL) * XROW + 16 * lane);
+            const u32x4 d = *p;
+            *p = u32x4{__builtin_amdgcn_alignbyte(d[1], d[0], 2), __builtin_amdgcn_alignbyte(d[2], d[1], 2),
+                       __builtin_amdgcn_alignbyte(d[3], d[2], 2), d[3] >> 16};
+          }
+        }
+      }
     }
   };
   auto load_a = [&](int b, PrefillA& st) {
@@ -1097,16 +1156,19 @@ __device__ inline void prefill_phase_lds(const SpmmArgs& a, const BufRes& res, u
   Iw[0] = load_idx(2);
   store_a(tile[0], mtile[0], A[0]);
   wait_vm<1>();                      // the X rows of block 0 (only the index load of block 2 is younger)
+  fix_x(tile[0]);
   __syncthreads();
   auto step = [&](auto kc, int bb) {
     constexpr int k = decltype(kc)::value;
     if (bb + 1 < nb) load_x(CI, tile[(k + 1) % 2]);   // X(bb+1)
+    else fixm = 0;
     Iw[(k + 1) % 2] = load_idx(bb + 3);
     load_a(bb + DA, A[k % DA]);
     compute(tile[k % 2], mtile[k % 2]);
     store_a(tile[(k + 1) % 2], mtile[(k + 1) % 2], A[(k + 1) % DA]);
     spread_idx(Iw[k % 2], CI);        // indices of bb+2
     wait_vm<PA>();                    // this wave's X rows of bb+1 are in LDS
+    fix_x(tile[(k + 1) % 2]);
     __syncthreads();
   };
   int b = 0;
@@ -1121,15 +1183,17 @@ __device__ inline void prefill_phase_lds(const SpmmArgs& a, const BufRes& res, u
   if (b + 2 < nb) step(std::integral_constant<int, 2>{}, b + 2);
 }
 
-template <int NT, bool FAST>
+// FAST: 16-byte aligned X rows and a token block inside the batch; TAIL: the
+// token block ends past the batch (1: even batch, 2: odd batch).
+template <int NT, bool FAST, int TAIL>
 __device__ inline void prefill_body(const SpmmArgs& a, const BufRes& res, uint16_t* xs0, uint16_t* xs1,
                                     uint32_t* ms0, uint32_t* ms1, int t, int rb, int n0,
                                     f32x16 (&acc)[2][PrefillCfg<NT>::NTB]) {
   const TileK tk = tile_k(a, t);
   if constexpr (NT == 256) {
     if (a.x_lds) {
-      prefill_phase_lds<NT, true>(a, res, xs0, xs1, ms0, ms1, tk.kd0, tk.nbd, rb, n0, acc);
-      prefill_phase_lds<NT, false>(a, res, xs0, xs1, ms0, ms1, tk.ks0, tk.nbs, rb, n0, acc);
+      prefill_phase_lds<NT, true, TAIL>(a, res, xs0, xs1, ms0, ms1, tk.kd0, tk.nbd, rb, n0, acc);
+      prefill_phase_lds<NT, false, TAIL>(a, res, xs0, xs1, ms0, ms1, tk.ks0, tk.nbs, rb, n0, acc);
       return;
     }
   }
@@ -1216,8 +1280,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
         for (int j = 0; j < C::NTB; ++j)
           for (int e = 0; e < 16; ++e) acc[r][j][e] = 0.f;
 
-      if (a.x_vec && n0 + NT <= a.batch) prefill_body<NT, true>(a, res, xs[0], xs[1], ms[0], ms[1], t, rb, n0, acc);
-      else prefill_body<NT, false>(a, res, xs[0], xs[1], ms[0], ms[1], t, rb, n0, acc);
+      if (n0 + NT > a.batch) {
+        if (a.batch & 1) prefill_body<NT, false, 2>(a, res, xs[0], xs[1], ms[0], ms[1], t, rb, n0, acc);
+        else prefill_body<NT, false, 1>(a, res, xs[0], xs[1], ms[0], ms[1], t, rb, n0, acc);
+      } else if (a.x_vec) {
+        prefill_body<NT, true, 0>(a, res, xs[0], xs[1], ms[0], ms[1], t, rb, n0, acc);
+      } else {
+        prefill_body<NT, false, 0>(a, res, xs[0], xs[1], ms[0], ms[1], t, rb, n0, acc);
+      }
       __syncthreads();
 
       // epilogue: acc[r][j][e] is row 32r + 8(e/4) + 4(lane/32) + e%4, token tok_w + 32j + lane%32.
@@ -1340,11 +1410,12 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
   a.n_kunits = sh.n_kunits;
   a.x_vec = hinm::aligned(x_bf16, 16) && (ldx % 8 == 0);
   {
-    // At 256-token blocks X rows go straight into LDS when they are 16-byte
-    // aligned (the register-staged gather stays selectable for comparison);
-    // at 128-token blocks the register-staged gather measured faster.
+    // At 256-token blocks X rows go straight into LDS, whatever their
+    // alignment (the register-staged gather stays selectable for
+    // comparison); at 128-token blocks the register-staged gather measured
+    // faster.
     const char* pp = getenv("HINM_PREFILL_PATH");
-    a.x_lds = a.x_vec && !(pp && strcmp(pp, "staged") == 0);
+    a.x_lds = !(pp && strcmp(pp, "staged") == 0);
   }
   a.y_vec = hinm::aligned(y_bf16, 16) && (ldy % 8 == 0);
   a.n_tiles = p.n_tiles;

@@ -108,3 +108,35 @@ def test_prefill_nonfinite_pruned_rows_do_not_reach_y(monkeypatch):
     xf = synth.as_f64(x)
     xf[dead] = 0.0                                           # pruned everywhere: never multiplied
     check_y(y, oh.spmm(wh, xf), np.abs(wh) @ np.abs(xf), "non-finite pruned rows")
+
+
+@pytest.mark.parametrize("layout", ["aligned", "contiguous", "offset"])
+def test_prefill_last_x_row_ragged_tails(monkeypatch, layout):
+    """The last input channel kept in every tile, at batches whose last token block ends inside a
+    16-byte chunk (odd and even remainders), with X rows 16-byte aligned (row stride a multiple of 8
+    tokens), contiguous (stride = batch) or starting 2 bytes past a 16-byte boundary.  The gathers of
+    the last X row end at the buffer's end, where the range check works per dword; both X paths must
+    bring every token of it back."""
+    w = synth.small(128, 264, 64, 0.6, 0.35, 1, seed=23)
+    w.importance[:, -1] = w.importance.max() * 4.0
+    pk = hinm.pack(w.w_bf16.to(DEV), w.importance.to(DEV), 64, 0.6, 0.35, w.perm.to(DEV))
+    _, _, inter = oracle_pack(w)
+    wh = oh.masked_weight(bits_of(w.w_bf16), inter["mask"])
+    assert (wh[:, -1] != 0).all()
+    for b in (65, 97, 129, 300, 1025, 1027, 1030, 1031, 1279, 2047):
+        x = torch.randn(264, b, generator=torch.Generator().manual_seed(b)).to(torch.bfloat16)
+        x[-1] = torch.linspace(1.0, 2.0, b).to(torch.bfloat16)          # never zero: a lost token shows
+        if layout == "aligned":
+            buf = torch.zeros(264, (b + 7) // 8 * 8, dtype=torch.bfloat16, device=DEV)
+            buf[:, :b].copy_(x.to(DEV))
+            xd = buf[:, :b]
+        elif layout == "contiguous":
+            xd = x.to(DEV)
+        else:
+            buf = torch.empty(264 * b + 1, dtype=torch.bfloat16, device=DEV)
+            buf[1:].copy_(x.reshape(-1).to(DEV))
+            xd = buf[1:].view(264, b)
+        print(f"[prefill] last row, batch={b} layout={layout}", flush=True)
+        y = both_paths(monkeypatch, lambda: hinm.spmm(pk, xd))
+        xf = synth.as_f64(x)
+        check_y(y, oh.spmm(wh, xf), np.abs(wh) @ np.abs(xf), f"last row batch {b} {layout}")
