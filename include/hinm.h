@@ -198,10 +198,10 @@ int hinm_spmm_workspace_bytes(const hinm_plan_t* plan, int64_t batch, size_t* by
  * permutation folded in).  X (device) bf16 [cin][ldx], ldx >= batch; Y
  * (device) bf16 [cout][ldy], ldy >= batch, every element of Y[:, 0:batch] is
  * written (rounded to nearest even from the fp32 accumulator), nothing else.
- * X and Y must be 2-byte aligned.  Above batch 64, 16-byte aligned X with
- * ldx % 8 == 0 takes the vector-load path (other X layouts gather through
- * narrower loads); up to batch 64 every layout and batch is gathered with
- * 16-byte loads.  workspace (device, 256-byte aligned) of at least
+ * X and Y must be 2-byte aligned.  X rows are gathered with 16-byte loads
+ * whatever the layout; rows that are not 16-byte aligned (X not 16-byte
+ * aligned, or ldx % 8 != 0) cost more, as most loads then straddle cache
+ * lines.  workspace (device, 256-byte aligned) of at least
  * hinm_spmm_workspace_bytes(plan, batch) bytes, may be NULL when that is 0.
  * The workspace must be zero-filled before its first use; every call that
  * returns HINM_OK leaves it ready for the next one (its arrival counters are
