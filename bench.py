@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--decode-batch", type=int, default=16)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense torch.matmul comparator")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 32-layer stack batch sweep")
     ap.add_argument("--profile-only", type=int, default=0, metavar="K",
                     help="run K products at each batch plus a 256 MiB calibration copy, print nothing else "
                          "(for rocprofv3 runs)")
@@ -203,6 +204,95 @@ def time_dense(torch, w, x, steps, warmup):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / steps
+
+
+STACK_LAYERS = 32
+STACK_BATCHES = (1, 16, 64, 256, 1024, 2048, 4096)
+
+
+def stack_sweep(hinm, torch, synth, dev, with_dense):
+    """The 7B-shaped stack: 32 layers x {q, k, v, o 4096x4096; gate, up 11008x4096;
+    down 4096x11008}, HiNM packed once (tile_rows 64, t_s 0.75, v_s 0.55), and
+    the sum of all linear-layer products of one forward pass at each batch.
+
+    Weights are drawn on the device (iid N(0, 0.02), importance |W|, random
+    per-tile permutations): the product's time depends on the shapes and the
+    region counts only.  The 224 products of a forward are captured in one
+    HIP graph (X and Y buffers shared by the projections of the same shape),
+    replayed untimed, then timed over one replay with HIP events.  The packed
+    stack (3.4 GB) is well past the 256 MB last-level cache, so every weight
+    comes from HBM.  The dense comparator runs torch.matmul on the unpruned
+    bf16 weights (13 GB) the same way.
+    """
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    packs, dense = [], []
+    t0 = time.perf_counter()
+    for _layer in range(STACK_LAYERS):
+        for _name, cout, cin in synth.STACK_PROJS:
+            w = (torch.randn(cout, cin, device=dev, generator=g) * 0.02).to(torch.bfloat16)
+            imp = w.float().abs()
+            perm = torch.rand(cout // 64, cin, device=dev, generator=g).argsort(dim=1).to(torch.int32)
+            packs.append(hinm.pack(w, imp, 64, 0.75, 0.55, perm))
+            del imp, perm
+            if with_dense:
+                dense.append(w)
+            else:
+                del w
+    pack_s = time.perf_counter() - t0
+
+    def run_graph(fn, replays=3):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        for _ in range(replays):
+            graph.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        del graph
+        return ms
+
+    rows = []
+    for B in STACK_BATCHES:
+        xs = {c: torch.randn(c, B, device=dev, generator=g).to(torch.bfloat16) for c in (4096, 11008)}
+        ys = {c: torch.empty(c, B, dtype=torch.bfloat16, device=dev) for c in (4096, 11008)}
+        ws_bytes = max(hinm.spmm_workspace_bytes(pk.plan, B) for pk in packs[:7])
+        ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        useful = sum(2 * pk.plan.cout * (pk.plan.cin - pk.plan.z) * B for pk in packs)
+
+        def fwd():
+            for pk in packs:
+                hinm.spmm(pk, xs[pk.plan.cin], out=ys[pk.plan.cout], workspace=ws)
+        ms = run_graph(fwd)
+        row = {"batch": B, "ms_per_forward": round(ms, 4), "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2)}
+        if with_dense:
+            def fwd_dense():
+                for i, wt in enumerate(dense):
+                    _n, cout, cin = synth.STACK_PROJS[i % 7]
+                    torch.matmul(wt, xs[cin], out=ys[cout])
+            dms = run_graph(fwd_dense)
+            row["dense_ms_per_forward"] = round(dms, 4)
+            row["speedup_vs_dense"] = round(dms / ms, 3)
+        rows.append(row)
+        del xs, ys, ws
+    packed_gb = sum(pk.nbytes() for pk in packs) / 1e9
+    del packs, dense
+    torch.cuda.empty_cache()
+    return {"what": "32-layer 7B-shaped stack (q, k, v, o 4096x4096; gate, up 11008x4096; down 4096x11008), "
+                    "tile_rows 64, t_s 0.75, v_s 0.55, packed once; time of all 224 linear-layer products of one "
+                    "forward pass, one HIP graph replay after three untimed ones",
+            "packed_gb": round(packed_gb, 3), "pack_all_s": round(pack_s, 2), "per_batch": rows}
 
 
 def cpu_baseline(w, batch):
@@ -430,6 +520,8 @@ def main():
                  "batch_2048_ms": round(dense_ms, 4), "batch_16_ms": round(dense_ms_d, 4),
                  "speedup_batch_2048": round(dense_ms / ms, 3), "speedup_batch_16": round(dense_ms_d / rd["ms_mean"], 3)}
 
+    stack = None if args.no_stack else stack_sweep(hinm, torch, synth, dev, not args.no_dense)
+
     cpu = None if args.no_cpu else cpu_baseline(w, B)
 
     line = {
@@ -473,6 +565,7 @@ def main():
         "next_per_tile_v_s": next_tiles,
         "next_gyro_permutation": next_gyro,
         "dense_comparator": dense,
+        "stack_sweep": stack,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
