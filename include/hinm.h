@@ -219,7 +219,10 @@ int hinm_spmm_workspace_bytes(const hinm_plan_t* plan, int64_t batch, size_t* by
  * HINM_DECODE_PATH = rows16 (the 16-row batch <= 64 kernel without a K
  * split), HINM_PREFILL_PATH = staged (the batch > 64 kernel gathers X
  * through registers instead of loading it straight into LDS; same result
- * bits).  The workspace size asked for must come from the same settings.
+ * bits), HINM_PREFILL_SPLITS = 1 | 2 | 4 (K split of each batch > 64 work
+ * item; by default 2 or 4 when there are fewer than 512 items, which
+ * changes the last bits of Y).  The workspace size asked for must come from
+ * the same settings.
  * Errors (host-side checks only): HINM_EINVAL, HINM_ESHAPE, HINM_EALIGN,
  * HINM_EWORKSPACE, HINM_EHIP (launch failure). */
 int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_t batch, int64_t ldx,

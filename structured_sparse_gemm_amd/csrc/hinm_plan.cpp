@@ -161,7 +161,9 @@ extern "C" const char* hinm_last_error(void) { return hinm::g_last_error; }
 //  - other batch <= 64: the 16-row decode kernel (K split over the waves of
 //    a workgroup, no workspace);
 //  - larger batches with tile_rows % 64 == 0: the prefill kernel (64-row x
-//    128/256-token workgroups, no workspace);
+//    128/256-token items on a persistent grid; with fewer items than the grid
+//    holds, each item's K range is split over 2 or 4 workgroups and the
+//    partial sums go through the workspace);
 //  - otherwise the generic kernel, which splits K over workgroups when there
 //    are too few of them and reduces the partials through the workspace.
 namespace hinm {
@@ -204,6 +206,23 @@ SpmmShape spmm_shape(const hinm_plan_t* p, int64_t batch) {
     const char* env = getenv("HINM_PREFILL_NT");
     if (env && (atoi(env) == 128 || atoi(env) == 256)) s.nt = atoi(env);
     s.n_tblocks = (int)((batch + s.nt - 1) / s.nt);
+    // Fewer work items than the persistent grid holds (two workgroups per
+    // compute unit, 512): split each item's K range over 2 or 4 workgroups,
+    // each keeping >= 8 K-blocks; partial sums through the workspace.
+    const int64_t items = (int64_t)p->n_tiles * (p->tile_rows / 64) * s.n_tblocks;
+    const int nblk = p->n_dense_pad / HINM_KB_DENSE + p->n_24_pad / HINM_KB_24;
+    int splits = 1;
+    const char* es = getenv("HINM_PREFILL_SPLITS");
+    if (es && atoi(es) >= 1) {
+      splits = atoi(es) >= 4 ? 4 : (atoi(es) >= 2 ? 2 : 1);
+    } else {
+      while (splits < 4 && items * splits * 2 <= 512 && nblk / (splits * 2) >= 8) splits *= 2;
+    }
+    if (splits > 1 && items <= kWsCounters) {
+      s.splits = splits;
+      s.ws_counter_bytes = kWsCounterBytes;
+      s.ws_bytes = kWsCounterBytes + (int64_t)splits * items * 256 * s.nt;   // 256 threads x NT/4 floats
+    }
     return s;
   }
   s.path = kPathGeneric;

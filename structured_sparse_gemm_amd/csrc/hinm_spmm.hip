@@ -52,7 +52,7 @@ struct SpmmArgs {
   int n_rblocks, splits, n_kunits;
   int x_vec;                 // 1: 16-byte aligned X rows (ldx % 8 == 0)
   int y_vec;                 // 1: 16-byte aligned Y rows (ldy % 8 == 0)
-  int x_lds;                 // 1: the batch > 64 kernel loads X rows straight into LDS (needs x_vec)
+  int x_lds;                 // 1: the batch > 64 kernel loads X rows straight into LDS (256-token blocks)
   int n_tiles;
   const int32_t* out_rows;   // NULL, or the Y row of each product row
   const int32_t* tiles;      // NULL (uniform counts), or [n_tiles][4]: first dense block, n_dense,
@@ -1185,21 +1185,27 @@ __device__ inline void prefill_phase_lds(const SpmmArgs& a, const BufRes& res, u
 
 // FAST: 16-byte aligned X rows and a token block inside the batch; TAIL: the
 // token block ends past the batch (1: even batch, 2: odd batch).
+// The K range is split `splits` ways (blocks in order, dense first); this
+// call multiplies share `split` of it.
 template <int NT, bool FAST, int TAIL>
 __device__ inline void prefill_body(const SpmmArgs& a, const BufRes& res, uint16_t* xs0, uint16_t* xs1,
-                                    uint32_t* ms0, uint32_t* ms1, int t, int rb, int n0,
+                                    uint32_t* ms0, uint32_t* ms1, int t, int rb, int n0, int split, int splits,
                                     f32x16 (&acc)[2][PrefillCfg<NT>::NTB]) {
   const TileK tk = tile_k(a, t);
+  const int nblk = tk.nbd + tk.nbs;
+  const int lo = (int)((int64_t)split * nblk / splits), hi = (int)((int64_t)(split + 1) * nblk / splits);
+  const int d_lo = min(lo, tk.nbd), d_hi = min(hi, tk.nbd);
+  const int s_lo = max(lo, tk.nbd) - tk.nbd, s_hi = max(hi, tk.nbd) - tk.nbd;
   if constexpr (NT == 256) {
     if (a.x_lds) {
-      prefill_phase_lds<NT, true, TAIL>(a, res, xs0, xs1, ms0, ms1, tk.kd0, tk.nbd, rb, n0, acc);
-      prefill_phase_lds<NT, false, TAIL>(a, res, xs0, xs1, ms0, ms1, tk.ks0, tk.nbs, rb, n0, acc);
+      prefill_phase_lds<NT, true, TAIL>(a, res, xs0, xs1, ms0, ms1, tk.kd0 + d_lo, d_hi - d_lo, rb, n0, acc);
+      prefill_phase_lds<NT, false, TAIL>(a, res, xs0, xs1, ms0, ms1, tk.ks0 + s_lo, s_hi - s_lo, rb, n0, acc);
       return;
     }
   }
   {
-    prefill_phase<NT, FAST, true>(a, res, xs0, xs1, ms0, ms1, tk.kd0, tk.nbd, rb, n0, acc);
-    prefill_phase<NT, FAST, false>(a, res, xs0, xs1, ms0, ms1, tk.ks0, tk.nbs, rb, n0, acc);
+    prefill_phase<NT, FAST, true>(a, res, xs0, xs1, ms0, ms1, tk.kd0 + d_lo, d_hi - d_lo, rb, n0, acc);
+    prefill_phase<NT, FAST, false>(a, res, xs0, xs1, ms0, ms1, tk.ks0 + s_lo, s_hi - s_lo, rb, n0, acc);
   }
 }
 
@@ -1244,7 +1250,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
   // order cannot change the finish time and is skipped; tiles past the
   // order's LDS room keep their natural order.  The costs are staged in the
   // second X buffer, which no item has used yet.
-  const int items = n_tb * n_tr;
+  // With fewer items than the grid holds, each item's K range is split over
+  // `splits` workgroups (consecutive item numbers, so on one XCD); the
+  // partial sums meet through the workspace as in the split decode.
+  const int splits = a.splits;
+  const int n_items = n_tb * n_tr;
+  const int items = n_items * splits;
+  __shared__ int s_last;
   constexpr int kMaxOrdered = 1024;
   __shared__ int16_t order[kMaxOrdered];
   const bool ordered = a.tiles != nullptr && a.n_tiles <= kMaxOrdered && items > (int)gridDim.x;
@@ -1270,7 +1282,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
   const int i_lo = (int)((int64_t)xcd * items / 8), i_hi = (int)((int64_t)(xcd + 1) * items / 8);
   for (int it = i_lo + slot; it < i_hi; it += per_xcd) {
     {
-      const int tb = it / n_tr, trb = it % n_tr;
+      const int split = it % splits, item = it / splits;
+      const int tb = item / n_tr, trb = item % n_tr;
       const int n0 = tb * NT;
       int t = trb / nrb;
       const int rb = trb % nrb;
@@ -1281,14 +1294,53 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
           for (int e = 0; e < 16; ++e) acc[r][j][e] = 0.f;
 
       if (n0 + NT > a.batch) {
-        if (a.batch & 1) prefill_body<NT, false, 2>(a, res, xs[0], xs[1], ms[0], ms[1], t, rb, n0, acc);
-        else prefill_body<NT, false, 1>(a, res, xs[0], xs[1], ms[0], ms[1], t, rb, n0, acc);
+        if (a.batch & 1) prefill_body<NT, false, 2>(a, res, xs[0], xs[1], ms[0], ms[1], t, rb, n0, split, splits, acc);
+        else prefill_body<NT, false, 1>(a, res, xs[0], xs[1], ms[0], ms[1], t, rb, n0, split, splits, acc);
       } else if (a.x_vec) {
-        prefill_body<NT, true, 0>(a, res, xs[0], xs[1], ms[0], ms[1], t, rb, n0, acc);
+        prefill_body<NT, true, 0>(a, res, xs[0], xs[1], ms[0], ms[1], t, rb, n0, split, splits, acc);
       } else {
-        prefill_body<NT, false, 0>(a, res, xs[0], xs[1], ms[0], ms[1], t, rb, n0, acc);
+        prefill_body<NT, false, 0>(a, res, xs[0], xs[1], ms[0], ms[1], t, rb, n0, split, splits, acc);
       }
       __syncthreads();
+
+      if (splits > 1) {
+        // Partials part[split][item][NACC][thread] (the accumulators' own
+        // register order, lanes adjacent), through agent-scope (device-coherent) stores and
+        // loads; each workgroup waits for its stores before it counts itself
+        // in, and the last to arrive adds the partials in split order and
+        // puts the counter back to 0.
+        constexpr int NACC = 2 * C::NTB * 16;
+        unsigned* ctr = reinterpret_cast<unsigned*>(reinterpret_cast<char*>(a.ws) - hinm::kWsCounterBytes) + item;
+        float* my = a.ws + ((int64_t)split * n_items + item) * 256 * NACC + threadIdx.x;
+        for (int r = 0; r < 2; ++r)
+          for (int j = 0; j < C::NTB; ++j)
+            for (int e = 0; e < 16; ++e)
+              __hip_atomic_store(my + ((r * C::NTB + j) * 16 + e) * 256, acc[r][j][e], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0)
+          s_last = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(splits - 1);
+        __syncthreads();
+        if (!s_last) continue;
+        for (int r = 0; r < 2; ++r)
+          for (int j = 0; j < C::NTB; ++j)
+            for (int e = 0; e < 16; ++e) acc[r][j][e] = 0.f;
+        for (int sp = 0; sp < splits; ++sp) {
+          const float* ps = a.ws + ((int64_t)sp * n_items + item) * 256 * NACC + threadIdx.x;
+          for (int r = 0; r < 2; ++r)
+            for (int j = 0; j < C::NTB; ++j) {
+              float v[16];
+#pragma unroll
+              for (int e = 0; e < 16; ++e)
+                v[e] = __hip_atomic_load(ps + ((r * C::NTB + j) * 16 + e) * 256, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+              for (int e = 0; e < 16; ++e) acc[r][j][e] += v[e];
+            }
+        }
+        if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // next call
+      }
 
       // epilogue: acc[r][j][e] is row 32r + 8(e/4) + 4(lane/32) + e%4, token tok_w + 32j + lane%32.
       uint16_t* ys = xs[0];
@@ -1479,7 +1531,7 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
     }
   } else if (sh.path == hinm::kPathPrefill) {
     // persistent grid: 8 XCDs x (32 CUs x 2 workgroups), never more than the work items.
-    const int items = p.n_tiles * (p.tile_rows / 64) * sh.n_tblocks;
+    const int items = p.n_tiles * (p.tile_rows / 64) * sh.n_tblocks * sh.splits;
     int per_xcd = 64;
     const char* pe = getenv("HINM_PREFILL_PER_XCD");
     if (pe && atoi(pe) > 0) per_xcd = atoi(pe);

@@ -140,3 +140,43 @@ def test_prefill_last_x_row_ragged_tails(monkeypatch, layout):
         y = both_paths(monkeypatch, lambda: hinm.spmm(pk, xd))
         xf = synth.as_f64(x)
         check_y(y, oh.spmm(wh, xf), np.abs(wh) @ np.abs(xf), f"last row batch {b} {layout}")
+
+
+@pytest.mark.parametrize("splits", [2, 4])
+def test_prefill_split_k(monkeypatch, splits):
+    """Each work item's K range split over 2 or 4 workgroups (partial sums through the workspace, added
+    in split order): within the bar of the oracle, identical on both X paths, bit-identical from one
+    call to the next (the counters are back at zero), and ragged tails included."""
+    w = synth.small(256, 2048, 64, 0.6, 0.35, 1, seed=61)
+    pk = hinm.pack(w.w_bf16.to(DEV), w.importance.to(DEV), 64, 0.6, 0.35, w.perm.to(DEV))
+    _, _, inter = oracle_pack(w)
+    wh = oh.masked_weight(bits_of(w.w_bf16), inter["mask"])
+    monkeypatch.setenv("HINM_PREFILL_SPLITS", str(splits))
+    for b in (65, 200, 1031, 1100):
+        x = torch.randn(2048, b, generator=torch.Generator().manual_seed(b)).to(torch.bfloat16)
+        xd = x.to(DEV)
+        ws = torch.zeros(hinm.spmm_workspace_bytes(pk.plan, b), dtype=torch.uint8, device=DEV)
+        assert ws.numel() > 0
+        print(f"[prefill] split K {splits} ways, batch={b}", flush=True)
+        y = both_paths(monkeypatch, lambda: hinm.spmm(pk, xd, workspace=ws))
+        y2 = hinm.spmm(pk, xd, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+        assert not ws[:4 * 16384].any(), "arrival counters not back at zero"
+        xf = synth.as_f64(x)
+        check_y(y, oh.spmm(wh, xf), np.abs(wh) @ np.abs(xf), f"split K {splits}, batch {b}")
+
+
+def test_prefill_split_k_default_full_size():
+    """q_proj 4096x4096 at batch 128: 64 work items, so the default splits each one 4 ways."""
+    w = synth.q_proj(batch=16)
+    pk = hinm.pack(w.w_bf16.to(DEV), w.importance.to(DEV), 64, w.t_s, w.v_s, w.perm.to(DEV))
+    assert hinm.spmm_workspace_bytes(pk.plan, 128) > 0
+    _, _, inter = oracle_pack(w)
+    wh = oh.masked_weight(bits_of(w.w_bf16), inter["mask"])
+    x = torch.randn(4096, 128, generator=torch.Generator().manual_seed(128)).to(torch.bfloat16)
+    print("[prefill] q_proj batch 128, default K split", flush=True)
+    y = hinm.spmm(pk, x.to(DEV))
+    torch.cuda.synchronize()
+    xf = synth.as_f64(x)
+    check_y(y, oh.spmm(wh, xf), np.abs(wh) @ np.abs(xf), "q_proj batch 128")
