@@ -191,12 +191,21 @@ def test_pack_host_errors(lib):
     assert call(out=hinm.PackedT(p.raw, None, None, None, None, None)) == 1
 
 
-def test_workspace_sizes(lib):
+def test_workspace_sizes(lib, monkeypatch):
+    monkeypatch.delenv("HINM_PREFILL_SPLITS", raising=False)
+    counters = 16384 * 4
     p = hinm.plan(11008, 4096, 64, 0.75, 0.55)
-    for b in (0, 65, 2048, 4096):
+    for b in (0, 2048, 4096):                  # 1376 and 2752 work items: no K split
         assert hinm.spmm_workspace_bytes(p, b) == 0
+    # 172 items of 128 tokens: split 2 ways; per item and split 256 threads x 32 fp32 partials
+    assert hinm.spmm_workspace_bytes(p, 65) == counters + 2 * 172 * 256 * 128
     for b in (1, 16, 64):
         assert hinm.spmm_workspace_bytes(p, b) % 4 == 0
+    q = hinm.plan(4096, 4096, 64, 0.5, 0.25)   # 64 items at batch 128: split 4 ways
+    assert hinm.spmm_workspace_bytes(q, 128) == counters + 4 * 64 * 256 * 128
+    assert hinm.spmm_workspace_bytes(q, 1024) == counters + 2 * 256 * 256 * 256
+    monkeypatch.setenv("HINM_PREFILL_SPLITS", "1")
+    assert hinm.spmm_workspace_bytes(q, 128) == 0
     p = hinm.plan(96, 4096, 48, 0.75, 0.55)
     assert hinm.spmm_workspace_bytes(p, 200) % 256 == 0
 
