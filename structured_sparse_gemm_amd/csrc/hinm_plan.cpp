@@ -206,16 +206,18 @@ SpmmShape spmm_shape(const hinm_plan_t* p, int64_t batch) {
     const char* env = getenv("HINM_PREFILL_NT");
     if (env && (atoi(env) == 128 || atoi(env) == 256)) s.nt = atoi(env);
     s.n_tblocks = (int)((batch + s.nt - 1) / s.nt);
-    // Fewer work items than the persistent grid holds (two workgroups per
-    // compute unit, 512): split each item's K range over 2 or 4 workgroups,
-    // each keeping >= 8 K-blocks; partial sums through the workspace.
+    // Fewer work items than compute units: split each item's K range over 2
+    // or 4 workgroups (at most 512 in all, two per compute unit; each keeps
+    // >= 8 K-blocks); partial sums through the workspace.  With 256 items or
+    // more the partials' traffic costs more than the idle units: with the
+    // weight streamed from HBM, 2 splits at 256 items were slower.
     const int64_t items = (int64_t)p->n_tiles * (p->tile_rows / 64) * s.n_tblocks;
     const int nblk = p->n_dense_pad / HINM_KB_DENSE + p->n_24_pad / HINM_KB_24;
     int splits = 1;
     const char* es = getenv("HINM_PREFILL_SPLITS");
     if (es && atoi(es) >= 1) {
       splits = atoi(es) >= 4 ? 4 : (atoi(es) >= 2 ? 2 : 1);
-    } else {
+    } else if (items < 256) {
       while (splits < 4 && items * splits * 2 <= 512 && nblk / (splits * 2) >= 8) splits *= 2;
     }
     if (splits > 1 && items <= kWsCounters) {

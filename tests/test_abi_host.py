@@ -203,7 +203,7 @@ def test_workspace_sizes(lib, monkeypatch):
         assert hinm.spmm_workspace_bytes(p, b) % 4 == 0
     q = hinm.plan(4096, 4096, 64, 0.5, 0.25)   # 64 items at batch 128: split 4 ways
     assert hinm.spmm_workspace_bytes(q, 128) == counters + 4 * 64 * 256 * 128
-    assert hinm.spmm_workspace_bytes(q, 1024) == counters + 2 * 256 * 256 * 256
+    assert hinm.spmm_workspace_bytes(q, 512) == 0     # 256 items: no split
     monkeypatch.setenv("HINM_PREFILL_SPLITS", "1")
     assert hinm.spmm_workspace_bytes(q, 128) == 0
     p = hinm.plan(96, 4096, 48, 0.75, 0.55)
