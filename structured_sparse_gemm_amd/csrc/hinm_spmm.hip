@@ -375,7 +375,8 @@ struct BufRes {
 // ---------------------------------------------------------------------------
 // Decode kernel with split K and specialised waves (batch <= 64, tile_rows %
 // 64 == 0).  Workgroup = 64 rows of one tile x NTOK tokens x one K range;
-// waves 0-3 own 16 rows each, waves 4-5 gather X.  The index -> X-row chain
+// waves 0-3 own 16 rows each, the others (2 at 16 tokens, 4 at 32 and 64)
+// gather X.  The index -> X-row chain
 // is the latency-critical part, so the gather waves issue it first and the
 // row waves send only a few packed-value loads ahead of it; once the X loads
 // are on their way (one barrier) the row waves keep a fixed number of
@@ -410,12 +411,14 @@ __device__ inline int xs_gran(int p, int g) {
   else return 4 * p + (g ^ (((p >> 1) & 1) | (((p >> 3) & 1) << 1)));
 }
 
-template <int NTOK, int MAXB, bool FAST>
-__global__ __launch_bounds__(384) void decode5_kernel(SpmmArgs a, int splits, int n_tb, float* __restrict__ part,
-                                                      unsigned* __restrict__ counters) {
+template <int NTOK, int MAXB, bool FAST, int NG>
+__global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(SpmmArgs a, int splits, int n_tb,
+                                                                float* __restrict__ part,
+                                                                unsigned* __restrict__ counters) {
   constexpr int CPR = NTOK / 8;                // 16-byte chunks per X row
   constexpr int MAXP = MAXB * 64;              // LDS positions per round
-  constexpr int GT = 128;                      // gather threads
+  constexpr int GT = 64 * NG;                  // gather threads (NG gather waves)
+  static_assert(GT / CPR <= 64, "a gather step covers at most one block's positions per lane group");
   constexpr int MAXCH = MAXP * CPR / GT;       // X chunks per gather thread per round
   constexpr int NB = NTOK / 16;
   constexpr int DPF = MAXB < 8 ? MAXB : 8;   // packed-value blocks in flight ahead of the multiplies
@@ -1507,14 +1510,16 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
     const bool fast = a.x_vec && (batch % sh.nt == 0);
     unsigned* counters = static_cast<unsigned*>(workspace);
     float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + sh.ws_counter_bytes);
-    const dim3 grid(p.n_tiles * (p.tile_rows / 64) * sh.splits, sh.n_tblocks), block(384);
+    // 16 tokens: 24 blocks a round (48 KB of LDS), 2 gather waves; 32 and
+    // 64 tokens: 96 KB rounds (24 / 12 blocks) with 4 gather waves.
+    const dim3 grid(p.n_tiles * (p.tile_rows / 64) * sh.splits, sh.n_tblocks), b6(384), b8(512);
     switch (sh.nt * 2 + (fast ? 1 : 0)) {
-      case 33: hipLaunchKernelGGL((decode5_kernel<16, 24, true>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
-      case 32: hipLaunchKernelGGL((decode5_kernel<16, 24, false>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
-      case 65: hipLaunchKernelGGL((decode5_kernel<32, 12, true>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
-      case 64: hipLaunchKernelGGL((decode5_kernel<32, 12, false>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
-      case 129: hipLaunchKernelGGL((decode5_kernel<64, 6, true>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
-      default: hipLaunchKernelGGL((decode5_kernel<64, 6, false>), grid, block, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
+      case 33: hipLaunchKernelGGL((decode5_kernel<16, 24, true, 2>), grid, b6, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
+      case 32: hipLaunchKernelGGL((decode5_kernel<16, 24, false, 2>), grid, b6, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
+      case 65: hipLaunchKernelGGL((decode5_kernel<32, 24, true, 4>), grid, b8, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
+      case 64: hipLaunchKernelGGL((decode5_kernel<32, 24, false, 4>), grid, b8, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
+      case 129: hipLaunchKernelGGL((decode5_kernel<64, 12, true, 4>), grid, b8, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
+      default: hipLaunchKernelGGL((decode5_kernel<64, 12, false, 4>), grid, b8, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
     }
   } else if (sh.path == hinm::kPathDecode) {
     const dim3 grid(p.n_tiles * (p.tile_rows / 16), sh.n_tblocks), block(kDecWaves * 64);
