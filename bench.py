@@ -555,7 +555,7 @@ def main():
                    "algorithmic_bytes": algd["bytes"], "hbm_gbs": round(gbs_d, 1),
                    "roofline": {"bound": "hbm", "achieved": round(gbs_d, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": round(gbs_d / HBM_PEAK_GBS, 4), "traffic": measured_traffic(Bd),
-                                "kernel": "decode5_kernel<16,24,true> (one launch per call)"},
+                                "kernel": "decode5_kernel<16,24,true,2> (one launch per call)"},
                    "useful_tflops": round(algd["useful_flops"] / (rd["ms_mean"] * 1e-3) / 1e12, 3),
                    "rotation_copies": rotd.k},
         "batch_2048_hbm_gbs": round(alg["bytes"] / (ms * 1e-3) / 1e9, 1),
