@@ -376,25 +376,24 @@ struct BufRes {
 // Decode kernel with split K and specialised waves (batch <= 64, tile_rows %
 // 64 == 0).  Workgroup = 64 rows of one tile x NTOK tokens x one K range;
 // waves 0-3 own 16 rows each, the others (2 at 16 tokens, 4 at 32 and 64)
-// gather X.  The index -> X-row chain
-// is the latency-critical part, so the gather waves issue it first and the
-// row waves send only a few packed-value loads ahead of it; once the X loads
-// are on their way (one barrier) the row waves keep a fixed number of
-// blocks in flight ahead of their multiplies.  The two roles sit in
-// different waves, so the X rows never wait behind the packed values in a
-// wave's in-order load queue.  A K range longer than one LDS round is
-// processed in rounds, each role issuing the next round's loads as soon as
-// its registers are free.
+// gather X.  The index -> X-row chain is the latency-critical part, so the
+// gather waves issue it first and the row waves send only a few
+// packed-value loads ahead of it; once the X loads are on their way (one
+// barrier) the row waves keep a fixed number of blocks in flight ahead of
+// their multiplies.  The two roles sit in different waves, so the X rows
+// never wait behind the packed values in a wave's in-order load queue.  A K
+// range longer than one LDS round is processed in rounds, each role issuing
+// the next round's loads as soon as its registers are free.
 //
 // Every block, dense or 2:4, takes 64 LDS positions and one
 // v_smfmac_f32_16x16x64_bf16: a dense block's 32 columns sit at positions
 // 4q and 4q+1 of its groups (column 2q+e at position 4q+e; positions 4q+2
 // and 4q+3 hold zeros) and use the fixed index pattern 0x4 (positions 0 and
 // 1 of every group), which is exactly the dense product because the A
-// operand of a dense block is its 32 values in order.  The multiply loop is then the same straight-line code for every
-// block: blocks past the K range get zero values and zero X rows, and blocks
-// alternate between two accumulators so consecutive SMFMACs do not wait on
-// each other.
+// operand of a dense block is its 32 values in order.  The multiply loop is
+// then the same straight-line code for every block: blocks past the K range
+// get zero values and zero X rows, and blocks alternate between two
+// accumulators so consecutive SMFMACs do not wait on each other.
 // ---------------------------------------------------------------------------
 // LDS layout of the gathered X rows in the split decode kernel: position p
 // holds its NB = NTOK/16 groups of 16 tokens as 32-byte granules, granule g
@@ -1308,10 +1307,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
 
       if (splits > 1) {
         // Partials part[split][item][NACC][thread] (the accumulators' own
-        // register order, lanes adjacent), through agent-scope (device-coherent) stores and
-        // loads; each workgroup waits for its stores before it counts itself
-        // in, and the last to arrive adds the partials in split order and
-        // puts the counter back to 0.
+        // register order, lanes adjacent) through agent-scope
+        // (device-coherent) stores and loads; each workgroup waits for its
+        // stores before it counts itself in, and the last to arrive adds the
+        // partials in split order and puts the counter back to 0.
         constexpr int NACC = 2 * C::NTB * 16;
         unsigned* ctr = reinterpret_cast<unsigned*>(reinterpret_cast<char*>(a.ws) - hinm::kWsCounterBytes) + item;
         float* my = a.ws + ((int64_t)split * n_items + item) * 256 * NACC + threadIdx.x;
