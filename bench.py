@@ -534,7 +534,7 @@ def main():
                    "batch": B, "regions_per_tile": {"dense": p.n_dense, "two_four": p.n_24, "pruned": p.n_pruned}},
         "roofline": {"bound": "mfma", "achieved": round(value, 3), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(value / MFMA_BF16_PEAK_TFLOPS, 5), "traffic": measured_traffic(B),
-                     "kernel": "prefill_kernel<256> (one launch per step)",
+                     "kernel": "prefill_kernel<256, false> (one launch per step)",
                      "kernel_source_hash": kernel_source_hash(),
                      "per_launch": {"useful_flops": alg["useful_flops"], "algorithmic_bytes": alg["bytes"],
                                     "ms_mean": round(ms, 5),

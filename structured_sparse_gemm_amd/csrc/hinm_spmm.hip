@@ -1187,28 +1187,37 @@ __device__ inline void prefill_phase_lds(const SpmmArgs& a, const BufRes& res, u
 
 // FAST: 16-byte aligned X rows and a token block inside the batch; TAIL: the
 // token block ends past the batch (1: even batch, 2: odd batch).
-// The K range is split `splits` ways (blocks in order, dense first); this
-// call multiplies share `split` of it.
-template <int NT, bool FAST, int TAIL>
-__device__ inline void prefill_body(const SpmmArgs& a, const BufRes& res, uint16_t* xs0, uint16_t* xs1,
-                                    uint32_t* ms0, uint32_t* ms1, int t, int rb, int n0, int split, int splits,
-                                    f32x16 (&acc)[2][PrefillCfg<NT>::NTB]) {
-  const TileK tk = tile_k(a, t);
+// Share `split` of an item's K range split `splits` ways (blocks in order,
+// dense first): the first dense and 2:4 block and the counts.
+struct KShare {
+  int kd, nd, ks, ns;
+};
+__device__ inline KShare k_share(const TileK& tk, int split, int splits) {
   const int nblk = tk.nbd + tk.nbs;
   const int lo = (int)((int64_t)split * nblk / splits), hi = (int)((int64_t)(split + 1) * nblk / splits);
   const int d_lo = min(lo, tk.nbd), d_hi = min(hi, tk.nbd);
   const int s_lo = max(lo, tk.nbd) - tk.nbd, s_hi = max(hi, tk.nbd) - tk.nbd;
-  if constexpr (NT == 256) {
-    if (a.x_lds) {
-      prefill_phase_lds<NT, true, TAIL>(a, res, xs0, xs1, ms0, ms1, tk.kd0 + d_lo, d_hi - d_lo, rb, n0, acc);
-      prefill_phase_lds<NT, false, TAIL>(a, res, xs0, xs1, ms0, ms1, tk.ks0 + s_lo, s_hi - s_lo, rb, n0, acc);
-      return;
-    }
-  }
-  {
-    prefill_phase<NT, FAST, true>(a, res, xs0, xs1, ms0, ms1, tk.kd0 + d_lo, d_hi - d_lo, rb, n0, acc);
-    prefill_phase<NT, FAST, false>(a, res, xs0, xs1, ms0, ms1, tk.ks0 + s_lo, s_hi - s_lo, rb, n0, acc);
-  }
+  return {tk.kd0 + d_lo, d_hi - d_lo, tk.ks0 + s_lo, s_hi - s_lo};
+}
+
+// X straight into LDS; TAIL: the token block ends past the batch (1: even
+// batch, 2: odd batch).
+template <int NT, int TAIL>
+__device__ inline void prefill_body_lds(const SpmmArgs& a, const BufRes& res, uint16_t* xs0, uint16_t* xs1,
+                                        uint32_t* ms0, uint32_t* ms1, const KShare& ks, int rb, int n0,
+                                        f32x16 (&acc)[2][PrefillCfg<NT>::NTB]) {
+  prefill_phase_lds<NT, true, TAIL>(a, res, xs0, xs1, ms0, ms1, ks.kd, ks.nd, rb, n0, acc);
+  prefill_phase_lds<NT, false, TAIL>(a, res, xs0, xs1, ms0, ms1, ks.ks, ks.ns, rb, n0, acc);
+}
+
+// X through registers; FAST: 16-byte aligned X rows and a token block inside
+// the batch.
+template <int NT, bool FAST>
+__device__ inline void prefill_body_staged(const SpmmArgs& a, const BufRes& res, uint16_t* xs0, uint16_t* xs1,
+                                           uint32_t* ms0, uint32_t* ms1, const KShare& ks, int rb, int n0,
+                                           f32x16 (&acc)[2][PrefillCfg<NT>::NTB]) {
+  prefill_phase<NT, FAST, true>(a, res, xs0, xs1, ms0, ms1, ks.kd, ks.nd, rb, n0, acc);
+  prefill_phase<NT, FAST, false>(a, res, xs0, xs1, ms0, ms1, ks.ks, ks.ns, rb, n0, acc);
 }
 
 // Persistent launch: gridDim.x = 8 * per_xcd workgroups, workgroup L runs on
@@ -1216,7 +1225,7 @@ __device__ inline void prefill_body(const SpmmArgs& a, const BufRes& res, uint16
 // token-block major, are cut into 8 contiguous ranges, one per XCD; the XCD's
 // workgroups take its range in order, so each XCD works through its token
 // blocks one after another and keeps the current X slice in its L2.
-template <int NT>
+template <int NT, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
   using C = PrefillCfg<NT>;
   __shared__ __attribute__((aligned(16))) uint16_t xs_a[64 * C::PITCH];
@@ -1255,7 +1264,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
   // With fewer items than the grid holds, each item's K range is split over
   // `splits` workgroups (consecutive item numbers, so on one XCD); the
   // partial sums meet through the workspace as in the split decode.
-  const int splits = a.splits;
+  const int splits = SPLIT ? a.splits : 1;
   const int n_items = n_tb * n_tr;
   const int items = n_items * splits;
   __shared__ int s_last;
@@ -1284,7 +1293,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
   const int i_lo = (int)((int64_t)xcd * items / 8), i_hi = (int)((int64_t)(xcd + 1) * items / 8);
   for (int it = i_lo + slot; it < i_hi; it += per_xcd) {
     {
-      const int split = it % splits, item = it / splits;
+      const int split = SPLIT ? it % splits : 0, item = SPLIT ? it / splits : it;
       const int tb = item / n_tr, trb = item % n_tr;
       const int n0 = tb * NT;
       int t = trb / nrb;
@@ -1295,17 +1304,25 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
         for (int j = 0; j < C::NTB; ++j)
           for (int e = 0; e < 16; ++e) acc[r][j][e] = 0.f;
 
-      if (n0 + NT > a.batch) {
-        if (a.batch & 1) prefill_body<NT, false, 2>(a, res, xs[0], xs[1], ms[0], ms[1], t, rb, n0, split, splits, acc);
-        else prefill_body<NT, false, 1>(a, res, xs[0], xs[1], ms[0], ms[1], t, rb, n0, split, splits, acc);
-      } else if (a.x_vec) {
-        prefill_body<NT, true, 0>(a, res, xs[0], xs[1], ms[0], ms[1], t, rb, n0, split, splits, acc);
+      const TileK tk = tile_k(a, t);
+      const KShare ks = SPLIT ? k_share(tk, split, splits) : KShare{tk.kd0, tk.nbd, tk.ks0, tk.nbs};
+      const bool tail = n0 + NT > a.batch;
+      bool direct = false;
+      if constexpr (NT == 256) direct = a.x_lds;
+      if (direct) {
+        if constexpr (NT == 256) {
+          if (!tail) prefill_body_lds<NT, 0>(a, res, xs[0], xs[1], ms[0], ms[1], ks, rb, n0, acc);
+          else if (a.batch & 1) prefill_body_lds<NT, 2>(a, res, xs[0], xs[1], ms[0], ms[1], ks, rb, n0, acc);
+          else prefill_body_lds<NT, 1>(a, res, xs[0], xs[1], ms[0], ms[1], ks, rb, n0, acc);
+        }
+      } else if (a.x_vec && !tail) {
+        prefill_body_staged<NT, true>(a, res, xs[0], xs[1], ms[0], ms[1], ks, rb, n0, acc);
       } else {
-        prefill_body<NT, false, 0>(a, res, xs[0], xs[1], ms[0], ms[1], t, rb, n0, split, splits, acc);
+        prefill_body_staged<NT, false>(a, res, xs[0], xs[1], ms[0], ms[1], ks, rb, n0, acc);
       }
       __syncthreads();
 
-      if (splits > 1) {
+      if constexpr (SPLIT) {
         // Partials part[split][item][NACC][thread] (the accumulators' own
         // register order, lanes adjacent) through agent-scope
         // (device-coherent) stores and loads; each workgroup waits for its
@@ -1540,10 +1557,14 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
     const char* pe = getenv("HINM_PREFILL_PER_XCD");
     if (pe && atoi(pe) > 0) per_xcd = atoi(pe);
     const int nwg = 8 * std::min(per_xcd, (items + 7) / 8);
+    // the K-split epilogue is a separate instantiation, so the unsplit
+    // kernel keeps its registers
     if (sh.nt == 256) {
-      hipLaunchKernelGGL(prefill_kernel<256>, dim3(nwg), dim3(256), 0, stream, a, sh.n_tblocks);
+      if (sh.splits > 1) hipLaunchKernelGGL((prefill_kernel<256, true>), dim3(nwg), dim3(256), 0, stream, a, sh.n_tblocks);
+      else hipLaunchKernelGGL((prefill_kernel<256, false>), dim3(nwg), dim3(256), 0, stream, a, sh.n_tblocks);
     } else {
-      hipLaunchKernelGGL(prefill_kernel<128>, dim3(nwg), dim3(256), 0, stream, a, sh.n_tblocks);
+      if (sh.splits > 1) hipLaunchKernelGGL((prefill_kernel<128, true>), dim3(nwg), dim3(256), 0, stream, a, sh.n_tblocks);
+      else hipLaunchKernelGGL((prefill_kernel<128, false>), dim3(nwg), dim3(256), 0, stream, a, sh.n_tblocks);
     }
   } else {
     const dim3 grid(sh.n_tblocks, p.n_tiles * sh.n_rblocks, sh.splits), block(kWaves * 64);
