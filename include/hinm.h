@@ -220,12 +220,9 @@ int hinm_spmm_workspace_bytes(const hinm_plan_t* plan, int64_t batch, size_t* by
  * split), HINM_PREFILL_PATH = staged (the batch > 64 kernel gathers X
  * through registers instead of loading it straight into LDS; same result
  * bits), HINM_PREFILL_SPLITS = 1 | 2 | 4 (K split of each batch > 64 work
- * item; by default 2 or 4 when there are fewer than 256 items, which
- * changes the last bits of Y), HINM_PREFILL_TB_GROUP = n > 0 (256-token
- * blocks that share each XCD's tiles; by default the largest power of two
- * whose X slices fit a 4 MB L2; ignored unless it divides the token blocks
- * and the tiles; same result bits).  The workspace size asked for must come
- * from the same settings.
+ * item; by default 2 or 4 when there are fewer than 512 items, which
+ * changes the last bits of Y).  The workspace size asked for must come from
+ * the same settings.
  * Errors (host-side checks only): HINM_EINVAL, HINM_ESHAPE, HINM_EALIGN,
  * HINM_EWORKSPACE, HINM_EHIP (launch failure). */
 int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_t batch, int64_t ldx,

@@ -53,7 +53,6 @@ struct SpmmArgs {
   int x_vec;                 // 1: 16-byte aligned X rows (ldx % 8 == 0)
   int y_vec;                 // 1: 16-byte aligned Y rows (ldy % 8 == 0)
   int x_lds;                 // 1: the batch > 64 kernel loads X rows straight into LDS (256-token blocks)
-  int tb_group;              // batch > 64 item order: token blocks that share one XCD's tiles (1: token-block major)
   int n_tiles;
   const int32_t* out_rows;   // NULL, or the Y row of each product row
   const int32_t* tiles;      // NULL (uniform counts), or [n_tiles][4]: first dense block, n_dense,
@@ -1223,10 +1222,9 @@ __device__ inline void prefill_body_staged(const SpmmArgs& a, const BufRes& res,
 
 // Persistent launch: gridDim.x = 8 * per_xcd workgroups, workgroup L runs on
 // XCD L % 8 (round-robin dispatch).  The (token block, tile row block) items,
-// token-block major (or in groups of a.tb_group token blocks, tile-major
-// inside a group), are cut into 8 contiguous ranges, one per XCD; the XCD's
+// token-block major, are cut into 8 contiguous ranges, one per XCD; the XCD's
 // workgroups take its range in order, so each XCD works through its token
-// blocks one after another and keeps the current X slices in its L2.
+// blocks one after another and keeps the current X slice in its L2.
 template <int NT, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
   using C = PrefillCfg<NT>;
@@ -1296,17 +1294,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
   for (int it = i_lo + slot; it < i_hi; it += per_xcd) {
     {
       const int split = SPLIT ? it % splits : 0, item = SPLIT ? it / splits : it;
-      int tb = item / n_tr, trb = item % n_tr;
-      if (!SPLIT && !ordered && a.tb_group > 1) {
-        // Groups of tb_group token blocks; within a group, tile-major runs of
-        // n_tr items take tb_group token blocks of n_tr / tb_group tiles each,
-        // so the XCD that holds a run reads those tiles' packed values once
-        // for several token blocks.
-        const int gsz = a.tb_group * n_tr, g = item / gsz, j = item % gsz;
-        const int c = j / n_tr, r = j % n_tr;
-        tb = g * a.tb_group + r % a.tb_group;
-        trb = c * (n_tr / a.tb_group) + r / a.tb_group;
-      }
+      const int tb = item / n_tr, trb = item % n_tr;
       const int n0 = tb * NT;
       int t = trb / nrb;
       const int rb = trb % nrb;
@@ -1500,7 +1488,6 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
     const char* pp = getenv("HINM_PREFILL_PATH");
     a.x_lds = !(pp && strcmp(pp, "staged") == 0);
   }
-  a.tb_group = 1;
   a.y_vec = hinm::aligned(y_bf16, 16) && (ldy % 8 == 0);
   a.n_tiles = p.n_tiles;
   a.out_rows = out_rows;
@@ -1570,21 +1557,6 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
     const char* pe = getenv("HINM_PREFILL_PER_XCD");
     if (pe && atoi(pe) > 0) per_xcd = atoi(pe);
     const int nwg = 8 * std::min(per_xcd, (items + 7) / 8);
-    // Item order at 256-token blocks: the largest power of two of token
-    // blocks whose X slices (cin x 256 tokens, 2 bytes each) fit one XCD's
-    // 4 MB L2 together share each XCD's tiles, so fewer XCDs read each
-    // tile's packed values.  Past the L2 the X re-reads cost more than the
-    // packed values saved (cin 11008: 5.6 MB a slice, no grouping).
-    a.tb_group = 1;
-    if (sh.nt == 256 && sh.splits == 1) {
-      const int n_tr = p.n_tiles * (p.tile_rows / 64);
-      const int64_t slice = (int64_t)p.cin * 256 * 2;
-      int g = 1;
-      while (g < 8 && 2 * g * slice <= (4 << 20) && sh.n_tblocks % (2 * g) == 0 && n_tr % (2 * g) == 0) g *= 2;
-      const char* ge = getenv("HINM_PREFILL_TB_GROUP");
-      if (ge && atoi(ge) > 0) g = atoi(ge);
-      if (g > 1 && sh.n_tblocks % g == 0 && n_tr % g == 0) a.tb_group = g;
-    }
     // the K-split epilogue is a separate instantiation, so the unsplit
     // kernel keeps its registers
     if (sh.nt == 256) {

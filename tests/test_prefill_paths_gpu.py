@@ -180,31 +180,3 @@ def test_prefill_split_k_default_full_size():
     torch.cuda.synchronize()
     xf = synth.as_f64(x)
     check_y(y, oh.spmm(wh, xf), np.abs(wh) @ np.abs(xf), "q_proj batch 128")
-
-
-def test_prefill_tb_group_full_size(monkeypatch):
-    """q_proj 4096x4096 at batch 2048 (8 token blocks of 256, 64 tiles): the default item order pairs token
-    blocks on each XCD (two 2 MB X slices fit a 4 MB L2).  Every item still adds the same products in the
-    same order, so groups of 1, 2, 4 and 8 token blocks give bit-identical Y; sampled rows meet the bar
-    against the oracle."""
-    w = synth.q_proj(batch=16)
-    pk = hinm.pack(w.w_bf16.to(DEV), w.importance.to(DEV), 64, w.t_s, w.v_s, w.perm.to(DEV))
-    x = torch.randn(4096, 2048, generator=torch.Generator().manual_seed(2048)).to(torch.bfloat16)
-    xd = x.to(DEV)
-    ys = {}
-    for g in ("1", "2", "4", "8", None):
-        if g is None:
-            monkeypatch.delenv("HINM_PREFILL_TB_GROUP", raising=False)
-        else:
-            monkeypatch.setenv("HINM_PREFILL_TB_GROUP", g)
-        print(f"[prefill] q_proj batch 2048, token-block group {g or 'default'}", flush=True)
-        ys[g] = hinm.spmm(pk, xd)
-    torch.cuda.synchronize()
-    for g, y in ys.items():
-        assert torch.equal(y.view(torch.int16), ys["1"].view(torch.int16)), f"group {g} differs from group 1"
-    _, _, inter = oracle_pack(w)
-    rows = np.arange(5, 4096, 97)
-    wh = oh.masked_weight(bits_of(w.w_bf16), inter["mask"])[rows]
-    xf = synth.as_f64(x)
-    check_y(ys[None][torch.as_tensor(rows, device=DEV)], oh.spmm(wh, xf), np.abs(wh) @ np.abs(xf),
-            "q_proj batch 2048 sampled rows")
