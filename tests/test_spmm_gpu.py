@@ -270,3 +270,32 @@ def test_spmm_decode_ragged_full_width(unaligned):
         torch.cuda.synchronize()
         xf = synth.as_f64(x)
         check_y(y, oh.spmm(c.w_hat, xf), np.abs(c.w_hat) @ np.abs(xf), f"q_proj batch {b}")
+
+
+@pytest.mark.parametrize("batch", [16, 100])
+def test_spmm_x_beyond_32bit_offsets(batch):
+    """X whose row stride puts its last row past 2^31 bytes (4096 rows of 300000 elements, 2.46 GB).
+    The split decode and the batch > 64 kernel address X with 32-bit buffer offsets, so such a call
+    takes the 64-bit-addressed kernels (batch <= 64: the unsplit decode; batch > 64: the generic
+    LDS-gather kernel).  Sampled rows against the oracle; the same X copied contiguous (32-bit
+    kernels) meets the same bar."""
+    c = Case(synth.q_proj(batch=16))
+    g = torch.Generator().manual_seed(31 + batch)
+    x = torch.randn(4096, batch, generator=g).to(torch.bfloat16)
+    ldx = 300000
+    assert (4095 * ldx + batch) * 2 > 2**31
+    big = torch.zeros(4096, ldx, dtype=torch.bfloat16, device=DEV)
+    big[:, :batch].copy_(x.to(DEV))
+    print(f"[spmm]   batch={batch} ldx={ldx} (X past 2^31 bytes)", flush=True)
+    y = hinm.spmm(c.pk, big[:, :batch])
+    torch.cuda.synchronize()
+    del big
+    rows = sample_rows(4096)
+    xf = synth.as_f64(x)
+    wh = c.w_hat[rows]
+    ref, scale = oh.spmm(wh, xf), np.abs(wh) @ np.abs(xf)
+    ridx = torch.as_tensor(rows, device=DEV)
+    check_y(y[ridx], ref, scale, f"q_proj batch {batch}, X past 2^31 bytes")
+    y32 = hinm.spmm(c.pk, x.to(DEV))
+    torch.cuda.synchronize()
+    check_y(y32[ridx], ref, scale, f"q_proj batch {batch}, contiguous X")
