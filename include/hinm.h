@@ -220,7 +220,7 @@ int hinm_spmm_workspace_bytes(const hinm_plan_t* plan, int64_t batch, size_t* by
  * split), HINM_PREFILL_PATH = staged (the batch > 64 kernel gathers X
  * through registers instead of loading it straight into LDS; same result
  * bits), HINM_PREFILL_SPLITS = 1 | 2 | 4 (K split of each batch > 64 work
- * item; by default 2 or 4 when there are fewer than 512 items, which
+ * item; by default 2 or 4 when there are fewer than 256 items, which
  * changes the last bits of Y).  The workspace size asked for must come from
  * the same settings.
  * Errors (host-side checks only): HINM_EINVAL, HINM_ESHAPE, HINM_EALIGN,
