@@ -1162,10 +1162,15 @@ __device__ inline void prefill_phase_lds(const SpmmArgs& a, const BufRes& res, u
   __syncthreads();
   auto step = [&](auto kc, int bb) {
     constexpr int k = decltype(kc)::value;
+    // Raised priority while the wave issues its loads, so that on a SIMD
+    // shared with the other workgroup the gathers go out ahead of that
+    // workgroup's MFMA and LDS work and more lines stay in flight.
+    __builtin_amdgcn_s_setprio(2);
     if (bb + 1 < nb) load_x(CI, tile[(k + 1) % 2]);   // X(bb+1)
     else fixm = 0;
     Iw[(k + 1) % 2] = load_idx(bb + 3);
     load_a(bb + DA, A[k % DA]);
+    __builtin_amdgcn_s_setprio(0);
     compute(tile[k % 2], mtile[k % 2]);
     store_a(tile[(k + 1) % 2], mtile[(k + 1) % 2], A[(k + 1) % DA]);
     spread_idx(Iw[k % 2], CI);        // indices of bb+2
