@@ -331,6 +331,35 @@ def cpu_baseline(w, batch):
             "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
+
+def cpu_baseline_boundary(wb):
+    """CPU-baseline leg for the boundary-search row: the oracle's cost of one grid point of the same search
+    (retained importance at v_s 0.6, t_s 0.7), the vector scores computed beforehand."""
+    import oracle.hinm as oh
+    p_b = oh.plan(wb.cout, wb.cin, 64, 0.7, 0.7)
+    s_b = oh.vector_scores(wb.importance.numpy(), p_b)
+    t0 = time.perf_counter()
+    oh.retained_importance(wb.importance.numpy(), wb.perm.numpy(), oh.plan(wb.cout, wb.cin, 64, 0.7, 0.6), s_b)
+    return {"oracle_s_per_grid_point": round(time.perf_counter() - t0, 3),
+            "oracle_sample": "one grid point (v_s 0.6) of the same search, scores precomputed"}
+
+
+def cpu_baseline_gyro(w, g_sample, g_init, g_cs, g_it):
+    """CPU-baseline leg for the gyro-permutation row: one oracle round on tiles 0 and 1 with the same draws,
+    scaled to all tiles."""
+    import oracle.gyro as og
+    import oracle.hinm as oh
+    dd = w.importance.numpy()
+    op = oh.plan(w.cout, w.cin, w.tile_rows, w.t_s, w.v_s)
+    reg = oh.regions(oh.vector_scores(dd, op), op)
+    _, idx_s = oh.index_lists(reg, w.perm.numpy().astype("int64"), op)
+    t0 = time.perf_counter()
+    for t in range(2):
+        og.gyro_round(dd[t * 64:(t + 1) * 64], idx_s[t, :op.n_24].reshape(op.groups, 4).astype("int64"),
+                      g_sample[0, t].astype("int64"), g_init[0, t].astype("int64"), g_cs, g_it)
+    return {"oracle_s_per_round_all_tiles": round((time.perf_counter() - t0) / 2 * op.n_tiles, 2),
+            "oracle_sample": "one round on tiles 0 and 1, scaled to all tiles"}
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -418,13 +447,7 @@ def main():
                        "t_s 0.7 (synchronous: checks, scores, ranking, then one device pass and one host read per grid "
                        "point)", "ms": [round(x, 2) for x in bs_ms], "v_s": v_b, "grid_points": len(tr_b)}
     if not args.no_cpu:
-        import oracle.hinm as oh
-        p_b = oh.plan(wb_.cout, wb_.cin, 64, 0.7, 0.7)
-        s_b = oh.vector_scores(wb_.importance.numpy(), p_b)
-        t0 = time.perf_counter()
-        oh.retained_importance(wb_.importance.numpy(), wb_.perm.numpy(), oh.plan(wb_.cout, wb_.cin, 64, 0.7, 0.6), s_b)
-        next_bs["oracle_s_per_grid_point"] = round(time.perf_counter() - t0, 3)
-        next_bs["oracle_sample"] = "one grid point (v_s 0.6) of the same search, scores precomputed"
+        next_bs.update(cpu_baseline_boundary(wb_))
 
     # NEXT row: per-tile v_s (per-tile boundary search on the same weight and importance, then the
     # per-tile layout), products timed like the uniform ones but without buffer rotation
@@ -505,18 +528,7 @@ def main():
                  "cost_removed_frac": round(float(1 - g_trace[-1].sum() / g_trace[0].sum()), 5),
                  "total_importance": round(tot24, 3)}
     if not args.no_cpu:
-        import oracle.gyro as og
-        import oracle.hinm as oh
-        dd = w.importance.numpy()
-        op = oh.plan(w.cout, w.cin, w.tile_rows, w.t_s, w.v_s)
-        reg = oh.regions(oh.vector_scores(dd, op), op)
-        _, idx_s = oh.index_lists(reg, w.perm.numpy().astype("int64"), op)
-        t0 = time.perf_counter()
-        for t in range(2):
-            og.gyro_round(dd[t * 64:(t + 1) * 64], idx_s[t, :op.n_24].reshape(op.groups, 4).astype("int64"),
-                          g_sample[0, t].astype("int64"), g_init[0, t].astype("int64"), g_cs, g_it)
-        next_gyro["oracle_s_per_round_all_tiles"] = round((time.perf_counter() - t0) / 2 * p.n_tiles, 2)
-        next_gyro["oracle_sample"] = "one round on tiles 0 and 1, scaled to all tiles"
+        next_gyro.update(cpu_baseline_gyro(w, g_sample, g_init, g_cs, g_it))
 
     dense = None
     if not args.no_dense:
