@@ -1,7 +1,8 @@
 """CPU oracle for the HiNM sparse-weight x dense-activation product (test infrastructure).
 
 This package is test infrastructure.  Only ``tests/``, ``__graft_entry__.smoke()``
-and the ``cpu_baseline`` leg of ``bench.py`` may import or call it; the product
+and the CPU-baseline leg of ``bench.py`` (``cpu_baseline`` and its side-row
+functions) may import or call it; the product
 path (the HIP library and its Python binding) never does, and shares no code,
 header, table or constant with it.
 

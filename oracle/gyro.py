@@ -1,7 +1,7 @@
 """CPU oracle of the in-tile input-channel gyro permutation.
 
-TEST INFRASTRUCTURE ONLY: imported by tests/ and the cpu_baseline leg of
-bench.py, never by the product path.
+TEST INFRASTRUCTURE ONLY: imported by tests/ and the CPU-baseline leg of
+bench.py (cpu_baseline_gyro), never by the product path.
 
 Source: FlexHiNM-GP paper notes, key design 2 (陀螺置换, gyro permutation).
 The notes state the objective, argmax over the output and input channel

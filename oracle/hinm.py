@@ -1,7 +1,8 @@
 """Step-by-step CPU oracle of the HiNM (hierarchical N:M) pack and product.
 
 TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
-cpu_baseline leg of bench.py, never by the product path.
+CPU-baseline leg of bench.py (cpu_baseline, cpu_baseline_boundary), never by the
+product path.
 
 Sources (cited by page title and section; the pages are the FlexHiNM-GP paper
 notes, an article on N:M block sparsity, an article on 2:4 structured
