@@ -778,3 +778,53 @@ def test_mutation_gyro_maximising_assignment_is_caught(monkeypatch):
     monkeypatch.setattr(og, "hungarian", lambda c: orig(-np.asarray(c)))
     with pytest.raises(AssertionError):
         test_gyro_one_cluster_round_is_the_brute_force_optimum()
+
+
+def _kmeans_cases():
+    with open(os.path.join(GOLDEN, "gyro_kmeans_handworked.json")) as f:
+        return json.load(f)["cases"]
+
+
+def test_balanced_kmeans_handworked():
+    """Hand-worked cases (tests/golden/gyro_kmeans_handworked.json): the centroid update changes the
+    second assignment step, squared euclidean and L1 distances pick different clusters, and equal
+    distances go to the lower cluster and the lower point first."""
+    for c in _kmeans_cases():
+        label = og.balanced_kmeans(np.array(c["points"], dtype=np.float64), np.array(c["init"]), c["iters"],
+                                   np.array(c["caps"], dtype=np.int64))
+        assert label.tolist() == c["labels"], c["name"]
+
+
+def test_mutation_kmeans_without_update_is_caught(monkeypatch):
+    def frozen(points, init, iters, caps):
+        cents = points[np.asarray(init, dtype=np.int64)].copy()
+        label = None
+        for _ in range(iters):
+            label = og.balanced_assign(og.sq_dist(points, cents), caps)
+        return label
+    monkeypatch.setattr(og, "balanced_kmeans", frozen)
+    with pytest.raises(AssertionError):
+        test_balanced_kmeans_handworked()
+
+
+def test_mutation_kmeans_l1_distance_is_caught(monkeypatch):
+    monkeypatch.setattr(og, "sq_dist", lambda p, c: np.abs(p[:, None, :] - c[None, :, :]).sum(axis=-1))
+    with pytest.raises(AssertionError):
+        test_balanced_kmeans_handworked()
+
+
+@pytest.mark.parametrize("reverse", ["cluster", "point"])
+def test_mutation_kmeans_reversed_tie_order_is_caught(monkeypatch, reverse):
+    def assign(dist, caps):
+        g, n = dist.shape
+        qs, ks = np.repeat(np.arange(g), n), np.tile(np.arange(n), g)
+        keys = (-ks, qs, dist.reshape(-1)) if reverse == "cluster" else (ks, -qs, dist.reshape(-1))
+        label, room = np.full(g, -1, dtype=np.int64), caps.copy()
+        for e in np.lexsort(keys):
+            if label[qs[e]] < 0 and room[ks[e]] > 0:
+                label[qs[e]] = ks[e]
+                room[ks[e]] -= 1
+        return label
+    monkeypatch.setattr(og, "balanced_assign", assign)
+    with pytest.raises(AssertionError):
+        test_balanced_kmeans_handworked()
