@@ -36,6 +36,11 @@ ROTATE_BYTES = 1 << 30
 WARM_REPLAYS = 10              # untimed graph replays, back to back, before each timed replay
 
 
+def log(msg: str) -> None:
+    """Progress line on stderr (the JSON result is the only stdout line)."""
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -275,6 +280,7 @@ def stack_sweep(hinm, torch, synth, dev, with_dense):
             for pk in packs:
                 hinm.spmm(pk, xs[pk.plan.cin], out=ys[pk.plan.cout], workspace=ws)
         ms = run_graph(fwd)
+        log(f"stack batch {B}: {ms:.3f} ms per forward")
         row = {"batch": B, "ms_per_forward": round(ms, 4), "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2)}
         if with_dense:
             def fwd_dense():
@@ -400,6 +406,7 @@ def main():
         torch.cuda.synchronize()
         return
 
+    log(f"packed: {[round(v, 2) for v in pack_ms]} ms; timing batch {B}")
     rot = Rotation(hinm, torch, pk, x, B)
     r_eager = time_spmm(hinm, torch, rot, args.steps, args.warmup)
     r = time_spmm_graph(hinm, torch, rot, args.steps)
@@ -407,6 +414,7 @@ def main():
     ms = r["ms_mean"]
     value = alg["useful_flops"] / (ms * 1e-3) / 1e12
 
+    log(f"batch {B}: {ms * 1e3:.2f} us per product; timing batch {Bd}")
     rotd = Rotation(hinm, torch, pk, xd, Bd)
     rd_eager = time_spmm(hinm, torch, rotd, max(args.steps, 200), args.warmup)
     steps_d = max(args.steps, 200)
@@ -414,6 +422,7 @@ def main():
     algd = algorithmic(p, Bd)
     gbs_d = algd["bytes"] / (rd["ms_mean"] * 1e-3) / 1e9
 
+    log(f"batch {Bd}: {rd['ms_mean'] * 1e3:.2f} us per product; side rows")
     # NEXT row: output-channel permutation fused into the write-out, and the
     # one-time cross-layer index translation
     out_rows = torch.from_numpy(__import__("numpy").random.default_rng(0).permutation(p.cout).astype("int32")).to(dev)
@@ -539,7 +548,9 @@ def main():
                  "batch_2048_ms": round(dense_ms, 4), "batch_16_ms": round(dense_ms_d, 4),
                  "speedup_batch_2048": round(dense_ms / ms, 3), "speedup_batch_16": round(dense_ms_d / rd["ms_mean"], 3)}
 
+    log("stack sweep")
     stack = None if args.no_stack else stack_sweep(hinm, torch, synth, dev, not args.no_dense)
+    log("CPU oracle baseline")
 
     cpu = None if args.no_cpu else cpu_baseline(w, B)
 

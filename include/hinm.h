@@ -40,6 +40,11 @@ extern "C" {
 
 #define HINM_ABI_VERSION 1
 
+/* Version of the packed-buffer layout described at hinm_packed_t and
+ * hinm_tpacked_t.  A stored packed weight carries it; a different value
+ * means the bytes must be packed again from the weight. */
+#define HINM_FORMAT_VERSION 1
+
 /* K-block sizes of the packed layout: 32 dense columns; 64 positions
  * (16 groups of 4) of the 2:4 region. */
 #define HINM_KB_DENSE 32
@@ -150,6 +155,51 @@ typedef struct {
 /* Library ABI version (HINM_ABI_VERSION of the build). */
 int hinm_abi_version(void);
 
+/* Launch-shape options of the product (for tuning and for tests that run
+ * every kernel variant; the defaults are the measured best).  They are
+ * process-wide.  Each starts from its environment variable, read once, at
+ * the first call that uses any option; afterwards only hinm_set_option
+ * changes them.  An unset or invalid variable gives the default.
+ *   HINM_OPT_DECODE_PATH      env HINM_DECODE_PATH=rows16 -> 1: batch <= 64
+ *                             runs the 16-row kernel without a K split
+ *                             (default 0: the split kernel when tile_rows %
+ *                             64 == 0)
+ *   HINM_OPT_DECODE_WGS       env HINM_DECODE_WGS: about how many
+ *                             workgroups the batch <= 64 kernel splits K over
+ *                             (default 256; 1 .. 2^20).  A different split
+ *                             count may change the last bits of Y.
+ *   HINM_OPT_PREFILL_NT       env HINM_PREFILL_NT: token block of the
+ *                             batch > 64 kernel, 128 or 256 (default 0:
+ *                             256 from batch 1024, else 128)
+ *   HINM_OPT_PREFILL_SPLITS   env HINM_PREFILL_SPLITS: K split of each
+ *                             batch > 64 work item, 1, 2 or 4 (default 0: 2
+ *                             or 4 below 256 items, else 1; a different split
+ *                             may change the last bits of Y)
+ *   HINM_OPT_PREFILL_PATH     env HINM_PREFILL_PATH=staged -> 1: the
+ *                             batch > 64 kernel gathers X through registers
+ *                             instead of straight into LDS (same bits of Y)
+ *   HINM_OPT_PREFILL_PER_XCD  env HINM_PREFILL_PER_XCD: persistent
+ *                             workgroups per XCD of the batch > 64 kernel
+ *                             (default 0: 64; 1 .. 1024)
+ * A change applies to products launched afterwards; a workspace sized under
+ * other settings may then be too small (HINM_EWORKSPACE). */
+typedef enum {
+  HINM_OPT_DECODE_PATH = 1,
+  HINM_OPT_DECODE_WGS = 2,
+  HINM_OPT_PREFILL_NT = 3,
+  HINM_OPT_PREFILL_SPLITS = 4,
+  HINM_OPT_PREFILL_PATH = 5,
+  HINM_OPT_PREFILL_PER_XCD = 6,
+  HINM_OPT_COUNT = 7
+} hinm_option;
+
+/* Sets an option (host only).  Errors: HINM_EINVAL (unknown option or value
+ * out of its range; the option is then unchanged). */
+int hinm_set_option(int option, int64_t value);
+
+/* Current value of an option into *value (host).  Errors: HINM_EINVAL. */
+int hinm_get_option(int option, int64_t* value);
+
 /* Region counts for a cout x cin weight (FlexHiNM-GP notes, key design 1).
  * Host only, touches no device.  Requires cout, cin > 0, tile_rows % 16 == 0,
  * cout % tile_rows == 0, cin % 4 == 0 (pad the input dimension as the N:M
@@ -210,19 +260,8 @@ int hinm_spmm_workspace_bytes(const hinm_plan_t* plan, int64_t batch, size_t* by
  * batch == 0 is a no-op.  Asynchronous on `stream`; no host synchronisation.
  * Partial sums of a split reduction dimension are added in split order, so
  * the same inputs give bitwise-identical Y on every call.
- * Launch-shape overrides, read from the environment at each call (for
- * tuning; unset gives the defaults): HINM_PREFILL_NT = 128 | 256 (token
- * block of the batch > 64 kernel), HINM_PREFILL_PER_XCD = n > 0 (its
- * persistent workgroups per XCD, default 64), HINM_DECODE_WGS = n > 0
- * (about how many workgroups the batch <= 64 kernel splits K over, default
- * 256; this changes the split count and so may change the last bits of Y),
- * HINM_DECODE_PATH = rows16 (the 16-row batch <= 64 kernel without a K
- * split), HINM_PREFILL_PATH = staged (the batch > 64 kernel gathers X
- * through registers instead of loading it straight into LDS; same result
- * bits), HINM_PREFILL_SPLITS = 1 | 2 | 4 (K split of each batch > 64 work
- * item; by default 2 or 4 when there are fewer than 256 items, which
- * changes the last bits of Y).  The workspace size asked for must come from
- * the same settings.
+ * The launch shape follows the process-wide options of hinm_set_option;
+ * the workspace size asked for must come from the same settings.
  * Errors (host-side checks only): HINM_EINVAL, HINM_ESHAPE, HINM_EALIGN,
  * HINM_EWORKSPACE, HINM_EHIP (launch failure). */
 int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_t batch, int64_t ldx,

@@ -22,6 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhinm.so")
 
 HINM_ABI_VERSION = 1
+HINM_FORMAT_VERSION = 1       # packed-buffer layout version (include/hinm.h)
 STATUS = {0: "HINM_OK", 1: "HINM_EINVAL", 2: "HINM_ESHAPE", 3: "HINM_EPERM", 4: "HINM_EIMPORTANCE",
           5: "HINM_EALIGN", 6: "HINM_EWORKSPACE", 7: "HINM_EHIP", 8: "HINM_EDEVICE"}
 
@@ -31,7 +32,11 @@ EXPORTS = ("hinm_abi_version", "hinm_plan", "hinm_pack_workspace_bytes", "hinm_p
            "hinm_boundary_workspace_bytes", "hinm_boundary_search", "hinm_plan_tiles",
            "hinm_pack_tiles_workspace_bytes", "hinm_pack_tiles", "hinm_spmm_tiles_workspace_bytes",
            "hinm_spmm_tiles", "hinm_boundary_search_tiles", "hinm_gyro_workspace_bytes", "hinm_gyro_permute",
-           "hinm_status_str", "hinm_last_error")
+           "hinm_set_option", "hinm_get_option", "hinm_status_str", "hinm_last_error")
+
+# Launch-shape options (hinm_set_option): name -> HINM_OPT_* key.
+OPTIONS = {"decode_path": 1, "decode_wgs": 2, "prefill_nt": 3, "prefill_splits": 4, "prefill_path": 5,
+           "prefill_per_xcd": 6}
 
 
 class HinmError(RuntimeError):
@@ -112,6 +117,8 @@ def library() -> ctypes.CDLL:
             "hinm_gyro_workspace_bytes": ([P, I32, ctypes.POINTER(S)], ctypes.c_int),
             "hinm_gyro_permute": ([P, VP, I64, VP, I32, I32, I32, VP, VP, ctypes.POINTER(D), VP, S, VP],
                                   ctypes.c_int),
+            "hinm_set_option": ([ctypes.c_int, I64], ctypes.c_int),
+            "hinm_get_option": ([ctypes.c_int, ctypes.POINTER(I64)], ctypes.c_int),
             "hinm_status_str": ([ctypes.c_int], ctypes.c_char_p),
             "hinm_last_error": ([], ctypes.c_char_p),
         }
@@ -195,6 +202,51 @@ class HinmPacked:
 
     def nbytes(self) -> int:
         return self.plan.packed_bytes
+
+    def state_dict(self) -> dict:
+        """Plain tensors and numbers (torch.save / torch.load(weights_only=True) round-trip them): the
+        layout version, the plan's arguments and the five buffers."""
+        p = self.plan
+        return {"format": "hinm-packed", "format_version": HINM_FORMAT_VERSION, "cout": p.cout, "cin": p.cin,
+                "tile_rows": p.tile_rows, "t_s": p.t_s, "v_s": p.v_s,
+                **{k: getattr(self, k) for k in _BUFFERS}}
+
+    @classmethod
+    def from_state_dict(cls, sd: dict, device=None) -> "HinmPacked":
+        """Rebuilds a packed weight from state_dict() output: checks the layout version, recomputes the
+        plan from its arguments and checks every buffer's dtype and shape against it."""
+        _check_format(sd, "hinm-packed")
+        p = plan(int(sd["cout"]), int(sd["cin"]), int(sd["tile_rows"]), float(sd["t_s"]), float(sd["v_s"]))
+        T, R = p.n_tiles, p.tile_rows
+        want = {"val_dense": ((T, p.n_dense_pad // 32, R, 32), torch.int16),
+                "idx_dense": ((T, p.n_dense_pad), torch.int32),
+                "val_24": ((T, p.n_24_pad // 64, R, 32), torch.int16),
+                "meta_24": ((T, p.n_24_pad // 64, R), torch.int64),
+                "idx_24": ((T, p.n_24_pad), torch.int32)}
+        return cls(p, **_checked_buffers(sd, want, device))
+
+
+_BUFFERS = ("val_dense", "idx_dense", "val_24", "meta_24", "idx_24")
+
+
+def _check_format(sd: dict, kind: str) -> None:
+    if not isinstance(sd, dict) or sd.get("format") != kind:
+        raise ValueError(f"not a stored {kind} weight")
+    if sd.get("format_version") != HINM_FORMAT_VERSION:
+        raise ValueError(f"stored layout version {sd.get('format_version')!r}, this library reads "
+                         f"{HINM_FORMAT_VERSION}: pack the weight again")
+
+
+def _checked_buffers(sd: dict, want: dict, device) -> dict:
+    out = {}
+    for k, (shape, dtype) in want.items():
+        t = sd.get(k)
+        if not isinstance(t, torch.Tensor) or t.dtype != dtype or tuple(t.shape) != tuple(shape):
+            got = (None if not isinstance(t, torch.Tensor) else (t.dtype, tuple(t.shape)))
+            raise ValueError(f"stored buffer {k}: expected {dtype} {tuple(shape)}, found {got}")
+        t = t.contiguous()
+        out[k] = t.to(device) if device is not None else t
+    return out
 
 
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
@@ -322,6 +374,33 @@ class HinmTPacked:
     def nbytes(self) -> int:
         return self.plan.packed_bytes
 
+    def state_dict(self) -> dict:
+        """As HinmPacked.state_dict, with the per-tile v_s and the tile table."""
+        p = self.plan
+        return {"format": "hinm-packed-tiles", "format_version": HINM_FORMAT_VERSION, "cout": p.cout,
+                "cin": p.cin, "tile_rows": p.tile_rows, "t_s": p.t_s,
+                "v_s": torch.tensor(p.v_s, dtype=torch.float64), "tiles": self.tiles,
+                **{k: getattr(self, k) for k in _BUFFERS}}
+
+    @classmethod
+    def from_state_dict(cls, sd: dict, device=None) -> "HinmTPacked":
+        _check_format(sd, "hinm-packed-tiles")
+        v = sd.get("v_s")
+        if not isinstance(v, torch.Tensor):
+            raise ValueError("stored per-tile v_s missing")
+        p = plan_tiles(int(sd["cout"]), int(sd["cin"]), int(sd["tile_rows"]), float(sd["t_s"]), v.tolist())
+        R = p.tile_rows
+        want = {"tiles": ((p.n_tiles, 4), torch.int32),
+                "val_dense": ((p.dense_blocks, R, 32), torch.int16),
+                "idx_dense": ((p.dense_blocks * 32,), torch.int32),
+                "val_24": ((p.blocks_24, R, 32), torch.int16),
+                "meta_24": ((p.blocks_24, R), torch.int64),
+                "idx_24": ((p.blocks_24 * 64,), torch.int32)}
+        bufs = _checked_buffers(sd, want, device)
+        if not np.array_equal(bufs["tiles"].cpu().numpy(), p.tiles):
+            raise ValueError("stored tile table does not match the per-tile plan")
+        return cls(p, **bufs)
+
 
 def pack_tiles(w: torch.Tensor, importance: torch.Tensor, tile_rows: int, t_s: float, v_s,
                perm: Optional[torch.Tensor] = None) -> HinmTPacked:
@@ -367,15 +446,61 @@ def spmm_workspace_bytes(p: Plan, batch: int) -> int:
 
 
 _ws_cache = {}
+_ws_retired = []
+_opt_gen = 0
 
 
-def _workspace(device: torch.device, nbytes: int) -> Optional[torch.Tensor]:
+def get_option(name: str) -> int:
+    """Current value of a launch-shape option (see OPTIONS and hinm_set_option)."""
+    v = ctypes.c_int64()
+    _check(library().hinm_get_option(OPTIONS[name], ctypes.byref(v)))
+    return v.value
+
+
+def set_option(name: str, value: int) -> None:
+    """Sets a process-wide launch-shape option (hinm_set_option)."""
+    global _opt_gen
+    _check(library().hinm_set_option(OPTIONS[name], int(value)))
+    _opt_gen += 1          # workspace sizes remembered per weight depend on the options
+
+
+class options:
+    """Context manager: ``with options(prefill_splits=2): ...`` sets options and restores them on exit."""
+
+    def __init__(self, **kw):
+        for k in kw:
+            if k not in OPTIONS:
+                raise KeyError(f"unknown option {k!r}; known: {sorted(OPTIONS)}")
+        self.kw = kw
+        self.saved = {}
+
+    def __enter__(self):
+        for k, v in self.kw.items():
+            self.saved[k] = get_option(k)
+            set_option(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k, v in self.saved.items():
+            set_option(k, v)
+        return False
+
+
+def _workspace(device: torch.device, stream: int, nbytes: int) -> Optional[torch.Tensor]:
+    """The default workspace of (device, stream): zero-filled when made, at least nbytes.
+
+    One per stream, because a workspace holds the split reduction's arrival
+    counters and partial sums, so products that may overlap (different
+    streams) must not share one.  A buffer that is outgrown is kept alive, not
+    freed: HIP graphs captured earlier, or work still queued, may name it.
+    """
     if nbytes == 0:
         return None
-    key = (device.type, device.index)
+    key = (device.index, stream)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        # zero-filled: the product keeps its arrival counters here
+        if buf is not None:
+            _ws_retired.append(buf)
         buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf
@@ -387,11 +512,10 @@ def spmm(packed: HinmPacked, x: torch.Tensor, out: Optional[torch.Tensor] = None
 
     With ``out_rows`` (int32 [cout] on the device, a permutation), row r of the
     product is written to row out_rows[r] of Y (hinm_spmm_rows).
-    Asynchronous on the current stream.  ``workspace`` (uint8, device) may be
-    given; otherwise a per-device buffer is reused (calls on one device that
-    use it must not overlap on different streams).  The per-call host work is
-    kept to argument checks and one C call, so that small products are not
-    bound by Python.
+    Asynchronous on the current stream.  ``workspace`` (uint8, device, zero-filled before its first use) may
+    be given; otherwise each stream has its own default workspace, so products on different streams may
+    overlap.  The per-call host work is kept to argument checks and one C call, so that small products are
+    not bound by Python.
     """
     p = packed.plan
     dev = x.device
@@ -412,12 +536,13 @@ def spmm(packed: HinmPacked, x: torch.Tensor, out: Optional[torch.Tensor] = None
         raise ValueError(f"out_rows must be a contiguous int32 [{p.cout}] tensor on {dev}")
     st = packed.struct()
     need_cache = packed.__dict__["_ws_need"]
-    need = need_cache.get(batch)
+    need = need_cache.get((batch, _opt_gen))
     if need is None:
-        need = need_cache[batch] = (spmm_tiles_workspace_bytes(p, batch) if tiled else
-                                    spmm_workspace_bytes(p, batch))
+        need = need_cache[(batch, _opt_gen)] = (spmm_tiles_workspace_bytes(p, batch) if tiled else
+                                                spmm_workspace_bytes(p, batch))
+    stream = _stream_ptr(dev)
     if workspace is None:
-        workspace = _workspace(dev, need)
+        workspace = _workspace(dev, stream, need)
     lib = library()
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_n = workspace.numel() if workspace is not None else 0
@@ -425,13 +550,13 @@ def spmm(packed: HinmPacked, x: torch.Tensor, out: Optional[torch.Tensor] = None
     ldy = max(out.stride(0), batch) if batch else 0
     if tiled:
         call, args = lib.hinm_spmm_tiles, (ctypes.byref(st), x.data_ptr(), batch, ldx, out.data_ptr(), ldy, ws_ptr,
-                                           ws_n, _stream_ptr(dev))
+                                           ws_n, stream)
     elif out_rows is None:
         call, args = lib.hinm_spmm, (ctypes.byref(st), x.data_ptr(), batch, ldx, out.data_ptr(), ldy, ws_ptr, ws_n,
-                                     _stream_ptr(dev))
+                                     stream)
     else:
         call, args = lib.hinm_spmm_rows, (ctypes.byref(st), x.data_ptr(), batch, ldx, out.data_ptr(), ldy,
-                                          out_rows.data_ptr(), ws_ptr, ws_n, _stream_ptr(dev))
+                                          out_rows.data_ptr(), ws_ptr, ws_n, stream)
     if dev.index is None or dev.index == torch.cuda.current_device():
         _check(call(*args))
     else:
@@ -537,7 +662,8 @@ def boundary_search_tiles(importance: torch.Tensor, perm: Optional[torch.Tensor]
     return [v[i] for i in range(T)], [pts[i] for i in range(T)]
 
 
-__all__ = ["HinmError", "HinmPacked", "Plan", "plan", "pack", "spmm", "translate_indices", "boundary_search", "plan_tiles", "pack_tiles", "boundary_search_tiles",
+__all__ = ["HinmError", "HinmPacked", "Plan", "plan", "pack", "spmm", "set_option", "get_option", "options",
+           "OPTIONS", "translate_indices", "boundary_search", "plan_tiles", "pack_tiles", "boundary_search_tiles",
            "HinmTPacked", "TilePlan", "spmm_tiles_workspace_bytes", "alloc_packed",
            "pack_workspace_bytes",
            "spmm_workspace_bytes", "library", "LIB_PATH", "EXPORTS"]

@@ -47,6 +47,9 @@ struct SpmmShape {
 };
 SpmmShape spmm_shape(const hinm_plan_t* p, int64_t batch);
 
+// Current value of a launch-shape option (HINM_OPT_*).
+int64_t option(int key);
+
 // Current device is a gfx950 part (checked once per device); HINM_OK or
 // HINM_EDEVICE / HINM_EHIP with the message recorded.
 int ensure_device();

@@ -5,6 +5,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "hinm_internal.h"
 
 static_assert(sizeof(hinm_plan_t) == 120, "hinm_plan_t must have no padding");
@@ -76,11 +78,89 @@ hinm_plan_t shape_plan(const hinm_tplan_t& p) {
   return q;
 }
 
+// Launch-shape options: process-wide, each read from its environment variable
+// once (at the first use of any option), then changed only through
+// hinm_set_option.  Atomic, so a setting made in one thread is seen whole by
+// a product launched from another.
+namespace {
+struct OptionDef {
+  const char* env;
+  int64_t def;
+};
+constexpr OptionDef kOptionDefs[HINM_OPT_COUNT] = {
+    {nullptr, 0},                      // 0: unused
+    {"HINM_DECODE_PATH", 0},           // HINM_OPT_DECODE_PATH
+    {"HINM_DECODE_WGS", 256},          // HINM_OPT_DECODE_WGS
+    {"HINM_PREFILL_NT", 0},            // HINM_OPT_PREFILL_NT
+    {"HINM_PREFILL_SPLITS", 0},        // HINM_OPT_PREFILL_SPLITS
+    {"HINM_PREFILL_PATH", 0},          // HINM_OPT_PREFILL_PATH
+    {"HINM_PREFILL_PER_XCD", 0},       // HINM_OPT_PREFILL_PER_XCD
+};
+
+bool option_valid(int key, int64_t v) {
+  switch (key) {
+    case HINM_OPT_DECODE_PATH: return v == 0 || v == 1;
+    case HINM_OPT_DECODE_WGS: return v >= 1 && v <= (1 << 20);
+    case HINM_OPT_PREFILL_NT: return v == 0 || v == 128 || v == 256;
+    case HINM_OPT_PREFILL_SPLITS: return v == 0 || v == 1 || v == 2 || v == 4;
+    case HINM_OPT_PREFILL_PATH: return v == 0 || v == 1;
+    case HINM_OPT_PREFILL_PER_XCD: return v >= 0 && v <= 1024;
+    default: return false;
+  }
+}
+
+// Environment value of an option: the names HINM_DECODE_PATH=rows16 and
+// HINM_PREFILL_PATH=staged select 1, other variables hold a number.  An
+// unset, unparsable or out-of-range value leaves the default.
+int64_t option_from_env(int key) {
+  const OptionDef& d = kOptionDefs[key];
+  const char* e = getenv(d.env);
+  if (!e || !*e) return d.def;
+  if (key == HINM_OPT_DECODE_PATH) return strcmp(e, "rows16") == 0 ? 1 : 0;
+  if (key == HINM_OPT_PREFILL_PATH) return strcmp(e, "staged") == 0 ? 1 : 0;
+  char* end = nullptr;
+  const long long v = strtoll(e, &end, 10);
+  if (end == e || *end != '\0' || !option_valid(key, v)) return d.def;
+  return v;
+}
+
+struct Options {
+  std::atomic<int64_t> v[HINM_OPT_COUNT];
+  Options() {
+    for (int k = 0; k < HINM_OPT_COUNT; ++k) v[k].store(k == 0 ? 0 : option_from_env(k), std::memory_order_relaxed);
+  }
+};
+
+Options& options() {
+  static Options o;   // initialised once, thread-safe
+  return o;
+}
+}  // namespace
+
+int64_t option(int key) { return options().v[key].load(std::memory_order_relaxed); }
+
 }  // namespace hinm
 
 using hinm::fail;
 
 extern "C" int hinm_abi_version(void) { return HINM_ABI_VERSION; }
+
+extern "C" int hinm_set_option(int option, int64_t value) {
+  hinm::clear_error();
+  if (option <= 0 || option >= HINM_OPT_COUNT) return fail(HINM_EINVAL, "unknown option %d", option);
+  if (!hinm::option_valid(option, value))
+    return fail(HINM_EINVAL, "value %lld is out of range for option %d", (long long)value, option);
+  hinm::options().v[option].store(value, std::memory_order_relaxed);
+  return HINM_OK;
+}
+
+extern "C" int hinm_get_option(int option, int64_t* value) {
+  hinm::clear_error();
+  if (option <= 0 || option >= HINM_OPT_COUNT) return fail(HINM_EINVAL, "unknown option %d", option);
+  if (!value) return fail(HINM_EINVAL, "value is NULL");
+  *value = hinm::option(option);
+  return HINM_OK;
+}
 
 // FlexHiNM-GP notes, key design 1: t_s = v_s + (1 - v_s) p_s / 2.  The counts
 // are rounded half-up so that every row keeps exactly cin - z entries:
@@ -177,16 +257,13 @@ SpmmShape spmm_shape(const hinm_plan_t* p, int64_t batch) {
   if (batch <= 64) {
     s.nt = batch <= 16 ? 16 : (batch <= 32 ? 32 : 64);
     s.n_tblocks = (int)((batch + s.nt - 1) / s.nt);
-    const char* dp = getenv("HINM_DECODE_PATH");
-    if (p->tile_rows % 64 == 0 && !(dp && strcmp(dp, "rows16") == 0)) {
+    if (p->tile_rows % 64 == 0 && option(HINM_OPT_DECODE_PATH) == 0) {
       // 64-row workgroups, K split over a power-of-two number of workgroups
       // so that about `target` workgroups run, each with >= 4 K-blocks.
       s.path = kPathDecodeSplit;
       const int64_t base = (int64_t)p->n_tiles * (p->tile_rows / 64) * s.n_tblocks;
       const int nblk = p->n_dense_pad / HINM_KB_DENSE + p->n_24_pad / HINM_KB_24;
-      int64_t target = 256;
-      const char* env = getenv("HINM_DECODE_WGS");
-      if (env && atoi(env) > 0) target = atoi(env);
+      const int64_t target = option(HINM_OPT_DECODE_WGS);
       int splits = 1;
       if (base <= kWsCounters)
         while (splits < 64 && base * splits * 2 <= target && nblk / (splits * 2) >= 4) splits *= 2;
@@ -203,8 +280,7 @@ SpmmShape spmm_shape(const hinm_plan_t* p, int64_t batch) {
   if (p->tile_rows % 64 == 0) {
     s.path = kPathPrefill;
     s.nt = batch >= 1024 ? 256 : 128;
-    const char* env = getenv("HINM_PREFILL_NT");
-    if (env && (atoi(env) == 128 || atoi(env) == 256)) s.nt = atoi(env);
+    if (option(HINM_OPT_PREFILL_NT) != 0) s.nt = (int)option(HINM_OPT_PREFILL_NT);
     s.n_tblocks = (int)((batch + s.nt - 1) / s.nt);
     // Fewer work items than compute units: split each item's K range over 2
     // or 4 workgroups (at most 512 in all, two per compute unit; each keeps
@@ -214,9 +290,8 @@ SpmmShape spmm_shape(const hinm_plan_t* p, int64_t batch) {
     const int64_t items = (int64_t)p->n_tiles * (p->tile_rows / 64) * s.n_tblocks;
     const int nblk = p->n_dense_pad / HINM_KB_DENSE + p->n_24_pad / HINM_KB_24;
     int splits = 1;
-    const char* es = getenv("HINM_PREFILL_SPLITS");
-    if (es && atoi(es) >= 1) {
-      splits = atoi(es) >= 4 ? 4 : (atoi(es) >= 2 ? 2 : 1);
+    if (option(HINM_OPT_PREFILL_SPLITS) != 0) {
+      splits = (int)option(HINM_OPT_PREFILL_SPLITS);
     } else if (items < 256) {
       while (splits < 4 && items * splits * 2 <= 512 && nblk / (splits * 2) >= 8) splits *= 2;
     }

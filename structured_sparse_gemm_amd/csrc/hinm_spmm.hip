@@ -85,6 +85,26 @@ __device__ inline uint16_t bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Split-K hand-over: one workgroup of `splits` counts itself in on an
+// agent-scope counter; true for the last to arrive.  The increment wraps (the
+// hardware's atomic inc: old >= splits - 1 stores 0), so the counter is back
+// at 0 after the last arrival without a separate store.
+//
+// Why the partial sums are visible to the last arriver without a cache
+// writeback (gfx950 follows the gfx942 memory model of the LLVM AMDGPU
+// back end): the partials are written and read only with agent-scope atomic
+// stores and loads, which are issued with the sc1 bit and so are coherent
+// across the XCDs' L2 caches (a store writes through to the device-coherent
+// level, a load reads from it).  Each workgroup waits for its partial stores
+// to be acknowledged (s_waitcnt vmcnt(0)) before its increment, and the last
+// arriver issues its partial loads only after its increment has returned.
+// A release / acquire pair would add an L2 writeback and invalidate, which
+// are needed only for data written with ordinary stores; none is read here.
+__device__ inline bool arrive(unsigned* ctr, int splits) {
+  return __builtin_amdgcn_atomic_inc32(ctr, (unsigned)(splits - 1), __ATOMIC_RELAXED, "agent") ==
+         (unsigned)(splits - 1);
+}
+
 // Copies the X rows of one K-block into LDS as xt[n][k] (k fastest): row
 // idx[k] of X, tokens n0 .. n0+NT-1; -1 indices and tokens past the batch
 // read as zero.
@@ -659,8 +679,7 @@ __global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(SpmmArgs a, int 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   unsigned* ctr = counters + (int64_t)trb * n_tb + tb;
-  if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(splits - 1);
+  if (threadIdx.x == 0) s_last = arrive(ctr, splits);
   __syncthreads();
   if (!s_last || threadIdx.x >= 256) return;
   const int64_t plane = (int64_t)n_tb * a.cout * NTOK;
@@ -685,7 +704,6 @@ __global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(SpmmArgs a, int 
     const int n = o % NTOK;
     if (n0 + n < a.batch && yrow[k] >= 0) a.y[yrow[k] * a.ldy + n0 + n] = bf16_rne(sum[k]);
   }
-  if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next call
 }
 
 // ---------------------------------------------------------------------------
@@ -1343,8 +1361,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
                                  __HIP_MEMORY_SCOPE_AGENT);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (threadIdx.x == 0)
-          s_last = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(splits - 1);
+        if (threadIdx.x == 0) s_last = arrive(ctr, splits);
         __syncthreads();
         if (!s_last) continue;
         for (int r = 0; r < 2; ++r)
@@ -1363,7 +1380,6 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
               for (int e = 0; e < 16; ++e) acc[r][j][e] += v[e];
             }
         }
-        if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // next call
       }
 
       // epilogue: acc[r][j][e] is row 32r + 8(e/4) + 4(lane/32) + e%4, token tok_w + 32j + lane%32.
@@ -1485,14 +1501,10 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
   a.splits = sh.splits;
   a.n_kunits = sh.n_kunits;
   a.x_vec = hinm::aligned(x_bf16, 16) && (ldx % 8 == 0);
-  {
-    // At 256-token blocks X rows go straight into LDS, whatever their
-    // alignment (the register-staged gather stays selectable for
-    // comparison); at 128-token blocks the register-staged gather measured
-    // faster.
-    const char* pp = getenv("HINM_PREFILL_PATH");
-    a.x_lds = !(pp && strcmp(pp, "staged") == 0);
-  }
+  // At 256-token blocks X rows go straight into LDS, whatever their
+  // alignment (the register-staged gather stays selectable for comparison);
+  // at 128-token blocks the register-staged gather measured faster.
+  a.x_lds = hinm::option(HINM_OPT_PREFILL_PATH) == 0;
   a.y_vec = hinm::aligned(y_bf16, 16) && (ldy % 8 == 0);
   a.n_tiles = p.n_tiles;
   a.out_rows = out_rows;
@@ -1558,9 +1570,7 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
   } else if (sh.path == hinm::kPathPrefill) {
     // persistent grid: 8 XCDs x (32 CUs x 2 workgroups), never more than the work items.
     const int items = p.n_tiles * (p.tile_rows / 64) * sh.n_tblocks * sh.splits;
-    int per_xcd = 64;
-    const char* pe = getenv("HINM_PREFILL_PER_XCD");
-    if (pe && atoi(pe) > 0) per_xcd = atoi(pe);
+    const int per_xcd = hinm::option(HINM_OPT_PREFILL_PER_XCD) > 0 ? (int)hinm::option(HINM_OPT_PREFILL_PER_XCD) : 64;
     const int nwg = 8 * std::min(per_xcd, (items + 7) / 8);
     // the K-split epilogue is a separate instantiation, so the unsplit
     // kernel keeps its registers

@@ -191,8 +191,7 @@ def test_pack_host_errors(lib):
     assert call(out=hinm.PackedT(p.raw, None, None, None, None, None)) == 1
 
 
-def test_workspace_sizes(lib, monkeypatch):
-    monkeypatch.delenv("HINM_PREFILL_SPLITS", raising=False)
+def test_workspace_sizes(lib):
     counters = 16384 * 4
     p = hinm.plan(11008, 4096, 64, 0.75, 0.55)
     for b in (0, 2048, 4096):                  # 1376 and 2752 work items: no K split
@@ -204,8 +203,9 @@ def test_workspace_sizes(lib, monkeypatch):
     q = hinm.plan(4096, 4096, 64, 0.5, 0.25)   # 64 items at batch 128: split 4 ways
     assert hinm.spmm_workspace_bytes(q, 128) == counters + 4 * 64 * 256 * 128
     assert hinm.spmm_workspace_bytes(q, 512) == 0     # 256 items: no split
-    monkeypatch.setenv("HINM_PREFILL_SPLITS", "1")
-    assert hinm.spmm_workspace_bytes(q, 128) == 0
+    with hinm.options(prefill_splits=1):
+        assert hinm.spmm_workspace_bytes(q, 128) == 0
+    assert hinm.spmm_workspace_bytes(q, 128) == counters + 4 * 64 * 256 * 128
     p = hinm.plan(96, 4096, 48, 0.75, 0.55)
     assert hinm.spmm_workspace_bytes(p, 200) % 256 == 0
 
@@ -306,3 +306,28 @@ def test_gyro_host_errors(lib):
     assert call(ws=None) == 6
     assert call(wsb=n.value - 1) == 6
     assert call(ws=(1 << 22) + 16) == 5
+
+
+def test_options_set_get_and_reject(lib):
+    """Launch options through the C ABI: read back what was set, refuse unknown keys and out-of-range
+    values (leaving the option unchanged), and the workspace size follows the setting."""
+    import ctypes
+    v = ctypes.c_int64()
+    for name, key in hinm.OPTIONS.items():
+        assert lib.hinm_get_option(key, ctypes.byref(v)) == 0
+        before = v.value
+        assert lib.hinm_set_option(key, -3) == 1
+        assert lib.hinm_get_option(key, ctypes.byref(v)) == 0 and v.value == before
+        assert hinm.get_option(name) == before
+    assert lib.hinm_set_option(0, 1) == 1 and lib.hinm_set_option(len(hinm.OPTIONS) + 1, 1) == 1
+    assert lib.hinm_get_option(2, None) == 1
+    q = hinm.plan(4096, 4096, 64, 0.5, 0.25)
+    base = hinm.spmm_workspace_bytes(q, 128)
+    with hinm.options(prefill_splits=2, prefill_nt=128):
+        assert hinm.get_option("prefill_splits") == 2
+        assert hinm.spmm_workspace_bytes(q, 128) == 16384 * 4 + 2 * 64 * 256 * 128
+    assert hinm.get_option("prefill_splits") == 0 and hinm.spmm_workspace_bytes(q, 128) == base
+    with pytest.raises(hinm.HinmError):
+        hinm.set_option("prefill_nt", 192)
+    with pytest.raises(KeyError):
+        hinm.options(no_such_option=1)

@@ -52,14 +52,13 @@ def test_spmm_rows_scatter(case):
     torch.cuda.synchronize()
     # same bf16 values, rows moved: ys[out_rows[r]] == y[r]
     assert torch.equal(as_bits(ys)[out_rows.to(DEV).long()], as_bits(y))
-    # and against the oracle: scatter of the float64 product
-    if w.cout * w.cin * batch <= 96 * 1024 * 2048:
-        p, _, inter = oracle_pack(w)
-        wh = oh.masked_weight(bits_of(w.w_bf16), inter["mask"])
-        xf = synth.as_f64(x)
-        ref = oh.scatter_rows(oh.spmm(wh, xf), out_rows.numpy())
-        scale = oh.scatter_rows(np.abs(wh) @ np.abs(xf), out_rows.numpy())
-        check_y(ys, ref, scale, f"spmm_rows {what}")
+    # and against the oracle at every size: scatter of the float64 product
+    p, _, inter = oracle_pack(w)
+    wh = oh.masked_weight(bits_of(w.w_bf16), inter["mask"])
+    xf = synth.as_f64(x)
+    ref = oh.scatter_rows(oh.spmm(wh, xf), out_rows.numpy())
+    scale = oh.scatter_rows(np.abs(wh) @ np.abs(xf), out_rows.numpy())
+    check_y(ys, ref, scale, f"spmm_rows {what}")
 
 
 def test_spmm_rows_into_strided_output():

@@ -21,12 +21,11 @@ hinm = pytest.importorskip("structured_sparse_gemm_amd")
 DEV = torch.device("cuda:0")
 
 
-def both_paths(monkeypatch, fn):
-    monkeypatch.delenv("HINM_PREFILL_PATH", raising=False)
-    a = fn()
-    monkeypatch.setenv("HINM_PREFILL_PATH", "staged")
-    b = fn()
-    monkeypatch.delenv("HINM_PREFILL_PATH")
+def both_paths(fn):
+    with hinm.options(prefill_path=0):
+        a = fn()
+    with hinm.options(prefill_path=1):
+        b = fn()
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "LDS-direct and register-staged X paths differ"
     return a
@@ -40,21 +39,21 @@ def both_paths(monkeypatch, fn):
     (128, 700, 64, 0.75, 0.75),     # no 2:4 region
 ])
 @pytest.mark.parametrize("batch", [65, 300, 1024, 1300])
-def test_prefill_paths_vs_oracle(monkeypatch, shape, batch):
+def test_prefill_paths_vs_oracle(shape, batch):
     cout, cin, R, t, v = shape
     w = synth.small(cout, cin, R, t, v, 1, seed=cout + cin + batch)
     print(f"[prefill] {cout}x{cin} R={R} t_s={t} v_s={v} batch={batch}", flush=True)
     pk = hinm.pack(w.w_bf16.to(DEV), w.importance.to(DEV), R, t, v, w.perm.to(DEV))
     x = torch.randn(cin, batch, generator=torch.Generator().manual_seed(batch)).to(torch.bfloat16)
     xd = x.to(DEV)
-    y = both_paths(monkeypatch, lambda: hinm.spmm(pk, xd))
+    y = both_paths(lambda: hinm.spmm(pk, xd))
     _, _, inter = oracle_pack(w)
     wh = oh.masked_weight(bits_of(w.w_bf16), inter["mask"])
     xf = synth.as_f64(x)
     check_y(y, oh.spmm(wh, xf), np.abs(wh) @ np.abs(xf), f"prefill {shape} batch {batch}")
 
 
-def test_prefill_paths_row_map_and_stride(monkeypatch):
+def test_prefill_paths_row_map_and_stride():
     w = synth.small(256, 1536, 64, 0.75, 0.55, 1, seed=41)
     pk = hinm.pack(w.w_bf16.to(DEV), w.importance.to(DEV), 64, 0.75, 0.55, w.perm.to(DEV))
     big = torch.randn(1536, 1400, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
@@ -62,7 +61,7 @@ def test_prefill_paths_row_map_and_stride(monkeypatch):
     xd = big.to(DEV)[:, :1288]
     rows = torch.from_numpy(np.random.default_rng(3).permutation(256).astype(np.int32)).to(DEV)
     print("[prefill] row map, ldx 1400, batch 1288", flush=True)
-    y = both_paths(monkeypatch, lambda: hinm.spmm(pk, xd, out_rows=rows))
+    y = both_paths(lambda: hinm.spmm(pk, xd, out_rows=rows))
     _, _, inter = oracle_pack(w)
     wh = oh.masked_weight(bits_of(w.w_bf16), inter["mask"])
     xf = synth.as_f64(x)
@@ -70,7 +69,7 @@ def test_prefill_paths_row_map_and_stride(monkeypatch):
     check_y(y, ref, oh.scatter_rows(np.abs(wh) @ np.abs(xf), rows.cpu().numpy()), "row map")
 
 
-def test_prefill_paths_per_tile(monkeypatch):
+def test_prefill_paths_per_tile():
     w = synth.small(640, 2048, 64, 0.75, 0.55, 1, seed=43)
     rng = np.random.default_rng(43)
     v = [float(u) for u in rng.uniform(0.5, 0.75, w.cout // 64)]
@@ -78,7 +77,7 @@ def test_prefill_paths_per_tile(monkeypatch):
     x = torch.randn(2048, 1100, generator=torch.Generator().manual_seed(43)).to(torch.bfloat16)
     xd = x.to(DEV)
     print("[prefill] per-tile layout, batch 1100", flush=True)
-    y = both_paths(monkeypatch, lambda: hinm.spmm(pk, xd))
+    y = both_paths(lambda: hinm.spmm(pk, xd))
     plans = oh.plan_tiles(w.cout, w.cin, 64, 0.75, v)
     _, inter = oh.pack_tiles(bits_of(w.w_bf16), w.importance.numpy(), w.perm.numpy(), plans, with_intermediates=True)
     wh = oh.masked_weight(bits_of(w.w_bf16), inter["mask"])
@@ -86,7 +85,7 @@ def test_prefill_paths_per_tile(monkeypatch):
     check_y(y, oh.spmm(wh, xf), np.abs(wh) @ np.abs(xf), "per-tile")
 
 
-def test_prefill_nonfinite_pruned_rows_do_not_reach_y(monkeypatch):
+def test_prefill_nonfinite_pruned_rows_do_not_reach_y():
     """X rows of columns pruned in every tile (their weights are zero) hold NaN and Inf; the product
     gathers only kept columns and reads pads as zeros, so Y stays finite and equal to the oracle's."""
     w = synth.small(128, 1024, 64, 0.75, 0.55, 1, seed=44)
@@ -100,7 +99,7 @@ def test_prefill_nonfinite_pruned_rows_do_not_reach_y(monkeypatch):
     x[torch.as_tensor(dead[1::2])] = float("inf")
     xd = x.to(DEV)
     print("[prefill] non-finite pruned rows", flush=True)
-    y = both_paths(monkeypatch, lambda: hinm.spmm(pk, xd))
+    y = both_paths(lambda: hinm.spmm(pk, xd))
     p = oh.plan(128, 1024, 64, 0.75, 0.55)
     _, inter = oh.pack(bits_of(wb), imp.numpy(), w.perm.numpy(), p, with_intermediates=True)
     assert not inter["mask"][:, dead].any(), "the zero columns must be pruned in every tile"
@@ -111,7 +110,7 @@ def test_prefill_nonfinite_pruned_rows_do_not_reach_y(monkeypatch):
 
 
 @pytest.mark.parametrize("layout", ["aligned", "contiguous", "offset"])
-def test_prefill_last_x_row_ragged_tails(monkeypatch, layout):
+def test_prefill_last_x_row_ragged_tails(layout):
     """The last input channel kept in every tile, at batches whose last token block ends inside a
     16-byte chunk (odd and even remainders), with X rows 16-byte aligned (row stride a multiple of 8
     tokens), contiguous (stride = batch) or starting 2 bytes past a 16-byte boundary.  The gathers of
@@ -137,13 +136,13 @@ def test_prefill_last_x_row_ragged_tails(monkeypatch, layout):
             buf[1:].copy_(x.reshape(-1).to(DEV))
             xd = buf[1:].view(264, b)
         print(f"[prefill] last row, batch={b} layout={layout}", flush=True)
-        y = both_paths(monkeypatch, lambda: hinm.spmm(pk, xd))
+        y = both_paths(lambda: hinm.spmm(pk, xd))
         xf = synth.as_f64(x)
         check_y(y, oh.spmm(wh, xf), np.abs(wh) @ np.abs(xf), f"last row batch {b} {layout}")
 
 
 @pytest.mark.parametrize("splits", [2, 4])
-def test_prefill_split_k(monkeypatch, splits):
+def test_prefill_split_k(splits):
     """Each work item's K range split over 2 or 4 workgroups (partial sums through the workspace, added
     in split order): within the bar of the oracle, identical on both X paths, bit-identical from one
     call to the next (the counters are back at zero), and ragged tails included."""
@@ -151,15 +150,15 @@ def test_prefill_split_k(monkeypatch, splits):
     pk = hinm.pack(w.w_bf16.to(DEV), w.importance.to(DEV), 64, 0.6, 0.35, w.perm.to(DEV))
     _, _, inter = oracle_pack(w)
     wh = oh.masked_weight(bits_of(w.w_bf16), inter["mask"])
-    monkeypatch.setenv("HINM_PREFILL_SPLITS", str(splits))
     for b in (65, 200, 1031, 1100):
         x = torch.randn(2048, b, generator=torch.Generator().manual_seed(b)).to(torch.bfloat16)
         xd = x.to(DEV)
-        ws = torch.zeros(hinm.spmm_workspace_bytes(pk.plan, b), dtype=torch.uint8, device=DEV)
-        assert ws.numel() > 0
-        print(f"[prefill] split K {splits} ways, batch={b}", flush=True)
-        y = both_paths(monkeypatch, lambda: hinm.spmm(pk, xd, workspace=ws))
-        y2 = hinm.spmm(pk, xd, workspace=ws)
+        with hinm.options(prefill_splits=splits):
+            ws = torch.zeros(hinm.spmm_workspace_bytes(pk.plan, b), dtype=torch.uint8, device=DEV)
+            assert ws.numel() > 0
+            print(f"[prefill] split K {splits} ways, batch={b}", flush=True)
+            y = both_paths(lambda: hinm.spmm(pk, xd, workspace=ws))
+            y2 = hinm.spmm(pk, xd, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
         assert not ws[:4 * 16384].any(), "arrival counters not back at zero"

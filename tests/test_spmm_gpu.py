@@ -1,9 +1,9 @@
 """hinm_spmm on the GPU against the float64 oracle product.
 
 Bar: |Y - Y_o| <= 1e-2 (|W_hat| |X|) elementwise and relative Frobenius error
-<= 5e-3, Y_o = (W (.) M) X in float64 from the oracle's own mask.  Full
-outputs where the oracle product takes seconds; a fixed sample of rows (all
-tokens) at the large batches.
+<= 5e-3, Y_o = (W (.) M) X in float64 from the oracle's own mask.  Every
+output element is compared, at every batch (the float64 product of the
+largest case takes about a second on the host).
 """
 import json
 import os
@@ -48,12 +48,6 @@ class Case:
         return check_y(got, ref, scale, f"{self.w.name} batch {batch}")
 
 
-def sample_rows(cout: int, n: int = 384, seed: int = 0) -> np.ndarray:
-    rng = np.random.default_rng(seed)
-    rows = np.unique(np.concatenate([np.arange(64), np.arange(cout - 64, cout), rng.choice(cout, n, replace=False)]))
-    return rows
-
-
 def test_spmm_tiny():
     w = synth.tiny()
     c = Case(w)
@@ -75,13 +69,13 @@ def test_spmm_q_proj_decode():
 
 def test_spmm_up_proj_prefill():
     w = synth.up_proj(batch=2048)
-    Case(w).check(2048, x=w.x_bf16, rows=sample_rows(w.cout))
+    Case(w).check(2048, x=w.x_bf16)
 
 
 @pytest.mark.parametrize("batch", [16, 2048])
 def test_spmm_down_proj(batch):
     w = synth.down_proj(batch=batch)
-    Case(w).check(batch, x=w.x_bf16, rows=None if batch <= 64 else sample_rows(w.cout))
+    Case(w).check(batch, x=w.x_bf16)
 
 
 @pytest.mark.parametrize("idx", [0, 1, 2])
@@ -89,14 +83,16 @@ def test_spmm_down_proj_sweep(idx):
     g = json.load(open(os.path.join(GOLDEN, "down_proj_boundary.json")))["results"][idx]
     c = Case(synth.down_proj_sweep(g["t_s"], batch=1), v_s=g["v_s"])
     for b in (1, 64, 512):
-        c.check(b, seed=b, rows=None if b <= 64 else sample_rows(c.w.cout))
+        c.check(b, seed=b)
 
 
 @pytest.mark.parametrize("layer,proj", [(0, 0), (13, 4), (31, 6)])
 def test_spmm_stack_layers(layer, proj):
+    """The 7B-shaped stack's shapes at every batch of its sweep that changes the launch shape, plus
+    3000 (a prefill batch past 2048 that is not a multiple of the 256-token block)."""
     c = Case(synth.stack_layer(layer, proj, batch=1))
-    for b in (1, 16, 256, 2048):
-        c.check(b, seed=b, rows=None if b <= 256 else sample_rows(c.w.cout))
+    for b in (1, 16, 64, 256, 1024, 2048, 3000, 4096):
+        c.check(b, seed=b)
 
 
 def test_spmm_ragged_batches():
