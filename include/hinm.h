@@ -267,6 +267,34 @@ int hinm_spmm_workspace_bytes(const hinm_plan_t* plan, int64_t batch, size_t* by
 int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_t batch, int64_t ldx,
               void* y_bf16, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Size of the device array that holds hinm_spmm_noalloc's scratch: 64 KiB
+ * of arrival counters and 32 MiB of partial sums, one copy on every device
+ * the library runs on, held until the process ends.  Every launch shape the
+ * default options choose fits: the split decode (batch <= 64) needs at most
+ * 4 MiB of partials, the K split of larger batches (at most 512 workgroups
+ * of 256 threads x up to 64 floats) and the generic kernel's split at most
+ * 32 MiB. */
+#define HINM_NOALLOC_SCRATCH_BYTES ((size_t)65536 + ((size_t)32 << 20))
+
+/* hinm_spmm without a workspace argument and without any device allocation,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, serving loops and harnesses that forbid hipMalloc.  The scratch
+ * of the split reduction lives in a static device array of
+ * HINM_NOALLOC_SCRATCH_BYTES that the library holds on each device; the
+ * first call on a device takes its address and clears its counters (a fill
+ * kernel on `stream`).  Every call on one device shares that array, so calls
+ * that overlap in time on one device (different streams, or work queued
+ * from another thread) race on it and give wrong results; calls on one
+ * stream are safe.  The array keeps the last call's partial sums; its
+ * counters are back at zero whenever no call is in flight.
+ * A product whose scratch need (hinm_spmm_workspace_bytes) exceeds
+ * HINM_NOALLOC_SCRATCH_BYTES - possible only under options that force more
+ * splits (hinm_set_option) - is refused with HINM_EWORKSPACE before
+ * anything is launched.  Arguments, result bits and other errors as
+ * hinm_spmm. */
+int hinm_spmm_noalloc(const hinm_packed_t* packed, const void* x_bf16, int64_t batch, int64_t ldx, void* y_bf16,
+                      int64_t ldy, void* stream);
+
 /* hinm_spmm with the output-channel permutation fused into the write-out
  * (FlexHiNM-GP notes, key design 2: the output channels of a tile are
  * permuted before pruning, and the permutation is undone where the data

@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libhinm.so")
 
 HINM_ABI_VERSION = 1
 HINM_FORMAT_VERSION = 1       # packed-buffer layout version (include/hinm.h)
+HINM_NOALLOC_SCRATCH_BYTES = 65536 + (32 << 20)   # hinm_spmm_noalloc's device array (include/hinm.h)
 STATUS = {0: "HINM_OK", 1: "HINM_EINVAL", 2: "HINM_ESHAPE", 3: "HINM_EPERM", 4: "HINM_EIMPORTANCE",
           5: "HINM_EALIGN", 6: "HINM_EWORKSPACE", 7: "HINM_EHIP", 8: "HINM_EDEVICE"}
 
@@ -32,7 +33,7 @@ EXPORTS = ("hinm_abi_version", "hinm_plan", "hinm_pack_workspace_bytes", "hinm_p
            "hinm_boundary_workspace_bytes", "hinm_boundary_search", "hinm_plan_tiles",
            "hinm_pack_tiles_workspace_bytes", "hinm_pack_tiles", "hinm_spmm_tiles_workspace_bytes",
            "hinm_spmm_tiles", "hinm_boundary_search_tiles", "hinm_gyro_workspace_bytes", "hinm_gyro_permute",
-           "hinm_set_option", "hinm_get_option", "hinm_status_str", "hinm_last_error")
+           "hinm_set_option", "hinm_get_option", "hinm_spmm_noalloc", "hinm_status_str", "hinm_last_error")
 
 # Launch-shape options (hinm_set_option): name -> HINM_OPT_* key.
 OPTIONS = {"decode_path": 1, "decode_wgs": 2, "prefill_nt": 3, "prefill_splits": 4, "prefill_path": 5,
@@ -118,6 +119,7 @@ def library() -> ctypes.CDLL:
             "hinm_gyro_permute": ([P, VP, I64, VP, I32, I32, I32, VP, VP, ctypes.POINTER(D), VP, S, VP],
                                   ctypes.c_int),
             "hinm_set_option": ([ctypes.c_int, I64], ctypes.c_int),
+            "hinm_spmm_noalloc": ([ctypes.POINTER(PackedT), VP, I64, I64, VP, I64, VP], ctypes.c_int),
             "hinm_get_option": ([ctypes.c_int, ctypes.POINTER(I64)], ctypes.c_int),
             "hinm_status_str": ([ctypes.c_int], ctypes.c_char_p),
             "hinm_last_error": ([], ctypes.c_char_p),
@@ -565,6 +567,26 @@ def spmm(packed: HinmPacked, x: torch.Tensor, out: Optional[torch.Tensor] = None
     return out
 
 
+def spmm_noalloc(packed: HinmPacked, x: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    """Y = (W (.) M) X into ``out`` through hinm_spmm_noalloc: no workspace, no device allocation (the
+    scratch is the library's own device array, shared by every call on the device, so calls on different
+    streams of one device must not overlap).  x bf16 [cin, batch], out bf16 [cout, batch], both with unit
+    column stride.  Asynchronous on the current stream."""
+    p = packed.plan
+    dev = x.device
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[0] != p.cin or dev != packed.device or x.stride(1) != 1:
+        raise ValueError(f"x must be bf16 [{p.cin}, batch] with unit column stride on {packed.device}")
+    batch = x.shape[1]
+    if out.dtype != torch.bfloat16 or out.shape != (p.cout, batch) or out.stride(1) != 1 or out.device != dev:
+        raise ValueError(f"out must be bf16 [{p.cout}, {batch}] with unit column stride on {dev}")
+    ldx = max(x.stride(0), batch) if batch else 0
+    ldy = max(out.stride(0), batch) if batch else 0
+    with torch.cuda.device(dev):
+        _check(library().hinm_spmm_noalloc(ctypes.byref(packed.struct()), x.data_ptr(), batch, ldx, out.data_ptr(),
+                                           ldy, _stream_ptr(dev)))
+    return out
+
+
 def translate_indices(packed: HinmPacked, mapping: torch.Tensor) -> HinmPacked:
     """Rewrites the packed index lists in place through ``mapping`` (int32 [cin] permutation on the device):
     index i becomes mapping[i], pads stay -1 (hinm_translate_indices).  Synchronous; returns ``packed``."""
@@ -662,7 +684,7 @@ def boundary_search_tiles(importance: torch.Tensor, perm: Optional[torch.Tensor]
     return [v[i] for i in range(T)], [pts[i] for i in range(T)]
 
 
-__all__ = ["HinmError", "HinmPacked", "Plan", "plan", "pack", "spmm", "set_option", "get_option", "options",
+__all__ = ["HinmError", "HinmPacked", "Plan", "plan", "pack", "spmm", "spmm_noalloc", "set_option", "get_option", "options",
            "OPTIONS", "translate_indices", "boundary_search", "plan_tiles", "pack_tiles", "boundary_search_tiles",
            "HinmTPacked", "TilePlan", "spmm_tiles_workspace_bytes", "alloc_packed",
            "pack_workspace_bytes",

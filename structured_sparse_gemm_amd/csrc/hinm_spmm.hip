@@ -19,6 +19,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "hinm_internal.h"
@@ -1641,4 +1642,77 @@ extern "C" int hinm_spmm_rows(const hinm_packed_t* packed, const void* x_bf16, i
   if (!hinm::aligned(out_rows, 4)) return fail(HINM_EALIGN, "out_rows is not 4-byte aligned");
   return spmm_impl(packed->plan, uniform_view(*packed), x_bf16, batch, ldx, y_bf16, ldy, out_rows, workspace,
                    workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free product: the scratch of the split reduction (arrival
+// counters, then partial sums) lives in this file-scope device array, one
+// copy per device, instead of in a caller workspace.  In host code the name
+// `scratch` is only a stand-in; kernels get the device address taken with
+// hipGetSymbolAddress.
+// ---------------------------------------------------------------------------
+static_assert(hinm::kWsCounterBytes == 65536, "the scratch size counts 64 KiB of arrival counters");
+static __device__ __align__(256) unsigned char scratch[HINM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+__global__ void zero_words_kernel(unsigned* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];   // device address of `scratch` on each device, once set up
+
+// The device address of the current device's scratch array.  The first call
+// on a device takes the address (with that device current) and clears the
+// arrival counters with a fill kernel on `stream`; every product leaves them
+// at zero again.
+int scratch_address(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(HINM_EDEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(HINM_EDEVICE, "device ordinal %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(HINM_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    constexpr int n = (int)(hinm::kWsCounterBytes / 4);
+    hipLaunchKernelGGL(zero_words_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, static_cast<unsigned*>(p), n);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(HINM_EHIP, "clearing the scratch counters: %s", hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return HINM_OK;
+}
+
+}  // namespace
+
+extern "C" int hinm_spmm_noalloc(const hinm_packed_t* packed, const void* x_bf16, int64_t batch, int64_t ldx,
+                                 void* y_bf16, int64_t ldy, void* stream) {
+  hinm::clear_error();
+  if (!packed) return fail(HINM_EINVAL, "packed is NULL");
+  int st = hinm::check_plan(&packed->plan);
+  if (st) return st;
+  if (batch <= 0)   // spmm_impl's own checks (negative batch, no-op at 0)
+    return spmm_impl(packed->plan, uniform_view(*packed), x_bf16, batch, ldx, y_bf16, ldy, nullptr, nullptr, 0,
+                     stream);
+  const hinm::SpmmShape sh = hinm::spmm_shape(&packed->plan, batch);
+  if (sh.ws_bytes > (int64_t)HINM_NOALLOC_SCRATCH_BYTES)
+    return fail(HINM_EWORKSPACE,
+                "this product needs %lld bytes of scratch, more than the %lld the allocation-free entry point "
+                "holds; call hinm_spmm with a workspace",
+                (long long)sh.ws_bytes, (long long)HINM_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (sh.ws_bytes > 0) {
+    st = hinm::ensure_device();
+    if (st) return st;
+    st = scratch_address(reinterpret_cast<hipStream_t>(stream), &ws);
+    if (st) return st;
+  }
+  return spmm_impl(packed->plan, uniform_view(*packed), x_bf16, batch, ldx, y_bf16, ldy, nullptr, ws,
+                   sh.ws_bytes > 0 ? (size_t)HINM_NOALLOC_SCRATCH_BYTES : 0, stream);
 }

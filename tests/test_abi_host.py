@@ -331,3 +331,25 @@ def test_options_set_get_and_reject(lib):
         hinm.set_option("prefill_nt", 192)
     with pytest.raises(KeyError):
         hinm.options(no_such_option=1)
+
+
+def test_noalloc_host_checks(lib):
+    """hinm_spmm_noalloc's host-side checks, before any launch: a NULL weight, batch 0 (a no-op), every
+    default launch shape of the configured workloads fits the static scratch array, and a product whose
+    scratch need exceeds it (only under forced options) is refused with HINM_EWORKSPACE."""
+    import ctypes
+    assert lib.hinm_spmm_noalloc(None, 16, 16, 16, 16, 16, None) == 1
+    for cout, cin, R, t, v in ((4096, 4096, 64, 0.5, 0.25), (11008, 4096, 64, 0.75, 0.55),
+                               (4096, 11008, 64, 0.75, 0.55), (2048, 4096, 64, 0.75, 0.55),
+                               (960, 1024, 48, 0.5, 0.25), (128, 256, 32, 0.75, 0.5)):
+        p = hinm.plan(cout, cin, R, t, v)
+        for b in (1, 16, 17, 33, 64, 65, 100, 128, 129, 256, 300, 1000, 1024, 2048, 3000, 4096):
+            assert hinm.spmm_workspace_bytes(p, b) <= hinm.HINM_NOALLOC_SCRATCH_BYTES, (cout, cin, b)
+    p = hinm.plan(11008, 4096, 64, 0.75, 0.55)
+    pk = hinm.PackedT(p.raw, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20)
+    assert lib.hinm_spmm_noalloc(ctypes.byref(pk), 1 << 20, 0, 0, 1 << 20, 0, None) == 0
+    with hinm.options(prefill_splits=4):
+        # 1376 items of 256 tokens, each split 4 ways: 344 MiB of partials
+        assert hinm.spmm_workspace_bytes(p, 2048) > hinm.HINM_NOALLOC_SCRATCH_BYTES
+        assert lib.hinm_spmm_noalloc(ctypes.byref(pk), 1 << 20, 2048, 2048, 1 << 20, 2048, None) == 6
+        assert b"allocation-free" in lib.hinm_last_error()
