@@ -267,6 +267,26 @@ int hinm_spmm_workspace_bytes(const hinm_plan_t* plan, int64_t batch, size_t* by
 int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_t batch, int64_t ldx,
               void* y_bf16, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Several packed weights multiplied by one X, in one launch where possible:
+ *     Y_g = (W_g (.) M_g) X,   g = 0 .. n-1
+ * (FlexHiNM-GP notes, key design 4: each product gathers X rows through its
+ * weight's precomputed indices).  This is the product hinm_spmm computes,
+ * once per weight; weights that read the same activations (the q, k and v
+ * projections of a transformer layer, or gate and up) then share one launch,
+ * so at small batches the weights' rows together fill the device without
+ * splitting the reduction dimension, and no launch waits for another's tail.
+ * packed (host) [n] pointers to packed weights with equal cin and tile_rows
+ * (1 <= n <= 8; region counts may differ); y (host) [n] device pointers,
+ * Y_g bf16 [cout_g][ldy[g]]; ldy (host) [n], each >= batch.  X, workspace,
+ * stream, rounding and errors as hinm_spmm; the workspace comes from
+ * hinm_spmm_group_workspace_bytes.  With tile_rows % 64 == 0 one launch runs
+ * the group (the split count follows the group's total rows, so the last
+ * bits of Y_g may differ from hinm_spmm's at batch <= 64); otherwise the
+ * weights run one launch each on `stream`.  Deterministic. */
+int hinm_spmm_group_workspace_bytes(int n, const hinm_packed_t* const* packed, int64_t batch, size_t* bytes);
+int hinm_spmm_group(int n, const hinm_packed_t* const* packed, const void* x_bf16, int64_t batch, int64_t ldx,
+                    void* const* y_bf16, const int64_t* ldy, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Size of the device array that holds hinm_spmm_noalloc's scratch: 64 KiB
  * of arrival counters and 32 MiB of partial sums, one copy on every device
  * the library runs on, held until the process ends.  Every launch shape the

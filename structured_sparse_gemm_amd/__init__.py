@@ -33,7 +33,8 @@ EXPORTS = ("hinm_abi_version", "hinm_plan", "hinm_pack_workspace_bytes", "hinm_p
            "hinm_boundary_workspace_bytes", "hinm_boundary_search", "hinm_plan_tiles",
            "hinm_pack_tiles_workspace_bytes", "hinm_pack_tiles", "hinm_spmm_tiles_workspace_bytes",
            "hinm_spmm_tiles", "hinm_boundary_search_tiles", "hinm_gyro_workspace_bytes", "hinm_gyro_permute",
-           "hinm_set_option", "hinm_get_option", "hinm_spmm_noalloc", "hinm_status_str", "hinm_last_error")
+           "hinm_set_option", "hinm_get_option", "hinm_spmm_noalloc", "hinm_spmm_group_workspace_bytes",
+           "hinm_spmm_group", "hinm_status_str", "hinm_last_error")
 
 # Launch-shape options (hinm_set_option): name -> HINM_OPT_* key.
 OPTIONS = {"decode_path": 1, "decode_wgs": 2, "prefill_nt": 3, "prefill_splits": 4, "prefill_path": 5,
@@ -120,6 +121,8 @@ def library() -> ctypes.CDLL:
                                   ctypes.c_int),
             "hinm_set_option": ([ctypes.c_int, I64], ctypes.c_int),
             "hinm_spmm_noalloc": ([ctypes.POINTER(PackedT), VP, I64, I64, VP, I64, VP], ctypes.c_int),
+            "hinm_spmm_group_workspace_bytes": ([ctypes.c_int, VP, I64, ctypes.POINTER(S)], ctypes.c_int),
+            "hinm_spmm_group": ([ctypes.c_int, VP, VP, I64, I64, VP, VP, VP, S, VP], ctypes.c_int),
             "hinm_get_option": ([ctypes.c_int, ctypes.POINTER(I64)], ctypes.c_int),
             "hinm_status_str": ([ctypes.c_int], ctypes.c_char_p),
             "hinm_last_error": ([], ctypes.c_char_p),
@@ -567,6 +570,59 @@ def spmm(packed: HinmPacked, x: torch.Tensor, out: Optional[torch.Tensor] = None
     return out
 
 
+class Group:
+    """Several packed weights that multiply the same activations (hinm_spmm_group), e.g. the q, k and v
+    projections of a layer.  Holds the C array of weight pointers; the weights must stay alive."""
+
+    def __init__(self, packed):
+        self.packed = list(packed)
+        if not 1 <= len(self.packed) <= 8:
+            raise ValueError("a group holds 1 to 8 packed weights")
+        if any(isinstance(p, HinmTPacked) for p in self.packed):
+            raise ValueError("groups take uniform packed weights (pack, not pack_tiles)")
+        self.structs = [p.struct() for p in self.packed]
+        self.ptrs = (ctypes.c_void_p * len(self.structs))(*[ctypes.addressof(st) for st in self.structs])
+        self._need = {}
+
+    def workspace_bytes(self, batch: int) -> int:
+        key = (batch, _opt_gen)
+        if key not in self._need:
+            n = ctypes.c_size_t()
+            _check(library().hinm_spmm_group_workspace_bytes(len(self.packed), self.ptrs, batch, ctypes.byref(n)))
+            self._need[key] = n.value
+        return self._need[key]
+
+
+def spmm_group(group: Group, x: torch.Tensor, outs=None, workspace: Optional[torch.Tensor] = None):
+    """[(W_g (.) M_g) X for g in the group]: x bf16 [cin, batch]; returns (or fills) one bf16 [cout_g, batch]
+    output per weight.  Asynchronous on the current stream; workspace as in spmm."""
+    ws0 = group.packed[0]
+    p0 = ws0.plan
+    dev = x.device
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[0] != p0.cin or dev != ws0.device or x.stride(1) != 1:
+        raise ValueError(f"x must be bf16 [{p0.cin}, batch] with unit column stride on {ws0.device}")
+    batch = x.shape[1]
+    if outs is None:
+        outs = [torch.empty((pk.plan.cout, batch), dtype=torch.bfloat16, device=dev) for pk in group.packed]
+    for pk, o in zip(group.packed, outs):
+        if o.dtype != torch.bfloat16 or o.shape != (pk.plan.cout, batch) or o.stride(1) != 1 or o.device != dev:
+            raise ValueError(f"each output must be bf16 [cout, {batch}] with unit column stride on {dev}")
+    if len(outs) != len(group.packed):
+        raise ValueError("one output per weight")
+    need = group.workspace_bytes(batch)
+    stream = _stream_ptr(dev)
+    if workspace is None:
+        workspace = _workspace(dev, stream, need)
+    ys = (ctypes.c_void_p * len(outs))(*[o.data_ptr() for o in outs])
+    ldys = (ctypes.c_int64 * len(outs))(*[max(o.stride(0), batch) if batch else 0 for o in outs])
+    ldx = max(x.stride(0), batch) if batch else 0
+    with torch.cuda.device(dev):
+        _check(library().hinm_spmm_group(len(outs), group.ptrs, x.data_ptr(), batch, ldx, ys, ldys,
+                                         workspace.data_ptr() if workspace is not None else None,
+                                         workspace.numel() if workspace is not None else 0, stream))
+    return outs
+
+
 def spmm_noalloc(packed: HinmPacked, x: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
     """Y = (W (.) M) X into ``out`` through hinm_spmm_noalloc: no workspace, no device allocation (the
     scratch is the library's own device array, shared by every call on the device, so calls on different
@@ -684,7 +740,7 @@ def boundary_search_tiles(importance: torch.Tensor, perm: Optional[torch.Tensor]
     return [v[i] for i in range(T)], [pts[i] for i in range(T)]
 
 
-__all__ = ["HinmError", "HinmPacked", "Plan", "plan", "pack", "spmm", "spmm_noalloc", "set_option", "get_option", "options",
+__all__ = ["HinmError", "HinmPacked", "Plan", "plan", "pack", "spmm", "spmm_noalloc", "Group", "spmm_group", "set_option", "get_option", "options",
            "OPTIONS", "translate_indices", "boundary_search", "plan_tiles", "pack_tiles", "boundary_search_tiles",
            "HinmTPacked", "TilePlan", "spmm_tiles_workspace_bytes", "alloc_packed",
            "pack_workspace_bytes",

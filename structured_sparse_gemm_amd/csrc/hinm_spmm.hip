@@ -59,7 +59,56 @@ struct SpmmArgs {
   const int32_t* tiles;      // NULL (uniform counts), or [n_tiles][4]: first dense block, n_dense,
                              // first 2:4 block, n_24 of each tile
   int kd_total, ks_total;    // dense and 2:4 K-blocks over all tiles
+  int part_rows;             // rows of a split reduction's partial-sum planes (all weights of a group)
 };
+
+// Several packed weights multiplied by one X in one launch (hinm_spmm_group):
+// the weights' tile row blocks are numbered one after another, and a
+// workgroup (split decode) or work item (prefill) takes the fields of the
+// weight its row block belongs to.
+constexpr int kMaxSeg = 8;
+struct Seg {
+  const uint16_t* val_d;
+  const int32_t* idx_d;
+  const uint16_t* val_s;
+  const uint64_t* meta;
+  const int32_t* idx_s;
+  uint16_t* y;
+  int64_t ldy;
+  int cout, n_tiles, nkb_d, nkb_s, kd_total, ks_total;
+  int trb0;                  // first row block of this weight in the concatenation
+  int row0;                  // first row of this weight in the partial-sum planes
+};
+struct Segs {
+  int n;                     // 0 or 1: one weight, the fields of SpmmArgs
+  Seg s[kMaxSeg];
+};
+
+// The weight of concatenated row block gtrb: patches a's per-weight fields and
+// returns the first row block and row of that weight.
+__device__ inline void select_seg(const Segs& segs, int gtrb, SpmmArgs& a, int& trb0, int& row0) {
+  trb0 = 0;
+  row0 = 0;
+  if (segs.n <= 1) return;
+  int g = 0;
+  for (int k = 1; k < segs.n; ++k) g = gtrb >= segs.s[k].trb0 ? k : g;
+  const Seg& S = segs.s[g];
+  a.val_d = S.val_d;
+  a.idx_d = S.idx_d;
+  a.val_s = S.val_s;
+  a.meta = S.meta;
+  a.idx_s = S.idx_s;
+  a.y = S.y;
+  a.ldy = S.ldy;
+  a.cout = S.cout;
+  a.n_tiles = S.n_tiles;
+  a.nkb_d = S.nkb_d;
+  a.nkb_s = S.nkb_s;
+  a.kd_total = S.kd_total;
+  a.ks_total = S.ks_total;
+  trb0 = S.trb0;
+  row0 = S.row0;
+}
 
 // Tile t's K-blocks: first dense block and count, first 2:4 block and count.
 struct TileK {
@@ -432,7 +481,7 @@ __device__ inline int xs_gran(int p, int g) {
 }
 
 template <int NTOK, int MAXB, bool FAST, int NG>
-__global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(SpmmArgs a, int splits, int n_tb,
+__global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(SpmmArgs a0, Segs segs, int splits, int n_tb,
                                                                 float* __restrict__ part,
                                                                 unsigned* __restrict__ counters) {
   constexpr int CPR = NTOK / 8;                // 16-byte chunks per X row
@@ -450,9 +499,13 @@ __global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(SpmmArgs a, int 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool gather = wave >= 4;
   const int kc = lane >> 4, i16 = lane & 15;
-  const int nrb = a.rows / 64;
+  const int nrb = a0.rows / 64;
   const int split = blockIdx.x % splits;
-  const int trb = blockIdx.x / splits;           // tile * nrb + row block
+  const int gtrb = blockIdx.x / splits;          // row block over all weights of a group
+  SpmmArgs a = a0;
+  int trb0, row0;                                // this weight's first row block and partial-sum row
+  select_seg(segs, gtrb, a, trb0, row0);
+  const int trb = gtrb - trb0;                   // tile * nrb + row block
   const int t = trb / nrb, rb = trb % nrb;
   const int tb = blockIdx.y;
   const int n0 = tb * NTOK;
@@ -665,13 +718,13 @@ __global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(SpmmArgs a, int 
       }
     return;
   }
-  // Partial sums: part[split][tb][cout][NTOK].  Partials and the arrival
+  // Partial sums: part[split][tb][rows of all weights][NTOK].  Partials and the arrival
   // counter go through agent-scope (device-coherent) stores, loads and
   // atomics, and each workgroup waits for its stores to complete before it
   // counts itself in, so nothing needs a whole-cache writeback or
   // invalidate.  The last workgroup of a (tile row block, token block) to
   // arrive adds the partials in split order and puts the counter back to 0.
-  float* my = part + (((int64_t)split * n_tb + tb) * a.cout) * NTOK;
+  float* my = part + (((int64_t)split * n_tb + tb) * a.part_rows + row0) * NTOK;
   if (!gather)
     for (int nb = 0; nb < NB; ++nb)
       for (int e = 0; e < 4; ++e)
@@ -679,12 +732,12 @@ __global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(SpmmArgs a, int 
                            __HIP_MEMORY_SCOPE_AGENT);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  unsigned* ctr = counters + (int64_t)trb * n_tb + tb;
+  unsigned* ctr = counters + (int64_t)gtrb * n_tb + tb;
   if (threadIdx.x == 0) s_last = arrive(ctr, splits);
   __syncthreads();
   if (!s_last || threadIdx.x >= 256) return;
-  const int64_t plane = (int64_t)n_tb * a.cout * NTOK;
-  const float* p0 = part + ((int64_t)tb * a.cout + grow_base) * NTOK;
+  const int64_t plane = (int64_t)n_tb * a.part_rows * NTOK;
+  const float* p0 = part + ((int64_t)tb * a.part_rows + row0 + grow_base) * NTOK;
   float sum[OPT];
   for (int k = 0; k < OPT; ++k) sum[k] = 0.f;
   for (int sp0 = 0; sp0 < splits; sp0 += 8) {
@@ -1249,22 +1302,7 @@ __device__ inline void prefill_body_staged(const SpmmArgs& a, const BufRes& res,
 // token-block major, are cut into 8 contiguous ranges, one per XCD; the XCD's
 // workgroups take its range in order, so each XCD works through its token
 // blocks one after another and keeps the current X slice in its L2.
-template <int NT, bool SPLIT>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
-  using C = PrefillCfg<NT>;
-  __shared__ __attribute__((aligned(16))) uint16_t xs_a[64 * C::PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t xs_b[64 * C::PITCH];
-  __shared__ __attribute__((aligned(16))) uint32_t ms_a[128];
-  __shared__ __attribute__((aligned(16))) uint32_t ms_b[128];
-  uint16_t* const xs[2] = {xs_a, xs_b};   // separate LDS objects: loads into one tile never
-  uint32_t* const ms[2] = {ms_a, ms_b};   // hold up reads of the other
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nrb = a.rows / 64;
-  const int n_tr = a.n_tiles * nrb;
-  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8, per_xcd = gridDim.x / 8;
-  const int tok_w = wave * C::TW;
-
+__device__ inline BufRes make_res(const SpmmArgs& a) {
   BufRes res;
   const uint32_t xbytes = (uint32_t)(((int64_t)(a.cin - 1) * a.ldx + a.batch) * 2);
   res.x = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, (int)xbytes, kBufferWord3);
@@ -1274,6 +1312,25 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
   res.id = __builtin_amdgcn_make_buffer_rsrc((void*)a.idx_d, (short)0, (int)((uint32_t)a.kd_total * 32u * 4u), kBufferWord3);
   res.is = __builtin_amdgcn_make_buffer_rsrc((void*)a.idx_s, (short)0, (int)((uint32_t)a.ks_total * 64u * 4u), kBufferWord3);
   res.ldx_bytes = (uint32_t)a.ldx * 2u;
+  return res;
+}
+
+template <int NT, bool SPLIT>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a0, Segs segs, int n_tb) {
+  using C = PrefillCfg<NT>;
+  __shared__ __attribute__((aligned(16))) uint16_t xs_a[64 * C::PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t xs_b[64 * C::PITCH];
+  __shared__ __attribute__((aligned(16))) uint32_t ms_a[128];
+  __shared__ __attribute__((aligned(16))) uint32_t ms_b[128];
+  uint16_t* const xs[2] = {xs_a, xs_b};   // separate LDS objects: loads into one tile never
+  uint32_t* const ms[2] = {ms_a, ms_b};   // hold up reads of the other
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nrb = a0.rows / 64;
+  const int n_tr = a0.n_tiles * nrb;              // row blocks over all weights of a group
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8, per_xcd = gridDim.x / 8;
+  const int tok_w = wave * C::TW;
+  const SpmmArgs& a = a0;                         // fields shared by every weight (per-tile order below)
 
   // Per-tile counts: every tile runs the same number of K-block steps (its
   // kept entries per row are fixed by t_s), but a 2:4 block gathers 64 X rows
@@ -1318,7 +1375,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a, int n_tb) {
   for (int it = i_lo + slot; it < i_hi; it += per_xcd) {
     {
       const int split = SPLIT ? it % splits : 0, item = SPLIT ? it / splits : it;
-      const int tb = item / n_tr, trb = item % n_tr;
+      const int tb = item / n_tr, gtrb = item % n_tr;
+      SpmmArgs a = a0;
+      int trb0, row0;
+      select_seg(segs, gtrb, a, trb0, row0);
+      const BufRes res = make_res(a);
+      const int trb = gtrb - trb0;
       const int n0 = tb * NT;
       int t = trb / nrb;
       const int rb = trb % nrb;
@@ -1432,6 +1494,12 @@ int ensure_device() {
 
 }  // namespace hinm
 
+static bool segs_y_vec(const Segs& sg) {
+  for (int g = 0; g < sg.n; ++g)
+    if (!hinm::aligned(sg.s[g].y, 16) || sg.s[g].ldy % 8 != 0) return false;
+  return true;
+}
+
 // The packed buffers of either layout: the uniform one (tiles == NULL, block
 // counts from the plan) or the per-tile one (a device tile table).
 struct PackedView {
@@ -1446,9 +1514,23 @@ struct PackedView {
 
 // `p` has been validated by the caller (for the per-tile layout it carries
 // the largest per-tile pads and the buffer totals).
+// The prefill and split decode kernels address X and the packed buffers with
+// 32-bit buffer offsets and gather with a 24-bit multiply (row index and row
+// pitch in bytes both below 2^24).
+static bool fits32(const hinm_plan_t& p, int64_t ldx, int64_t batch) {
+  const int64_t lim = (int64_t)1 << 31, lim24 = (int64_t)1 << 24;
+  const int64_t xbytes = ((int64_t)(p.cin - 1) * ldx + batch) * 2;
+  return xbytes < lim && ldx * 2 < lim24 && p.cin <= lim24 && p.bytes_val_dense < lim && p.bytes_val_24 < lim &&
+         p.bytes_idx_dense < lim && p.bytes_idx_24 < lim && p.bytes_meta_24 < lim;
+}
+
+// segs: NULL, or the weights of a group (then p is their combined shape: cout
+// and n_tiles summed, pads and buffer sizes the largest; packed_v, y_bf16 and
+// ldy are the first weight's); only the split decode and prefill kernels
+// take a group, and the caller checks that one of them runs.
 static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const void* x_bf16, int64_t batch,
                      int64_t ldx, void* y_bf16, int64_t ldy, const int32_t* out_rows, void* workspace,
-                     size_t workspace_bytes, void* stream_) {
+                     size_t workspace_bytes, void* stream_, const Segs* segs = nullptr) {
   const PackedView* packed = &packed_v;
   int st = HINM_OK;
   if (batch < 0) return fail(HINM_ESHAPE, "batch=%lld is negative", (long long)batch);
@@ -1463,10 +1545,11 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
       {packed->val_dense, p.bytes_val_dense, "val_dense"}, {packed->idx_dense, p.bytes_idx_dense, "idx_dense"},
       {packed->val_24, p.bytes_val_24, "val_24"}, {packed->meta_24, p.bytes_meta_24, "meta_24"},
       {packed->idx_24, p.bytes_idx_24, "idx_24"}};
-  for (const Buf& b : bufs) {
-    if (b.bytes > 0 && !b.ptr) return fail(HINM_EINVAL, "%s is NULL but holds %lld bytes", b.name, (long long)b.bytes);
-    if (b.ptr && !hinm::aligned(b.ptr, 16)) return fail(HINM_EALIGN, "%s is not 16-byte aligned", b.name);
-  }
+  if (!segs)   // a group's weights are checked one by one by its entry point
+    for (const Buf& b : bufs) {
+      if (b.bytes > 0 && !b.ptr) return fail(HINM_EINVAL, "%s is NULL but holds %lld bytes", b.name, (long long)b.bytes);
+      if (b.ptr && !hinm::aligned(b.ptr, 16)) return fail(HINM_EALIGN, "%s is not 16-byte aligned", b.name);
+    }
   hinm::SpmmShape sh = hinm::spmm_shape(&p, batch);
   if (sh.ws_bytes > 0) {
     if (!workspace || workspace_bytes < (size_t)sh.ws_bytes)
@@ -1512,6 +1595,11 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
   a.tiles = packed->tiles;
   a.kd_total = packed->kd_total;
   a.ks_total = packed->ks_total;
+  a.part_rows = p.cout;
+  Segs one;
+  one.n = 0;
+  if (segs) a.y_vec = a.y_vec && segs_y_vec(*segs);
+  const Segs& sg = segs ? *segs : one;
 
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   // The prefill and split decode kernels address X and the packed buffers
@@ -1519,20 +1607,18 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
   // and row pitch in bytes both below 2^24); beyond those ranges kernels
   // with 64-bit addressing take over (the generic kernel without a K split,
   // or the 16-row decode kernel; neither needs a workspace).
-  const int64_t lim = (int64_t)1 << 31, lim24 = (int64_t)1 << 24;
-  const int64_t xbytes = ((int64_t)(p.cin - 1) * ldx + batch) * 2;
-  const bool fits32 = xbytes < lim && ldx * 2 < lim24 && p.cin <= lim24 && p.bytes_val_dense < lim &&
-                      p.bytes_val_24 < lim && p.bytes_idx_dense < lim && p.bytes_idx_24 < lim &&
-                      p.bytes_meta_24 < lim;
-  if (sh.path == hinm::kPathDecodeSplit && !fits32) {
+  const bool f32 = fits32(p, ldx, batch);
+  if (sh.path == hinm::kPathDecodeSplit && !f32) {
     sh.path = hinm::kPathDecode;
     sh.splits = 1;
     a.splits = 1;
   }
-  if (packed->tiles && !((sh.path == hinm::kPathPrefill || sh.path == hinm::kPathDecodeSplit) && fits32))
+  if (packed->tiles && !((sh.path == hinm::kPathPrefill || sh.path == hinm::kPathDecodeSplit) && f32))
     return fail(HINM_ESHAPE, "the per-tile layout needs tile_rows %% 64 == 0 and buffers below 2^31 bytes");
+  if (segs && !((sh.path == hinm::kPathPrefill || sh.path == hinm::kPathDecodeSplit) && f32))
+    return fail(HINM_ESHAPE, "internal: a group of weights needs the split decode or prefill kernel");
   if (sh.path == hinm::kPathPrefill) {
-    if (!fits32) {
+    if (!f32) {
       sh.path = hinm::kPathGeneric;
       sh.nt = 64;
       sh.n_tblocks = (int)((batch + 63) / 64);
@@ -1548,12 +1634,12 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
     // 64 tokens: 96 KB rounds (24 / 12 blocks) with 4 gather waves.
     const dim3 grid(p.n_tiles * (p.tile_rows / 64) * sh.splits, sh.n_tblocks), b6(384), b8(512);
     switch (sh.nt * 2 + (fast ? 1 : 0)) {
-      case 33: hipLaunchKernelGGL((decode5_kernel<16, 24, true, 2>), grid, b6, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
-      case 32: hipLaunchKernelGGL((decode5_kernel<16, 24, false, 2>), grid, b6, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
-      case 65: hipLaunchKernelGGL((decode5_kernel<32, 24, true, 4>), grid, b8, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
-      case 64: hipLaunchKernelGGL((decode5_kernel<32, 24, false, 4>), grid, b8, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
-      case 129: hipLaunchKernelGGL((decode5_kernel<64, 12, true, 4>), grid, b8, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
-      default: hipLaunchKernelGGL((decode5_kernel<64, 12, false, 4>), grid, b8, 0, stream, a, sh.splits, sh.n_tblocks, part, counters); break;
+      case 33: hipLaunchKernelGGL((decode5_kernel<16, 24, true, 2>), grid, b6, 0, stream, a, sg, sh.splits, sh.n_tblocks, part, counters); break;
+      case 32: hipLaunchKernelGGL((decode5_kernel<16, 24, false, 2>), grid, b6, 0, stream, a, sg, sh.splits, sh.n_tblocks, part, counters); break;
+      case 65: hipLaunchKernelGGL((decode5_kernel<32, 24, true, 4>), grid, b8, 0, stream, a, sg, sh.splits, sh.n_tblocks, part, counters); break;
+      case 64: hipLaunchKernelGGL((decode5_kernel<32, 24, false, 4>), grid, b8, 0, stream, a, sg, sh.splits, sh.n_tblocks, part, counters); break;
+      case 129: hipLaunchKernelGGL((decode5_kernel<64, 12, true, 4>), grid, b8, 0, stream, a, sg, sh.splits, sh.n_tblocks, part, counters); break;
+      default: hipLaunchKernelGGL((decode5_kernel<64, 12, false, 4>), grid, b8, 0, stream, a, sg, sh.splits, sh.n_tblocks, part, counters); break;
     }
   } else if (sh.path == hinm::kPathDecode) {
     const dim3 grid(p.n_tiles * (p.tile_rows / 16), sh.n_tblocks), block(kDecWaves * 64);
@@ -1576,11 +1662,11 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
     // the K-split epilogue is a separate instantiation, so the unsplit
     // kernel keeps its registers
     if (sh.nt == 256) {
-      if (sh.splits > 1) hipLaunchKernelGGL((prefill_kernel<256, true>), dim3(nwg), dim3(256), 0, stream, a, sh.n_tblocks);
-      else hipLaunchKernelGGL((prefill_kernel<256, false>), dim3(nwg), dim3(256), 0, stream, a, sh.n_tblocks);
+      if (sh.splits > 1) hipLaunchKernelGGL((prefill_kernel<256, true>), dim3(nwg), dim3(256), 0, stream, a, sg, sh.n_tblocks);
+      else hipLaunchKernelGGL((prefill_kernel<256, false>), dim3(nwg), dim3(256), 0, stream, a, sg, sh.n_tblocks);
     } else {
-      if (sh.splits > 1) hipLaunchKernelGGL((prefill_kernel<128, true>), dim3(nwg), dim3(256), 0, stream, a, sh.n_tblocks);
-      else hipLaunchKernelGGL((prefill_kernel<128, false>), dim3(nwg), dim3(256), 0, stream, a, sh.n_tblocks);
+      if (sh.splits > 1) hipLaunchKernelGGL((prefill_kernel<128, true>), dim3(nwg), dim3(256), 0, stream, a, sg, sh.n_tblocks);
+      else hipLaunchKernelGGL((prefill_kernel<128, false>), dim3(nwg), dim3(256), 0, stream, a, sg, sh.n_tblocks);
     }
   } else {
     const dim3 grid(sh.n_tblocks, p.n_tiles * sh.n_rblocks, sh.splits), block(kWaves * 64);
@@ -1642,6 +1728,126 @@ extern "C" int hinm_spmm_rows(const hinm_packed_t* packed, const void* x_bf16, i
   if (!hinm::aligned(out_rows, 4)) return fail(HINM_EALIGN, "out_rows is not 4-byte aligned");
   return spmm_impl(packed->plan, uniform_view(*packed), x_bf16, batch, ldx, y_bf16, ldy, out_rows, workspace,
                    workspace_bytes, stream);
+}
+
+// A group of packed weights for hinm_spmm_group: checked one by one, with
+// their combined shape (cout and n_tiles summed, pads and buffer sizes the
+// largest), which decides the launch shape of the one launch.
+static int group_shape(int n, const hinm_packed_t* const* packed, hinm_plan_t* comb) {
+  if (n < 1 || n > kMaxSeg) return fail(HINM_EINVAL, "n=%d weights; 1 to %d are supported", n, kMaxSeg);
+  if (!packed) return fail(HINM_EINVAL, "packed is NULL");
+  int64_t cout = 0, tiles = 0;
+  for (int g = 0; g < n; ++g) {
+    if (!packed[g]) return fail(HINM_EINVAL, "packed[%d] is NULL", g);
+    const hinm_plan_t& q = packed[g]->plan;
+    int st = hinm::check_plan(&q);
+    if (st) return st;
+    if (q.cin != packed[0]->plan.cin || q.tile_rows != packed[0]->plan.tile_rows)
+      return fail(HINM_ESHAPE, "packed[%d] has cin=%d, tile_rows=%d; a group needs those of packed[0] (%d, %d)", g, q.cin,
+                  q.tile_rows, packed[0]->plan.cin, packed[0]->plan.tile_rows);
+    const hinm_packed_t& k = *packed[g];
+    struct Buf { const void* ptr; int64_t bytes; const char* name; } bufs[5] = {
+        {k.val_dense, q.bytes_val_dense, "val_dense"}, {k.idx_dense, q.bytes_idx_dense, "idx_dense"},
+        {k.val_24, q.bytes_val_24, "val_24"}, {k.meta_24, q.bytes_meta_24, "meta_24"}, {k.idx_24, q.bytes_idx_24, "idx_24"}};
+    for (const Buf& b : bufs) {
+      if (b.bytes > 0 && !b.ptr) return fail(HINM_EINVAL, "packed[%d]: %s is NULL but holds %lld bytes", g, b.name, (long long)b.bytes);
+      if (b.ptr && !hinm::aligned(b.ptr, 16)) return fail(HINM_EALIGN, "packed[%d]: %s is not 16-byte aligned", g, b.name);
+    }
+    cout += q.cout;
+    tiles += q.n_tiles;
+  }
+  if (cout > INT32_MAX) return fail(HINM_ESHAPE, "the group's rows exceed 2^31");
+  hinm_plan_t c = packed[0]->plan;
+  for (int g = 1; g < n; ++g) {
+    const hinm_plan_t& q = packed[g]->plan;
+    c.n_dense_pad = std::max(c.n_dense_pad, q.n_dense_pad);
+    c.n_24_pad = std::max(c.n_24_pad, q.n_24_pad);
+    c.bytes_val_dense = std::max(c.bytes_val_dense, q.bytes_val_dense);
+    c.bytes_idx_dense = std::max(c.bytes_idx_dense, q.bytes_idx_dense);
+    c.bytes_val_24 = std::max(c.bytes_val_24, q.bytes_val_24);
+    c.bytes_meta_24 = std::max(c.bytes_meta_24, q.bytes_meta_24);
+    c.bytes_idx_24 = std::max(c.bytes_idx_24, q.bytes_idx_24);
+  }
+  c.cout = (int32_t)cout;
+  c.n_tiles = (int32_t)tiles;
+  *comb = c;
+  return HINM_OK;
+}
+
+// One launch for the whole group when the split decode or the prefill kernel
+// runs it; otherwise one launch per weight.
+static bool group_together(int n, const hinm_plan_t& comb, int64_t batch, int64_t ldx) {
+  if (n < 2 || comb.tile_rows % 64 != 0) return false;
+  const hinm::SpmmShape sh = hinm::spmm_shape(&comb, batch);
+  return (sh.path == hinm::kPathPrefill || sh.path == hinm::kPathDecodeSplit) && fits32(comb, ldx, batch);
+}
+
+extern "C" int hinm_spmm_group_workspace_bytes(int n, const hinm_packed_t* const* packed, int64_t batch,
+                                               size_t* bytes) {
+  hinm::clear_error();
+  hinm_plan_t comb;
+  int st = group_shape(n, packed, &comb);
+  if (st) return st;
+  if (!bytes) return fail(HINM_EINVAL, "bytes is NULL");
+  if (batch < 0) return fail(HINM_ESHAPE, "batch=%lld is negative", (long long)batch);
+  // enough for either way of running it (one launch, or one per weight)
+  int64_t need = 0;
+  if (batch > 0) {
+    need = n > 1 && comb.tile_rows % 64 == 0 ? hinm::spmm_shape(&comb, batch).ws_bytes : 0;
+    for (int g = 0; g < n; ++g) need = std::max(need, hinm::spmm_shape(&packed[g]->plan, batch).ws_bytes);
+  }
+  *bytes = (size_t)need;
+  return HINM_OK;
+}
+
+extern "C" int hinm_spmm_group(int n, const hinm_packed_t* const* packed, const void* x_bf16, int64_t batch,
+                               int64_t ldx, void* const* y_bf16, const int64_t* ldy, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  hinm::clear_error();
+  hinm_plan_t comb;
+  int st = group_shape(n, packed, &comb);
+  if (st) return st;
+  if (!y_bf16 || !ldy) return fail(HINM_EINVAL, "y and ldy must be non-NULL");
+  for (int g = 0; g < n; ++g) {
+    if (ldy[g] < batch) return fail(HINM_ESHAPE, "ldy[%d]=%lld is below batch=%lld", g, (long long)ldy[g], (long long)batch);
+    if (batch > 0 && (!y_bf16[g] || !hinm::aligned(y_bf16[g], 2)))
+      return fail(y_bf16[g] ? HINM_EALIGN : HINM_EINVAL, "y[%d] must be non-NULL and 2-byte aligned", g);
+  }
+  if (!group_together(n, comb, batch, ldx)) {
+    for (int g = 0; g < n; ++g) {
+      st = spmm_impl(packed[g]->plan, uniform_view(*packed[g]), x_bf16, batch, ldx, y_bf16[g], ldy[g], nullptr,
+                     workspace, workspace_bytes, stream);
+      if (st) return st;
+    }
+    return HINM_OK;
+  }
+  Segs sg;
+  sg.n = n;
+  int trb = 0, row = 0;
+  for (int g = 0; g < n; ++g) {
+    const hinm_packed_t& k = *packed[g];
+    const hinm_plan_t& q = k.plan;
+    Seg& S = sg.s[g];
+    S.val_d = static_cast<const uint16_t*>(k.val_dense);
+    S.idx_d = k.idx_dense;
+    S.val_s = static_cast<const uint16_t*>(k.val_24);
+    S.meta = k.meta_24;
+    S.idx_s = k.idx_24;
+    S.y = static_cast<uint16_t*>(y_bf16[g]);
+    S.ldy = ldy[g];
+    S.cout = q.cout;
+    S.n_tiles = q.n_tiles;
+    S.nkb_d = q.n_dense_pad / HINM_KB_DENSE;
+    S.nkb_s = q.n_24_pad / HINM_KB_24;
+    S.kd_total = q.n_tiles * S.nkb_d;
+    S.ks_total = q.n_tiles * S.nkb_s;
+    S.trb0 = trb;
+    S.row0 = row;
+    trb += q.n_tiles * (q.tile_rows / 64);
+    row += q.cout;
+  }
+  return spmm_impl(comb, uniform_view(*packed[0]), x_bf16, batch, ldx, y_bf16[0], ldy[0], nullptr, workspace,
+                   workspace_bytes, stream, &sg);
 }
 
 // ---------------------------------------------------------------------------

@@ -353,3 +353,31 @@ def test_noalloc_host_checks(lib):
         assert hinm.spmm_workspace_bytes(p, 2048) > hinm.HINM_NOALLOC_SCRATCH_BYTES
         assert lib.hinm_spmm_noalloc(ctypes.byref(pk), 1 << 20, 2048, 2048, 1 << 20, 2048, None) == 6
         assert b"allocation-free" in lib.hinm_last_error()
+
+
+def test_group_host_errors(lib):
+    """hinm_spmm_group's host-side checks (before any launch): weight count, NULL entries, unequal cin
+    or tile_rows, NULL outputs, ldy below the batch; batch 0 is a no-op."""
+    import ctypes
+    p1 = hinm.plan(256, 1024, 64, 0.75, 0.55)
+    p2 = hinm.plan(128, 1024, 64, 0.5, 0.25)
+    p3 = hinm.plan(128, 512, 64, 0.5, 0.25)
+    fake = 1 << 20
+    k1, k2, k3 = (hinm.PackedT(p.raw, fake, fake, fake, fake, fake) for p in (p1, p2, p3))
+    arr = lambda *ks: (ctypes.c_void_p * len(ks))(*[ctypes.addressof(k) for k in ks])
+    ys = (ctypes.c_void_p * 2)(fake, fake)
+    ldy = (ctypes.c_int64 * 2)(16, 16)
+    n = ctypes.c_size_t()
+    assert lib.hinm_spmm_group_workspace_bytes(0, arr(k1), 16, ctypes.byref(n)) == 1
+    assert lib.hinm_spmm_group_workspace_bytes(9, arr(*([k1] * 9)), 16, ctypes.byref(n)) == 1
+    assert lib.hinm_spmm_group_workspace_bytes(2, arr(k1, k2), 16, ctypes.byref(n)) == 0
+    assert n.value >= max(hinm.spmm_workspace_bytes(p1, 16), hinm.spmm_workspace_bytes(p2, 16))
+    assert lib.hinm_spmm_group(2, arr(k1, k3), fake, 16, 16, ys, ldy, None, 0, None) == 2     # unequal cin
+    assert lib.hinm_spmm_group(2, None, fake, 16, 16, ys, ldy, None, 0, None) == 1
+    assert lib.hinm_spmm_group(2, arr(k1, k2), fake, 16, 16, None, ldy, None, 0, None) == 1
+    assert lib.hinm_spmm_group(2, arr(k1, k2), fake, 16, 16, ys, (ctypes.c_int64 * 2)(16, 8), None, 0, None) == 2
+    assert lib.hinm_spmm_group(2, arr(k1, k2), fake, 16, 16, (ctypes.c_void_p * 2)(fake, None), ldy, None, 0,
+                               None) == 1
+    assert lib.hinm_spmm_group(2, arr(k1, k2), fake, 0, 0, ys, (ctypes.c_int64 * 2)(0, 0), None, 0, None) == 0
+    bad = hinm.PackedT(p2.raw, fake, None, fake, fake, fake)
+    assert lib.hinm_spmm_group(2, arr(k1, bad), fake, 16, 16, ys, ldy, None, 0, None) == 1

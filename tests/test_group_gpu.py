@@ -1,0 +1,78 @@
+"""hinm_spmm_group: several packed weights that read the same X, in one launch, against the float64
+oracle per weight (the same bar as hinm_spmm), and bit for bit against hinm_spmm where both launches
+split the reduction the same way."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.hinm as oh
+import synth
+from helpers import bits_of, check_y, oracle_pack
+
+pytestmark = pytest.mark.gpu
+hinm = pytest.importorskip("structured_sparse_gemm_amd")
+DEV = torch.device("cuda:0")
+
+
+def _packed(w):
+    pk = hinm.pack(w.w_bf16.to(DEV), w.importance.to(DEV), w.tile_rows, w.t_s, w.v_s, w.perm.to(DEV))
+    _, _, inter = oracle_pack(w)
+    return pk, oh.masked_weight(bits_of(w.w_bf16), inter["mask"])
+
+
+def _check_group(ws, batches, label):
+    pks, whs = zip(*[_packed(w) for w in ws])
+    grp = hinm.Group(pks)
+    cin = ws[0].cin
+    for b in batches:
+        x = torch.randn(cin, b, generator=torch.Generator().manual_seed(b)).to(torch.bfloat16)
+        print(f"[group] {label}: {len(ws)} weights, batch {b}", flush=True)
+        ys = hinm.spmm_group(grp, x.to(DEV))
+        torch.cuda.synchronize()
+        xf = synth.as_f64(x)
+        for g, (y, wh) in enumerate(zip(ys, whs)):
+            check_y(y, oh.spmm(wh, xf), np.abs(wh) @ np.abs(xf), f"{label} weight {g} batch {b}")
+    return pks, grp
+
+
+def test_group_qkv_shapes():
+    """Three 4096 x 4096 weights (the q, k, v of a 7B-shaped layer) at decode and prefill batches."""
+    ws = [synth.stack_layer(3, proj, batch=1) for proj in (0, 1, 2)]
+    pks, grp = _check_group(ws, (1, 16, 64, 2048), "qkv")
+    # at batch 2048 both the group and each single product run unsplit: same bits
+    x = torch.randn(4096, 2048, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).to(DEV)
+    ys = hinm.spmm_group(grp, x)
+    for pk, y in zip(pks, ys):
+        assert torch.equal(y.view(torch.int16), hinm.spmm(pk, x).view(torch.int16))
+
+
+def test_group_gate_up_shapes():
+    ws = [synth.stack_layer(7, proj, batch=1) for proj in (4, 5)]
+    _check_group(ws, (1, 16, 300), "gate/up")
+
+
+def test_group_mixed_regions_and_ragged_batches():
+    """Weights with different t_s / v_s (so different K-block counts) and rows, ragged batches, a
+    strided X."""
+    ws = [synth.small(512, 2048, 64, 0.75, 0.55, 1, seed=21), synth.small(256, 2048, 64, 0.5, 0.25, 1, seed=22),
+          synth.small(768, 2048, 64, 0.6, 0.6, 1, seed=23)]
+    pks, grp = _check_group(ws, (1, 7, 17, 33, 63, 65, 129, 1000, 1031), "mixed")
+    big = torch.randn(2048, 40, generator=torch.Generator().manual_seed(9)).to(torch.bfloat16)
+    outs = [torch.full((pk.plan.cout, 48), 7.0, dtype=torch.bfloat16, device=DEV) for pk in pks]
+    hinm.spmm_group(grp, big.to(DEV)[:, :24], outs=[o[:, :24] for o in outs])
+    torch.cuda.synchronize()
+    xf = synth.as_f64(big[:, :24])
+    for o, w in zip(outs, ws):
+        _, _, inter = oracle_pack(w)
+        wh = oh.masked_weight(bits_of(w.w_bf16), inter["mask"])
+        check_y(o[:, :24], oh.spmm(wh, xf), np.abs(wh) @ np.abs(xf), "strided")
+        assert (o[:, 24:] == 7.0).all()
+
+
+def test_group_32_row_tiles_run_one_launch_each():
+    ws = [synth.small(128, 512, 32, 0.75, 0.5, 1, seed=31), synth.small(96, 512, 32, 0.5, 0.25, 1, seed=32)]
+    pks, grp = _check_group(ws, (1, 16, 100), "32-row tiles")
+    x = torch.randn(512, 100, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16).to(DEV)
+    ys = hinm.spmm_group(grp, x)
+    for pk, y in zip(pks, ys):
+        assert torch.equal(y.view(torch.int16), hinm.spmm(pk, x).view(torch.int16))
