@@ -1,23 +1,28 @@
 """Benchmark of the HiNM sparse-weight x dense-activation product on one MI355X.
 
-Workload: LLaMA-7B down_proj weight 4096 x 11008 (cout x cin) in bf16, HiNM
-packed with tile_rows 64, t_s 0.75, v_s 0.55 (550 dense / 4404 2:4 / 6054
-pruned vectors per tile), random per-tile input permutations; X bf16
+Headline workload: LLaMA-7B down_proj weight 4096 x 11008 (cout x cin) in
+bf16, HiNM packed with tile_rows 64, t_s 0.75, v_s 0.55 (550 dense / 4404 2:4
+/ 6054 pruned vectors per tile), random per-tile input permutations; X bf16
 [11008 x batch].  A step is one product Y = (W (.) M) X at batch 2048 (the
 compute-bound point); the batch-16 product (the bandwidth-bound point) and
-the one-time pack are timed beside it and reported in the same JSON line.
+the one-time pack are timed beside it and reported in the same JSON line,
+with one row per workload and batch of the five configurations (each with
+its roofline fractions), the 13-point batch sweep of the 32-layer 7B-shaped
+stack, the dense torch.matmul comparator, the GPU's empirical peaks and its
+clocks, the side rows of the later steps and the CPU oracle baseline.
 
-Inputs are resident in HBM before timing starts; successive steps rotate
+Inputs are resident in HBM before timing starts; successive products rotate
 through enough copies of the packed weight, X and Y (>= 1 GiB) that the
-256 MB last-level cache cannot serve a repeat.  The K timed steps are one
-replay of a HIP graph holding K products (captured once, replayed once
-untimed first), bracketed by device synchronisation and timed with HIP
-events on the replaying stream: the products run back to back as a serving
-loop would issue them, without the Python binding's per-call host cost
-(about 10 us, which exceeds a batch-16 product).  Eager per-call times are
-reported beside.
+256 MB last-level cache cannot serve a repeat, and so does the dense
+comparator's weight.  The K timed steps are one replay of a HIP graph
+holding K products (captured once, replayed ten times untimed first),
+bracketed by device synchronisation and timed with HIP events on the
+replaying stream: the products run back to back as a serving loop would
+issue them, without the Python binding's per-call host cost (about 10 us,
+which exceeds a batch-16 product).  Further replays give the median, p10
+and p90.  Eager per-call times are reported beside.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-stack] [--no-configs]
 """
 from __future__ import annotations
 
@@ -51,6 +56,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense torch.matmul comparator")
     ap.add_argument("--no-stack", action="store_true", help="skip the 32-layer stack batch sweep")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration rows")
     ap.add_argument("--profile-only", type=int, default=0, metavar="K",
                     help="run K products at each batch plus a 256 MiB calibration copy, print nothing else "
                          "(for rocprofv3 runs)")
@@ -140,23 +146,22 @@ def time_spmm(hinm, torch, rot, steps, warmup):
             "ms_p10": per[len(per) // 10], "ms_p90": per[(9 * len(per)) // 10], "wall_s": wall}
 
 
-def time_spmm_graph(hinm, torch, rot, steps, extra=4, out_rows=None):
-    """Time of exactly `steps` products launched from one HIP graph.
+REPLAYS = 7                    # timed graph replays behind each spread (median, p10, p90)
 
-    Product i uses rotation copy i % k.  The graph is captured on a side
-    stream and replayed WARM_REPLAYS times back to back untimed (the clock
-    settles only after tens of milliseconds of continuous work: a traced run
-    shows the batch-2048 product falling from 116 to 99 us over its first
-    eight passes); the timed region is one replay,
-    bracketed by device synchronisation, with HIP events on the replaying
-    stream.  A graph launches the products back to back with no host work in
-    between, so short products are not bound by the host's per-call cost.
-    `extra` further replays give the spread (per-step time of each replay).
+
+def graph_replays(torch, run, steps, replays=REPLAYS):
+    """Per-product times of `run` (which launches `steps` products) from a HIP graph.
+
+    The graph is captured once on a side stream and replayed WARM_REPLAYS
+    times back to back untimed (the clock settles only after tens of
+    milliseconds of continuous work: a traced run shows the batch-2048
+    product falling from 116 to 99 us over its first eight passes).  Then
+    `replays` timed replays, each bracketed by device synchronisation and
+    timed with HIP events on the replaying stream.  The first timed replay is
+    the step time; the others give the spread.  A graph launches the products
+    back to back with no host work in between, so short products are not
+    bound by the host's per-call cost.
     """
-    def run():
-        for i in range(steps):
-            pk, x, y = rot[i]
-            hinm.spmm(pk, x, out=y, workspace=rot.ws, out_rows=out_rows)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -170,64 +175,199 @@ def time_spmm_graph(hinm, torch, rot, steps, extra=4, out_rows=None):
         g.replay()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 + extra)]
-    t0 = time.perf_counter()
-    ev[0].record(stream)
-    g.replay()
-    ev[1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    for i in range(extra):
+    per = []
+    wall = None
+    for i in range(replays):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        a.record(stream)
         g.replay()
-        ev[2 + i].record(stream)
-    torch.cuda.synchronize()
-    total_ms = ev[0].elapsed_time(ev[1])
-    per = sorted([total_ms / steps] + [ev[1 + i].elapsed_time(ev[2 + i]) / steps for i in range(extra)])
-    return {"ms_total": total_ms, "ms_mean": total_ms / steps, "steps": steps, "wall_s": wall,
-            "replay_ms_per_step_min": per[0], "replay_ms_per_step_max": per[-1]}
+        b.record(stream)
+        torch.cuda.synchronize()
+        if i == 0:
+            wall = time.perf_counter() - t0
+        per.append(a.elapsed_time(b) / steps)
+    srt = sorted(per)
+    q = lambda f: srt[min(len(srt) - 1, int(round(f * (len(srt) - 1))))]
+    del g
+    return {"ms_step": per[0], "ms_median": q(0.5), "ms_p10": q(0.1), "ms_p90": q(0.9), "ms_min": srt[0],
+            "ms_max": srt[-1], "replays": replays, "steps": steps, "wall_s": wall}
 
 
-def time_dense(torch, w, x, steps, warmup):
-    """torch.matmul of the unpruned weight, timed like the products: one replay of a graph of `steps` calls."""
-    y = torch.empty(w.shape[0], x.shape[1], dtype=torch.bfloat16, device=x.device)
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        for _ in range(warmup):
-            torch.matmul(w, x, out=y)
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for _ in range(steps):
-            torch.matmul(w, x, out=y)
-    g.replay()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    g.replay()
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / steps
+def time_spmm_graph(hinm, torch, rot, steps, out_rows=None, replays=REPLAYS):
+    """Graph-timed products over the rotation copies (product i uses copy i % k)."""
+    def run():
+        for i in range(steps):
+            pk, x, y = rot[i]
+            hinm.spmm(pk, x, out=y, workspace=rot.ws, out_rows=out_rows)
+    return graph_replays(torch, run, steps, replays)
+
+
+def spread(r):
+    return {"ms_median": round(r["ms_median"], 5), "ms_p10": round(r["ms_p10"], 5), "ms_p90": round(r["ms_p90"], 5)}
+
+
+def time_dense(torch, w, x, steps, replays=REPLAYS):
+    """torch.matmul (hipBLASLt) of the unpruned weight at the same shape, timed like the products: the
+    weight rotates over copies of >= 1 GiB in all, so the last-level cache does not serve repeats."""
+    k = max(2, -(-ROTATE_BYTES // (w.numel() * 2 + x.numel() * 2 + w.shape[0] * x.shape[1] * 2)))
+    ws = [w] + [w.clone() for _ in range(k - 1)]
+    xs = [x] + [x.clone() for _ in range(k - 1)]
+    ys = [torch.empty(w.shape[0], x.shape[1], dtype=torch.bfloat16, device=x.device) for _ in range(k)]
+
+    def run():
+        for i in range(steps):
+            torch.matmul(ws[i % k], xs[i % k], out=ys[i % k])
+    r = graph_replays(torch, run, steps, replays)
+    r["rotation_copies"] = k
+    del ws, xs, ys
+    return r
+
+
+def fracs(alg, ms, batch):
+    """Throughputs of one product and their fractions of the MI355X peaks; the bound is HBM up to batch
+    256, MFMA from batch 1024, both near the ridge (512)."""
+    gbs = alg["bytes"] / (ms * 1e-3) / 1e9
+    tfl = alg["useful_flops"] / (ms * 1e-3) / 1e12
+    bound = "hbm" if batch <= 256 else ("mfma" if batch >= 1024 else "ridge")
+    return {"hbm_gbs": round(gbs, 1), "useful_tflops": round(tfl, 3), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "frac_mfma": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4), "bound": bound,
+            "frac": round(gbs / HBM_PEAK_GBS if bound == "hbm" else tfl / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
+def config_rows(hinm, torch, synth, dev, steps, with_dense):
+    """One row per workload and batch of the five configurations that a single product covers (the
+    stack is its own sweep): the product graph-timed over >= 1 GiB of rotated copies, its algorithmic
+    bytes and useful flops, the roofline fractions, and (for the two orientations of the 4096 x 11008
+    headline shape and q_proj) the dense torch.matmul beside it."""
+    rows = []
+    cases = [("tiny 128x256 (fp32 drawn, bf16 path), tile_rows 32, t_s 0.75, v_s 0.5", synth.tiny(), None, (8,)),
+             ("q_proj 4096x4096, t_s 0.5, v_s 0.25", synth.q_proj(batch=16), None, (16,)),
+             ("up_proj 11008x4096, t_s 0.75, v_s 0.55", synth.up_proj(batch=16), None, (16, 2048)),
+             ("down_proj 4096x11008, t_s 0.75, v_s 0.55", synth.down_proj(batch=16), None, (16, 2048))]
+    for t in (0.6, 0.7, 0.8):
+        w = synth.down_proj_sweep(t, batch=1)
+        # v_s from the boundary search on the device (equal to the oracle's search, tested)
+        v, _ = hinm.boundary_search(w.importance.to(dev), w.perm.to(dev), 64, t)
+        cases.append((f"down_proj sweep 4096x11008 (5% outlier columns x10, importance W^2), t_s {t}, v_s {v:.4f} "
+                      f"(device boundary search)", w, v, (1, 64, 512)))
+    dense_for = {"q_proj", "up_proj", "down_proj"}
+    for name, w, v_s, batches in cases:
+        v = w.v_s if v_s is None else v_s
+        pk = hinm.pack(w.w_bf16.to(dev), w.importance.to(dev), w.tile_rows, w.t_s, v, w.perm.to(dev))
+        p = pk.plan
+        wd = w.w_bf16.to(dev) if with_dense and name.split()[0] in dense_for else None
+        for B in batches:
+            x = torch.randn(p.cin, B, device=dev, generator=torch.Generator(device=dev).manual_seed(B)).to(
+                torch.bfloat16)
+            rot = Rotation(hinm, torch, pk, x, B)
+            nst = max(steps, 200) if B <= 64 else steps
+            r = time_spmm_graph(hinm, torch, rot, nst)
+            alg = algorithmic(p, B)
+            row = {"workload": name, "batch": B, "ms": round(r["ms_step"], 5), **spread(r),
+                   "rotation_copies": rot.k, "algorithmic_bytes": alg["bytes"], "useful_flops": alg["useful_flops"],
+                   "regions_per_tile": {"dense": p.n_dense, "two_four": p.n_24, "pruned": p.n_pruned},
+                   **fracs(alg, r["ms_step"], B)}
+            if wd is not None:
+                d = time_dense(torch, wd, x, nst)
+                row["dense_ms"] = round(d["ms_step"], 5)
+                row["dense_rotation_copies"] = d["rotation_copies"]
+                row["speedup_vs_dense"] = round(d["ms_step"] / r["ms_step"], 3)
+            log(f"{name.split(',')[0]} batch {B}: {r['ms_step'] * 1e3:.2f} us, frac {row['frac']}")
+            rows.append(row)
+            del rot, x
+        del pk, wd
+        torch.cuda.empty_cache()
+    return rows
+
+
+def empirical_peaks(torch, dev):
+    """What this GPU reaches on plain work, beside the published peaks: a 1 GiB read (sum of fp32), a 1 GiB
+    copy (read + write) and torch.matmul bf16 at 8192^3.  Timed eagerly (each call lasts 100 us or more, so
+    the launch cost is noise), with HIP events around ten calls after three warm-up calls; the median of
+    five such groups."""
+    def eager(fn, n=10, groups=5):
+        for _ in range(3):
+            fn()
+        t = []
+        for _ in range(groups):
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(n):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            t.append(a.elapsed_time(b) / n)
+        return sorted(t)[len(t) // 2]
+    n = (1 << 30) // 4
+    src = torch.rand(n, device=dev)
+    dst = torch.empty_like(src)
+    t_read = eager(lambda: torch.sum(src))
+    t_copy = eager(lambda: dst.copy_(src))
+    del src, dst
+    a = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    c = torch.empty(8192, 8192, dtype=torch.bfloat16, device=dev)
+    t_mm = eager(lambda: torch.matmul(a, b, out=c))
+    del a, b, c
+    torch.cuda.empty_cache()
+    gib = float(1 << 30)
+    return {"read_1gib_gbs": round(gib / (t_read * 1e-3) / 1e9, 1),
+            "copy_1gib_gbs": round(2 * gib / (t_copy * 1e-3) / 1e9, 1),
+            "matmul_bf16_8192_tflops": round(2 * 8192 ** 3 / (t_mm * 1e-3) / 1e12, 1),
+            "what": "torch.sum over 1 GiB of fp32 (read), copy_ of 1 GiB (read + write, counted twice), "
+                    "torch.matmul bf16 8192^3 (hipBLASLt); eager, median of five groups of ten calls"}
+
+
+def gpu_clocks(busy=None):
+    """GPU clocks as amd-smi (else rocm-smi) reports them, read in a child process; with `busy`, that
+    function keeps the GPU working until the report is in, so the clocks are those under load.  None where
+    neither tool answers."""
+    import subprocess
+    for cmd in (["amd-smi", "metric", "-c", "--json"], ["rocm-smi", "--showclocks", "--json"]):
+        try:
+            proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+        except OSError:
+            continue
+        t0 = time.perf_counter()
+        while busy is not None and proc.poll() is None and time.perf_counter() - t0 < 20:
+            busy()
+        try:
+            out, _ = proc.communicate(timeout=20)
+        except subprocess.TimeoutExpired:
+            proc.kill()
+            continue
+        if proc.returncode == 0 and out.strip():
+            try:
+                rep = json.loads(out)
+            except ValueError:
+                rep = out.strip()[:2000]
+            return {"tool": cmd[0], "under_load": busy is not None, "report": rep}
+    return None
 
 
 STACK_LAYERS = 32
-STACK_BATCHES = (1, 16, 64, 256, 1024, 2048, 4096)
+STACK_BATCHES = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096)
 
 
 def stack_sweep(hinm, torch, synth, dev, with_dense):
     """The 7B-shaped stack: 32 layers x {q, k, v, o 4096x4096; gate, up 11008x4096;
     down 4096x11008}, HiNM packed once (tile_rows 64, t_s 0.75, v_s 0.55), and
-    the sum of all linear-layer products of one forward pass at each batch.
+    the sum of all linear-layer products of one forward pass at each of 13
+    batches.
 
     Weights are drawn on the device (iid N(0, 0.02), importance |W|, random
     per-tile permutations): the product's time depends on the shapes and the
-    region counts only.  The 224 products of a forward are captured in one
-    HIP graph (X and Y buffers shared by the projections of the same shape),
-    replayed untimed, then timed over one replay with HIP events.  The packed
-    stack (3.4 GB) is well past the 256 MB last-level cache, so every weight
-    comes from HBM.  The dense comparator runs torch.matmul on the unpruned
-    bf16 weights (13 GB) the same way.
+    region counts only.  Every layer has its own activations and outputs
+    (three inputs of 4096 rows - attention, o, MLP - and one of 11008), so no
+    product reads an X that an earlier one left in a cache.  A forward pass
+    is timed two ways, each from one HIP graph: grouped (q, k, v in one
+    hinm_spmm_group launch, gate and up in another: they read the same X), and
+    one launch per product.  The packed stack (3.8 GB) is well past the 256 MB
+    last-level cache, so every weight comes from HBM.  The dense comparator
+    runs torch.matmul on the unpruned bf16 weights (13 GB) the same way.
     """
     g = torch.Generator(device=dev)
     g.manual_seed(7)
@@ -245,60 +385,66 @@ def stack_sweep(hinm, torch, synth, dev, with_dense):
             else:
                 del w
     pack_s = time.perf_counter() - t0
-
-    def run_graph(fn, replays=3):
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            fn()
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            fn()
-        for _ in range(replays):
-            graph.replay()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        graph.replay()
-        b.record()
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b)
-        del graph
-        return ms
+    layers = [packs[7 * l:7 * l + 7] for l in range(STACK_LAYERS)]
+    groups = [(hinm.Group(ly[0:3]), hinm.Group(ly[4:6])) for ly in layers]
+    bytes_w = sum(pk.nbytes() for pk in packs)
 
     rows = []
     for B in STACK_BATCHES:
-        xs = {c: torch.randn(c, B, device=dev, generator=g).to(torch.bfloat16) for c in (4096, 11008)}
-        ys = {c: torch.empty(c, B, dtype=torch.bfloat16, device=dev) for c in (4096, 11008)}
-        ws_bytes = max(hinm.spmm_workspace_bytes(pk.plan, B) for pk in packs[:7])
-        ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(B)
+        xs = [[torch.randn(c, B, device=dev, generator=gen).to(torch.bfloat16) for c in (4096, 4096, 4096, 11008)]
+              for _ in range(STACK_LAYERS)]
+        ys = [[torch.empty(pk.plan.cout, B, dtype=torch.bfloat16, device=dev) for pk in ly] for ly in layers]
+        need = max([hinm.spmm_workspace_bytes(pk.plan, B) for pk in packs[:7]] +
+                   [grp.workspace_bytes(B) for grp in groups[0]])
+        ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
         useful = sum(2 * pk.plan.cout * (pk.plan.cin - pk.plan.z) * B for pk in packs)
+        nbytes = bytes_w + sum(2 * B * (pk.plan.cin + pk.plan.cout) for pk in packs)
+        xin = (0, 0, 0, 1, 2, 2, 3)                # which of a layer's four inputs each product reads
 
-        def fwd():
-            for pk in packs:
-                hinm.spmm(pk, xs[pk.plan.cin], out=ys[pk.plan.cout], workspace=ws)
-        ms = run_graph(fwd)
-        log(f"stack batch {B}: {ms:.3f} ms per forward")
-        row = {"batch": B, "ms_per_forward": round(ms, 4), "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2)}
+        def fwd_grouped():
+            for l, ly in enumerate(layers):
+                hinm.spmm_group(groups[l][0], xs[l][0], outs=ys[l][0:3], workspace=ws)
+                hinm.spmm(ly[3], xs[l][1], out=ys[l][3], workspace=ws)
+                hinm.spmm_group(groups[l][1], xs[l][2], outs=ys[l][4:6], workspace=ws)
+                hinm.spmm(ly[6], xs[l][3], out=ys[l][6], workspace=ws)
+
+        def fwd_single():
+            for l, ly in enumerate(layers):
+                for i, pk in enumerate(ly):
+                    hinm.spmm(pk, xs[l][xin[i]], out=ys[l][i], workspace=ws)
+        rg = graph_replays(torch, fwd_grouped, 1, 5)
+        rs = graph_replays(torch, fwd_single, 1, 3)
+        ms = rg["ms_step"]
+        gbs, tfl = nbytes / (ms * 1e-3) / 1e9, useful / (ms * 1e-3) / 1e12
+        bound = "hbm" if B <= 256 else ("mfma" if B >= 1024 else "ridge")
+        row = {"batch": B, "ms_per_forward": round(ms, 4), **spread(rg),
+               "ms_per_forward_one_launch_per_product": round(rs["ms_step"], 4),
+               "useful_tflops": round(tfl, 2), "hbm_gbs": round(gbs, 1), "algorithmic_bytes": nbytes,
+               "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "frac_mfma": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
+               "bound": bound,
+               "frac": round(gbs / HBM_PEAK_GBS if bound == "hbm" else tfl / MFMA_BF16_PEAK_TFLOPS, 4)}
         if with_dense:
             def fwd_dense():
-                for i, wt in enumerate(dense):
-                    _n, cout, cin = synth.STACK_PROJS[i % 7]
-                    torch.matmul(wt, xs[cin], out=ys[cout])
-            dms = run_graph(fwd_dense)
-            row["dense_ms_per_forward"] = round(dms, 4)
-            row["speedup_vs_dense"] = round(dms / ms, 3)
+                for l in range(STACK_LAYERS):
+                    for i in range(7):
+                        torch.matmul(dense[7 * l + i], xs[l][xin[i]], out=ys[l][i])
+            rd = graph_replays(torch, fwd_dense, 1, 3)
+            row["dense_ms_per_forward"] = round(rd["ms_step"], 4)
+            row["speedup_vs_dense"] = round(rd["ms_step"] / ms, 3)
+        log(f"stack batch {B}: {ms:.3f} ms per forward grouped, {rs['ms_step']:.3f} one launch per product")
         rows.append(row)
         del xs, ys, ws
-    packed_gb = sum(pk.nbytes() for pk in packs) / 1e9
-    del packs, dense
+        torch.cuda.empty_cache()
+    del packs, dense, layers, groups
     torch.cuda.empty_cache()
     return {"what": "32-layer 7B-shaped stack (q, k, v, o 4096x4096; gate, up 11008x4096; down 4096x11008), "
                     "tile_rows 64, t_s 0.75, v_s 0.55, packed once; time of all 224 linear-layer products of one "
-                    "forward pass, one HIP graph replay after three untimed ones",
-            "packed_gb": round(packed_gb, 3), "pack_all_s": round(pack_s, 2), "per_batch": rows}
+                    "forward pass (q/k/v and gate/up grouped into one launch each: 128 launches; beside it one "
+                    "launch per product: 224), every layer with its own activations; one HIP graph replay "
+                    "after ten untimed ones; algorithmic bytes = packed weights + X and Y of every product",
+            "packed_gb": round(bytes_w / 1e9, 3), "pack_all_s": round(pack_s, 2), "per_batch": rows}
 
 
 def cpu_baseline(w, batch):
@@ -372,6 +518,7 @@ def main():
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the product shards by output tiles with no exchange, see the design notes).", file=sys.stderr)
         sys.exit(2)
+    import numpy as np
     import torch
 
     import structured_sparse_gemm_amd as hinm
@@ -395,40 +542,50 @@ def main():
     xd = wd_.x_bf16.to(dev)
 
     if args.profile_only:
-        y = torch.empty(p.cout, B, dtype=torch.bfloat16, device=dev)
-        yd = torch.empty(p.cout, Bd, dtype=torch.bfloat16, device=dev)
-        for _ in range(args.profile_only):
-            hinm.spmm(pk, x, out=y)
-            hinm.spmm(pk, xd, out=yd)
+        # the products as the timed runs issue them: each on the next rotation copy
+        for bb, xx in ((B, x), (Bd, xd)):
+            rot = Rotation(hinm, torch, pk, xx, bb)
+            for i in range(args.profile_only):
+                pki, xi, yi = rot[i]
+                hinm.spmm(pki, xi, out=yi, workspace=rot.ws)
+            torch.cuda.synchronize()
+            del rot
         src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)                      # calibration: reads and writes CALIB_BYTES once
         torch.cuda.synchronize()
         return
 
+    clocks_idle = gpu_clocks()
     log(f"packed: {[round(v, 2) for v in pack_ms]} ms; timing batch {B}")
     rot = Rotation(hinm, torch, pk, x, B)
     r_eager = time_spmm(hinm, torch, rot, args.steps, args.warmup)
     r = time_spmm_graph(hinm, torch, rot, args.steps)
     alg = algorithmic(p, B)
-    ms = r["ms_mean"]
+    ms = r["ms_step"]
     value = alg["useful_flops"] / (ms * 1e-3) / 1e12
 
+    def busy():                              # about 2 ms of the headline products
+        for i in range(20):
+            pki, xi, yi = rot[i]
+            hinm.spmm(pki, xi, out=yi, workspace=rot.ws)
+        torch.cuda.synchronize()
+    clocks_load = gpu_clocks(busy)
     log(f"batch {B}: {ms * 1e3:.2f} us per product; timing batch {Bd}")
     rotd = Rotation(hinm, torch, pk, xd, Bd)
-    rd_eager = time_spmm(hinm, torch, rotd, max(args.steps, 200), args.warmup)
     steps_d = max(args.steps, 200)
+    rd_eager = time_spmm(hinm, torch, rotd, steps_d, args.warmup)
     rd = time_spmm_graph(hinm, torch, rotd, steps_d)
     algd = algorithmic(p, Bd)
-    gbs_d = algd["bytes"] / (rd["ms_mean"] * 1e-3) / 1e9
+    gbs_d = algd["bytes"] / (rd["ms_step"] * 1e-3) / 1e9
 
-    log(f"batch {Bd}: {rd['ms_mean'] * 1e3:.2f} us per product; side rows")
+    log(f"batch {Bd}: {rd['ms_step'] * 1e3:.2f} us per product; side rows")
     # NEXT row: output-channel permutation fused into the write-out, and the
     # one-time cross-layer index translation
-    out_rows = torch.from_numpy(__import__("numpy").random.default_rng(0).permutation(p.cout).astype("int32")).to(dev)
-    r_rows = time_spmm_graph(hinm, torch, rot, args.steps, extra=0, out_rows=out_rows)
-    rd_rows = time_spmm_graph(hinm, torch, rotd, steps_d, extra=0, out_rows=out_rows)
-    sigma = torch.from_numpy(__import__("numpy").random.default_rng(1).permutation(p.cin).astype("int32")).to(dev)
+    out_rows = torch.from_numpy(np.random.default_rng(0).permutation(p.cout).astype("int32")).to(dev)
+    r_rows = time_spmm_graph(hinm, torch, rot, args.steps, out_rows=out_rows, replays=3)
+    rd_rows = time_spmm_graph(hinm, torch, rotd, steps_d, out_rows=out_rows, replays=3)
+    sigma = torch.from_numpy(np.random.default_rng(1).permutation(p.cin).astype("int32")).to(dev)
     pk_t = hinm.HinmPacked(pk.plan, pk.val_dense, pk.idx_dense.clone(), pk.val_24, pk.meta_24, pk.idx_24.clone())
     tr_ms = []
     for _ in range(3):
@@ -438,8 +595,8 @@ def main():
         tr_ms.append((time.perf_counter() - t0) * 1e3)
     next_rows = {"what": "hinm_spmm_rows (Y row r written to out_rows[r]) next to hinm_spmm, same timing method; "
                          "hinm_translate_indices wall time (synchronous, includes the permutation check)",
-                 "spmm_rows_batch_2048_ms": round(r_rows["ms_mean"], 5), "spmm_batch_2048_ms": round(ms, 5),
-                 "spmm_rows_batch_16_ms": round(rd_rows["ms_mean"], 5), "spmm_batch_16_ms": round(rd["ms_mean"], 5),
+                 "spmm_rows_batch_2048_ms": round(r_rows["ms_step"], 5), "spmm_batch_2048_ms": round(ms, 5),
+                 "spmm_rows_batch_16_ms": round(rd_rows["ms_step"], 5), "spmm_batch_16_ms": round(rd["ms_step"], 5),
                  "translate_indices_ms": [round(v, 3) for v in tr_ms]}
 
     # NEXT row: the boundary search for v_s on the device (down_proj sweep workload, t_s 0.7)
@@ -454,48 +611,27 @@ def main():
         bs_ms.append((time.perf_counter() - t0) * 1e3)
     next_bs = {"what": "hinm_boundary_search wall time, down_proj 4096x11008 with 5% outlier columns, importance W*W, "
                        "t_s 0.7 (synchronous: checks, scores, ranking, then one device pass and one host read per grid "
-                       "point)", "ms": [round(x, 2) for x in bs_ms], "v_s": v_b, "grid_points": len(tr_b)}
+                       "point)", "ms": [round(v, 2) for v in bs_ms], "v_s": v_b, "grid_points": len(tr_b)}
     if not args.no_cpu:
         next_bs.update(cpu_baseline_boundary(wb_))
 
     # NEXT row: per-tile v_s (per-tile boundary search on the same weight and importance, then the
-    # per-tile layout), products timed like the uniform ones but without buffer rotation
+    # per-tile layout), graph-timed on one resident copy beside the uniform product timed the same way
     t0 = time.perf_counter()
     v_tiles, _ = hinm.boundary_search_tiles(igpu, pgpu, w.tile_rows, w.t_s)
     search_tiles_ms = (time.perf_counter() - t0) * 1e3
     t0 = time.perf_counter()
     pk_tiles = hinm.pack_tiles(wgpu, igpu, w.tile_rows, w.t_s, v_tiles, pgpu)
     pack_tiles_ms = (time.perf_counter() - t0) * 1e3
-
-    def graph_ms(fn, steps):
-        s_ = torch.cuda.Stream()
-        s_.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s_):
-            fn()
-        torch.cuda.current_stream().wait_stream(s_)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(steps):
-                fn()
-        for _ in range(WARM_REPLAYS):
-            g.replay()
-        torch.cuda.synchronize()
-        times = []
-        for _ in range(5):            # median of five replays: single replays vary by several percent
-            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a_.record()
-            g.replay()
-            b_.record()
-            torch.cuda.synchronize()
-            times.append(a_.elapsed_time(b_) / steps)
-        return sorted(times)[2]
-
     y_t = torch.empty(p.cout, B, dtype=torch.bfloat16, device=dev)
     yd_t = torch.empty(p.cout, Bd, dtype=torch.bfloat16, device=dev)
-    ws_t = torch.zeros(max(1, hinm.spmm_tiles_workspace_bytes(pk_tiles.plan, Bd)), dtype=torch.uint8, device=dev)
-    costs = [(int(r[1]) + 31) // 32 + 2 * ((int(r[3]) + 63) // 64) for r in pk_tiles.plan.tiles]
-    kept_t = sum(int(r[1]) + int(r[3]) // 2 for r in pk_tiles.plan.tiles)       # kept entries per row, summed over tiles
+    ws_t = torch.zeros(max(1, hinm.spmm_tiles_workspace_bytes(pk_tiles.plan, Bd),
+                           hinm.spmm_workspace_bytes(p, Bd)), dtype=torch.uint8, device=dev)
+
+    def gms(fn, n):
+        return graph_replays(torch, lambda: [fn() for _ in range(n)], n, 5)["ms_median"]
+    costs = [(int(rr[1]) + 31) // 32 + 2 * ((int(rr[3]) + 63) // 64) for rr in pk_tiles.plan.tiles]
+    kept_t = sum(int(rr[1]) + int(rr[3]) // 2 for rr in pk_tiles.plan.tiles)
     useful_t = 2 * p.tile_rows * kept_t * B
     next_tiles = {
         "what": "per-tile v_s from hinm_boundary_search_tiles on this weight (importance |W|, t_s 0.75), packed by "
@@ -506,14 +642,12 @@ def main():
         "dense_blocks": pk_tiles.plan.dense_blocks, "blocks_24": pk_tiles.plan.blocks_24,
         "uniform_dense_blocks": p.n_tiles * p.n_dense_pad // 32, "uniform_blocks_24": p.n_tiles * p.n_24_pad // 64,
         "search_tiles_ms": round(search_tiles_ms, 2), "pack_tiles_ms": round(pack_tiles_ms, 2),
-        "spmm_tiles_batch_2048_ms": round(graph_ms(lambda: hinm.spmm(pk_tiles, x, out=y_t), 20), 5),
-        "spmm_uniform_resident_batch_2048_ms": round(graph_ms(lambda: hinm.spmm(pk, x, out=y_t), 20), 5),
-        "spmm_tiles_batch_16_ms": round(graph_ms(lambda: hinm.spmm(pk_tiles, xd, out=yd_t, workspace=ws_t), 100), 5),
-        "spmm_uniform_resident_batch_16_ms": round(graph_ms(lambda: hinm.spmm(pk, xd, out=yd_t, workspace=ws_t), 100),
-                                                   5),
+        "spmm_tiles_batch_2048_ms": round(gms(lambda: hinm.spmm(pk_tiles, x, out=y_t), 20), 5),
+        "spmm_uniform_resident_batch_2048_ms": round(gms(lambda: hinm.spmm(pk, x, out=y_t), 20), 5),
+        "spmm_tiles_batch_16_ms": round(gms(lambda: hinm.spmm(pk_tiles, xd, out=yd_t, workspace=ws_t), 100), 5),
+        "spmm_uniform_resident_batch_16_ms": round(gms(lambda: hinm.spmm(pk, xd, out=yd_t, workspace=ws_t), 100), 5),
         "tile_cost_min": int(min(costs)), "tile_cost_mean": round(sum(costs) / len(costs), 2),
-        "tile_cost_max": int(max(costs)),
-        "useful_tflops_batch_2048": None}
+        "tile_cost_max": int(max(costs))}
     next_tiles["useful_tflops_batch_2048"] = round(useful_t / (next_tiles["spmm_tiles_batch_2048_ms"] * 1e-3) / 1e12, 2)
 
     # NEXT row: the in-tile input-channel gyro permutation on this weight (importance |W|, the bench's
@@ -538,20 +672,28 @@ def main():
                  "total_importance": round(tot24, 3)}
     if not args.no_cpu:
         next_gyro.update(cpu_baseline_gyro(w, g_sample, g_init, g_cs, g_it))
+    del rot, rotd
+    torch.cuda.empty_cache()
 
     dense = None
     if not args.no_dense:
-        dense_ms = time_dense(torch, wgpu, x, max(10, args.steps // 2), 3)
-        dense_ms_d = time_dense(torch, wgpu, xd, 200, 10)
-        dense = {"what": "torch.matmul bf16 of the unpruned 4096x11008 weight (hipBLASLt), same shapes, "
-                         "timed from one graph replay (no rotation: the dense weight stays in the last-level cache)",
-                 "batch_2048_ms": round(dense_ms, 4), "batch_16_ms": round(dense_ms_d, 4),
-                 "speedup_batch_2048": round(dense_ms / ms, 3), "speedup_batch_16": round(dense_ms_d / rd["ms_mean"], 3)}
+        d2 = time_dense(torch, wgpu, x, args.steps)
+        d16 = time_dense(torch, wgpu, xd, steps_d)
+        dense = {"what": "torch.matmul bf16 of the unpruned 4096x11008 weight (hipBLASLt), same shapes, graph-timed "
+                         "over rotated copies (>= 1 GiB) like the products",
+                 "batch_2048_ms": round(d2["ms_step"], 4), "batch_16_ms": round(d16["ms_step"], 4),
+                 "batch_2048_spread": spread(d2), "batch_16_spread": spread(d16),
+                 "rotation_copies": [d2["rotation_copies"], d16["rotation_copies"]],
+                 "speedup_batch_2048": round(d2["ms_step"] / ms, 3),
+                 "speedup_batch_16": round(d16["ms_step"] / rd["ms_step"], 3)}
 
+    log("configuration rows")
+    configs = None if args.no_configs else config_rows(hinm, torch, synth, dev, args.steps, not args.no_dense)
+    log("empirical peaks")
+    peaks = empirical_peaks(torch, dev)
     log("stack sweep")
     stack = None if args.no_stack else stack_sweep(hinm, torch, synth, dev, not args.no_dense)
     log("CPU oracle baseline")
-
     cpu = None if args.no_cpu else cpu_baseline(w, B)
 
     line = {
@@ -566,30 +708,29 @@ def main():
                      "frac": round(value / MFMA_BF16_PEAK_TFLOPS, 5), "traffic": measured_traffic(B),
                      "kernel": "prefill_kernel<256, false> (one launch per step)",
                      "kernel_source_hash": kernel_source_hash(),
+                     "frac_of_measured_matmul_peak": round(value / peaks["matmul_bf16_8192_tflops"], 4),
                      "per_launch": {"useful_flops": alg["useful_flops"], "algorithmic_bytes": alg["bytes"],
-                                    "ms_mean": round(ms, 5),
-                                    "replay_ms_min": round(r["replay_ms_per_step_min"], 5),
-                                    "replay_ms_max": round(r["replay_ms_per_step_max"], 5)},
-                     "timing": f"one HIP graph replay of {args.steps} products over {rot.k} rotated copies, after "
-                               f"{WARM_REPLAYS} untimed replays; "
-                               f"eager launches from Python: {r_eager['ms_mean'] * 1e3:.1f} us per step",
-                     "eager_ms_mean": round(r_eager["ms_mean"], 5),
-                     "rotation_copies": rot.k},
-        "decode": {"batch": Bd, "ms_mean": round(rd["ms_mean"], 5),
-                   "replay_ms_min": round(rd["replay_ms_per_step_min"], 5),
-                   "replay_ms_max": round(rd["replay_ms_per_step_max"], 5),
-                   "timing": f"one HIP graph replay of {steps_d} products over {rotd.k} rotated copies, after "
-                             f"{WARM_REPLAYS} untimed replays; "
-                             f"eager launches from Python: {rd_eager['ms_mean'] * 1e3:.1f} us per call",
+                                    "ms": round(ms, 5), **spread(r)},
+                     "timing": f"one HIP graph replay of {args.steps} products over {rot_k(p, B)} rotated copies, "
+                               f"after {WARM_REPLAYS} untimed replays; spread over {REPLAYS} replays; eager launches "
+                               f"from Python: {r_eager['ms_mean'] * 1e3:.1f} us per step",
+                     "eager_ms_mean": round(r_eager["ms_mean"], 5)},
+        "decode": {"batch": Bd, "ms": round(rd["ms_step"], 5), **spread(rd),
+                   "timing": f"one HIP graph replay of {steps_d} products over {rot_k(p, Bd)} rotated copies, after "
+                             f"{WARM_REPLAYS} untimed replays; eager launches from Python: "
+                             f"{rd_eager['ms_mean'] * 1e3:.1f} us per call",
                    "eager_ms_mean": round(rd_eager["ms_mean"], 5),
                    "algorithmic_bytes": algd["bytes"], "hbm_gbs": round(gbs_d, 1),
                    "roofline": {"bound": "hbm", "achieved": round(gbs_d, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": round(gbs_d / HBM_PEAK_GBS, 4), "traffic": measured_traffic(Bd),
+                                "frac_of_measured_read_peak": round(gbs_d / peaks["read_1gib_gbs"], 4),
                                 "kernel": "decode5_kernel<16,24,true,2> (one launch per call)"},
-                   "useful_tflops": round(algd["useful_flops"] / (rd["ms_mean"] * 1e-3) / 1e12, 3),
-                   "rotation_copies": rotd.k},
+                   "useful_tflops": round(algd["useful_flops"] / (rd["ms_step"] * 1e-3) / 1e12, 3)},
         "batch_2048_hbm_gbs": round(alg["bytes"] / (ms * 1e-3) / 1e9, 1),
         "pack_ms": [round(v, 2) for v in pack_ms],
+        "configs": configs,
+        "empirical_peaks": peaks,
+        "gpu_clocks": {"idle": clocks_idle, "under_headline_load": clocks_load},
         "next_output_permutation": next_rows,
         "next_boundary_search": next_bs,
         "next_per_tile_v_s": next_tiles,
@@ -599,6 +740,11 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
+
+
+def rot_k(p, batch):
+    per = p.packed_bytes + p.cin * batch * 2 + p.cout * batch * 2
+    return max(2, -(-ROTATE_BYTES // per))
 
 
 if __name__ == "__main__":
