@@ -672,7 +672,30 @@ def main():
                  "total_importance": round(tot24, 3)}
     if not args.no_cpu:
         next_gyro.update(cpu_baseline_gyro(w, g_sample, g_init, g_cs, g_it))
-    del rot, rotd
+    # NEXT row: block-diagonal input permutations (blocks of 64 channels): the pack flags the weight and
+    # the product pairs token blocks per tile; beside it the random-perm product above, and the same
+    # block-diagonal weight with the plain schedule (one token block per group, every tile's K loop from
+    # its first block)
+    rngb = np.random.default_rng(5)
+    permb = torch.from_numpy(np.stack([np.concatenate([64 * b + rngb.permutation(64) for b in range(p.cin // 64)])
+                                       for _ in range(p.n_tiles)]).astype(np.int32)).to(dev)
+    pkb = hinm.pack(wgpu, igpu, w.tile_rows, w.t_s, w.v_s, permb)
+    rotb, rotbd = Rotation(hinm, torch, pkb, x, B), Rotation(hinm, torch, pkb, xd, Bd)
+    rb_ = time_spmm_graph(hinm, torch, rotb, args.steps, replays=3)
+    rbd = time_spmm_graph(hinm, torch, rotbd, steps_d, replays=3)
+    with hinm.options(prefill_tb_group=1, prefill_stagger=1):
+        rb_plain = time_spmm_graph(hinm, torch, rotb, args.steps, replays=3)
+    next_block = {"what": "down_proj 4096x11008 packed with a block-diagonal input permutation (blocks of 64 "
+                          "channels; the pack sets HINM_PACKED_WINDOWED and the batch > 64 schedule pairs token "
+                          "blocks per tile, K loops staggered per tile), graph-timed over rotated copies like the "
+                          "headline; beside it the random-perm headline and the block-diagonal weight on the plain "
+                          "schedule (one token block per group, every tile from its first K-block)",
+                  "flags": int(pkb.flags), "batch_2048_ms": round(rb_["ms_step"], 5),
+                  "batch_16_ms": round(rbd["ms_step"], 5), "random_perm_batch_2048_ms": round(ms, 5),
+                  "random_perm_batch_16_ms": round(rd["ms_step"], 5),
+                  "plain_schedule_batch_2048_ms": round(rb_plain["ms_step"], 5),
+                  "useful_tflops_batch_2048": round(alg["useful_flops"] / (rb_["ms_step"] * 1e-3) / 1e12, 2)}
+    del rot, rotd, rotb, rotbd, pkb
     torch.cuda.empty_cache()
 
     dense = None
@@ -732,6 +755,7 @@ def main():
         "empirical_peaks": peaks,
         "gpu_clocks": {"idle": clocks_idle, "under_headline_load": clocks_load},
         "next_output_permutation": next_rows,
+        "next_block_diagonal_perm": next_block,
         "next_boundary_search": next_bs,
         "next_per_tile_v_s": next_tiles,
         "next_gyro_permutation": next_gyro,

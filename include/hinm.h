@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define HINM_ABI_VERSION 1
+#define HINM_ABI_VERSION 2
 
 /* Version of the packed-buffer layout described at hinm_packed_t and
  * hinm_tpacked_t.  A stored packed weight carries it; a different value
@@ -108,7 +108,20 @@ typedef struct {
   void* val_24;
   uint64_t* meta_24;
   int32_t* idx_24;
+  uint32_t flags;     /* HINM_PACKED_* bits describing the index lists (set by hinm_pack; 0 = none known) */
+  uint32_t reserved;  /* 0 */
 } hinm_packed_t;
+
+/* flags bit: every perm row kept each column inside its aligned block of 64
+ * positions (a block-diagonal permutation with blocks of 64, PermLLM
+ * summary, block-wise permutation; NULL perm included), so every tile's
+ * index lists walk X in windows of 64 rows, in the same order.  The product
+ * then orders its batch > 64 work items in pairs of token blocks per tile
+ * (the X rows that tiles read at one time stay near each other in the L2
+ * cache) - the same bits of Y.  hinm_translate_indices clears it unless its
+ * map is block-diagonal too.  A caller that builds hinm_packed_t itself may
+ * leave flags 0. */
+#define HINM_PACKED_WINDOWED 1u
 
 /* Per-tile region counts (FlexHiNM-GP notes, "整体框架": the ratio of the
  * three regions is decided inside each output-channel tile).  t_s is shared,
@@ -181,6 +194,23 @@ int hinm_abi_version(void);
  *   HINM_OPT_PREFILL_PER_XCD  env HINM_PREFILL_PER_XCD: persistent
  *                             workgroups per XCD of the batch > 64 kernel
  *                             (default 0: 64; 1 .. 1024)
+ *   HINM_OPT_PREFILL_TB_GROUP env HINM_PREFILL_TB_GROUP: the batch > 64
+ *                             kernel orders its (token block, row block)
+ *                             items in groups of this many token blocks,
+ *                             row-block major inside a group, so an XCD
+ *                             takes fewer tiles over more token blocks
+ *                             (default 0: 2 for a weight whose flags hold
+ *                             HINM_PACKED_WINDOWED, else 1, token-block
+ *                             major; 1 .. 64; same bits of Y)
+ *   HINM_OPT_PREFILL_STAGGER  env HINM_PREFILL_STAGGER: 0 (default): the
+ *                             batch > 64 kernel starts tile t's dense and
+ *                             2:4 K loops at block t * n / n_tiles of its n
+ *                             and wraps around, so tiles whose index lists
+ *                             walk X in the same order (block-diagonal or
+ *                             identity perms) do not read the same rows at
+ *                             the same time; 1: every tile from its first
+ *                             block.  Either order is deterministic; they
+ *                             add the products in different orders.
  * A change applies to products launched afterwards; a workspace sized under
  * other settings may then be too small (HINM_EWORKSPACE). */
 typedef enum {
@@ -190,7 +220,9 @@ typedef enum {
   HINM_OPT_PREFILL_SPLITS = 4,
   HINM_OPT_PREFILL_PATH = 5,
   HINM_OPT_PREFILL_PER_XCD = 6,
-  HINM_OPT_COUNT = 7
+  HINM_OPT_PREFILL_TB_GROUP = 7,
+  HINM_OPT_PREFILL_STAGGER = 8,
+  HINM_OPT_COUNT = 9
 } hinm_option;
 
 /* Sets an option (host only).  Errors: HINM_EINVAL (unknown option or value

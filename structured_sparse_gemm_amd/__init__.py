@@ -21,7 +21,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhinm.so")
 
-HINM_ABI_VERSION = 1
+HINM_ABI_VERSION = 2
+HINM_PACKED_WINDOWED = 1     # flags bit: block-diagonal perms (blocks of 64), see include/hinm.h
 HINM_FORMAT_VERSION = 1       # packed-buffer layout version (include/hinm.h)
 HINM_NOALLOC_SCRATCH_BYTES = 65536 + (32 << 20)   # hinm_spmm_noalloc's device array (include/hinm.h)
 STATUS = {0: "HINM_OK", 1: "HINM_EINVAL", 2: "HINM_ESHAPE", 3: "HINM_EPERM", 4: "HINM_EIMPORTANCE",
@@ -38,7 +39,7 @@ EXPORTS = ("hinm_abi_version", "hinm_plan", "hinm_pack_workspace_bytes", "hinm_p
 
 # Launch-shape options (hinm_set_option): name -> HINM_OPT_* key.
 OPTIONS = {"decode_path": 1, "decode_wgs": 2, "prefill_nt": 3, "prefill_splits": 4, "prefill_path": 5,
-           "prefill_per_xcd": 6}
+           "prefill_per_xcd": 6, "prefill_tb_group": 7, "prefill_stagger": 8}
 
 
 class HinmError(RuntimeError):
@@ -62,7 +63,8 @@ class PlanT(ctypes.Structure):
 
 class PackedT(ctypes.Structure):
     _fields_ = [("plan", PlanT), ("val_dense", ctypes.c_void_p), ("idx_dense", ctypes.c_void_p),
-                ("val_24", ctypes.c_void_p), ("meta_24", ctypes.c_void_p), ("idx_24", ctypes.c_void_p)]
+                ("val_24", ctypes.c_void_p), ("meta_24", ctypes.c_void_p), ("idx_24", ctypes.c_void_p),
+                ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
 
 
 class TPlanT(ctypes.Structure):
@@ -188,6 +190,7 @@ class HinmPacked:
     val_24: torch.Tensor      # int16 bits of bf16 [T, n_24_pad/64, R, 32]
     meta_24: torch.Tensor     # int64 bits of uint64 [T, n_24_pad/64, R]
     idx_24: torch.Tensor      # int32 [T, n_24_pad]
+    flags: int = 0            # HINM_PACKED_* bits (set by pack)
 
     def struct(self) -> PackedT:
         """The C view of this weight (built once; the tensors must not be replaced afterwards)."""
@@ -196,7 +199,7 @@ class HinmPacked:
             def ptr(t):
                 return t.data_ptr() if t.numel() else None
             st = PackedT(self.plan.raw, ptr(self.val_dense), ptr(self.idx_dense), ptr(self.val_24),
-                         ptr(self.meta_24), ptr(self.idx_24))
+                         ptr(self.meta_24), ptr(self.idx_24), self.flags, 0)
             self.__dict__["_struct"] = st
             self.__dict__["_ws_need"] = {}
         return st
@@ -213,7 +216,7 @@ class HinmPacked:
         layout version, the plan's arguments and the five buffers."""
         p = self.plan
         return {"format": "hinm-packed", "format_version": HINM_FORMAT_VERSION, "cout": p.cout, "cin": p.cin,
-                "tile_rows": p.tile_rows, "t_s": p.t_s, "v_s": p.v_s,
+                "tile_rows": p.tile_rows, "t_s": p.t_s, "v_s": p.v_s, "flags": int(self.flags),
                 **{k: getattr(self, k) for k in _BUFFERS}}
 
     @classmethod
@@ -228,7 +231,7 @@ class HinmPacked:
                 "val_24": ((T, p.n_24_pad // 64, R, 32), torch.int16),
                 "meta_24": ((T, p.n_24_pad // 64, R), torch.int64),
                 "idx_24": ((T, p.n_24_pad), torch.int32)}
-        return cls(p, **_checked_buffers(sd, want, device))
+        return cls(p, **_checked_buffers(sd, want, device), flags=int(sd.get("flags", 0)))
 
 
 _BUFFERS = ("val_dense", "idx_dense", "val_24", "meta_24", "idx_24")
@@ -311,6 +314,7 @@ def pack(w: torch.Tensor, importance: torch.Tensor, tile_rows: int, t_s: float, 
         _check(library().hinm_pack(ctypes.byref(p.raw), w.data_ptr(), w.stride(0), importance.data_ptr(),
                                    importance.stride(0), perm.data_ptr() if perm is not None else None,
                                    ctypes.byref(st), ws.data_ptr(), ws.numel(), _stream_ptr(w.device)))
+    out.flags = int(st.flags)
     return out
 
 
@@ -652,8 +656,10 @@ def translate_indices(packed: HinmPacked, mapping: torch.Tensor) -> HinmPacked:
         raise ValueError(f"mapping must be a contiguous int32 [{p.cin}] tensor on {dev}")
     ws = torch.empty(256, dtype=torch.uint8, device=dev)
     with torch.cuda.device(dev):
-        _check(library().hinm_translate_indices(ctypes.byref(packed.struct()), mapping.data_ptr(), ws.data_ptr(),
+        st = packed.struct()
+        _check(library().hinm_translate_indices(ctypes.byref(st), mapping.data_ptr(), ws.data_ptr(),
                                                 ws.numel(), _stream_ptr(dev)))
+    packed.flags = int(st.flags)
     return packed
 
 

@@ -31,6 +31,8 @@ __device__ inline TileDesc tile_desc(const int32_t* tiles, int t, int n_dense, i
   return {t * (n_dense_pad / 32), n_dense, t * (n_24_pad / 64), n_24};
 }
 constexpr int kFlagPerm = 1, kFlagImportance = 2;
+// set when some perm row moves a column out of its aligned block of 64 positions
+constexpr int kFlagNotBlock64 = 4;
 
 __global__ void zero_flag_kernel(int* flag) {
   if (threadIdx.x < 64) flag[threadIdx.x] = 0;
@@ -46,17 +48,19 @@ __global__ __launch_bounds__(1024) void check_perm_kernel(const int32_t* __restr
   for (int i = threadIdx.x; i < nw; i += blockDim.x) seen[i] = 0u;
   __syncthreads();
   const int32_t* row = perm + (int64_t)blockIdx.x * cin;
-  bool bad = false;
+  bool bad = false, off_block = false;
   for (int j = threadIdx.x; j < cin; j += blockDim.x) {
     const int c = row[j];
     if (c < 0 || c >= cin) {
       bad = true;
       continue;
     }
+    off_block |= (c >> 6) != (j >> 6);
     const uint32_t m = 1u << (c & 31);
     if (atomicOr(&seen[c >> 5], m) & m) bad = true;
   }
   if (bad) atomicOr(flag, kFlagPerm);
+  if (off_block) atomicOr(flag, kFlagNotBlock64);
 }
 
 // Score of the vector (tile t, column c): sum over the tile's rows of the
@@ -345,7 +349,7 @@ struct PackShape {
 static int pack_core(const PackShape& p, const int32_t* tiles, const void* w_bf16, int64_t ldw,
                      const float* importance, int64_t ldi, const int32_t* perm, void* val_dense, int32_t* idx_dense,
                      void* val_24, uint64_t* meta_24, int32_t* idx_24, void* workspace, size_t workspace_bytes,
-                     size_t need, void* stream_) {
+                     size_t need, void* stream_, uint32_t* packed_flags = nullptr) {
   if (!w_bf16 || !importance) return fail(HINM_EINVAL, "w and importance must be non-NULL");
   if (ldw < p.cin || ldi < p.cin)
     return fail(HINM_ESHAPE, "ldw=%lld and ldi=%lld must be >= cin=%d", (long long)ldw, (long long)ldi, p.cin);
@@ -388,6 +392,7 @@ static int pack_core(const PackShape& p, const int32_t* tiles, const void* w_bf1
   if (e != hipSuccess) return hip_fail(e, "pack stage-1");
   if (hflag & kFlagPerm) return fail(HINM_EPERM, "a perm row is not a permutation of 0..%d", cin - 1);
   if (hflag & kFlagImportance) return fail(HINM_EIMPORTANCE, "importance has a negative or non-finite entry");
+  if (packed_flags) *packed_flags = (hflag & kFlagNotBlock64) ? 0u : (uint32_t)HINM_PACKED_WINDOWED;
 
   // Stage 2: regions, index lists, values and metadata.
   hipLaunchKernelGGL(regions_kernel, dim3((cin + 255) / 256, T), dim3(256), 0, stream, scores, cin, p.n_dense,
@@ -460,8 +465,10 @@ extern "C" int hinm_pack(const hinm_plan_t* plan, const void* w_bf16, int64_t ld
   size_t need = 0;
   hinm_pack_workspace_bytes(plan, &need);
   out->plan = p;
+  out->flags = 0;
+  out->reserved = 0;
   return pack_core(ps, nullptr, w_bf16, ldw, importance, ldi, perm, out->val_dense, out->idx_dense, out->val_24,
-                   out->meta_24, out->idx_24, workspace, workspace_bytes, need, stream);
+                   out->meta_24, out->idx_24, workspace, workspace_bytes, need, stream, &out->flags);
 }
 
 extern "C" int hinm_pack_tiles(const hinm_tplan_t* plan, const void* w_bf16, int64_t ldw, const float* importance,
@@ -522,6 +529,8 @@ extern "C" int hinm_translate_indices(hinm_packed_t* packed, const int32_t* map,
   if (e != hipSuccess) return hip_fail(e, "translate launch");
   e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_fail(e, "translate");
+  // a map that moves a channel out of its block of 64 breaks the lists' window order
+  if (hflag & kFlagNotBlock64) packed->flags &= ~(uint32_t)HINM_PACKED_WINDOWED;
   return HINM_OK;
 }
 

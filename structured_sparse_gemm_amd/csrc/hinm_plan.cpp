@@ -95,6 +95,8 @@ constexpr OptionDef kOptionDefs[HINM_OPT_COUNT] = {
     {"HINM_PREFILL_SPLITS", 0},        // HINM_OPT_PREFILL_SPLITS
     {"HINM_PREFILL_PATH", 0},          // HINM_OPT_PREFILL_PATH
     {"HINM_PREFILL_PER_XCD", 0},       // HINM_OPT_PREFILL_PER_XCD
+    {"HINM_PREFILL_TB_GROUP", 0},      // HINM_OPT_PREFILL_TB_GROUP
+    {"HINM_PREFILL_STAGGER", 0},       // HINM_OPT_PREFILL_STAGGER
 };
 
 bool option_valid(int key, int64_t v) {
@@ -105,6 +107,8 @@ bool option_valid(int key, int64_t v) {
     case HINM_OPT_PREFILL_SPLITS: return v == 0 || v == 1 || v == 2 || v == 4;
     case HINM_OPT_PREFILL_PATH: return v == 0 || v == 1;
     case HINM_OPT_PREFILL_PER_XCD: return v >= 0 && v <= 1024;
+    case HINM_OPT_PREFILL_TB_GROUP: return v >= 0 && v <= 64;
+    case HINM_OPT_PREFILL_STAGGER: return v == 0 || v == 1;
     default: return false;
   }
 }

@@ -60,6 +60,8 @@ struct SpmmArgs {
                              // first 2:4 block, n_24 of each tile
   int kd_total, ks_total;    // dense and 2:4 K-blocks over all tiles
   int part_rows;             // rows of a split reduction's partial-sum planes (all weights of a group)
+  int tb_group;              // batch > 64 kernel: token blocks per group of its item order (>= 1)
+  int stagger;               // batch > 64 kernel: tile t starts its K loops at block t * n / n_tiles
 };
 
 // Several packed weights multiplied by one X in one launch (hinm_spmm_group):
@@ -814,7 +816,7 @@ struct PrefillA {
 //     into a small LDS array.
 template <int NT, bool FAST, bool DENSE>
 __device__ inline void prefill_phase(const SpmmArgs& a, const BufRes& res, uint16_t* xs0, uint16_t* xs1,
-                                     uint32_t* ms0, uint32_t* ms1, int kbase, int nb, int rb, int n0,
+                                     uint32_t* ms0, uint32_t* ms1, int kbase, int nb, int rot, int rb, int n0,
                                      f32x16 (&acc)[2][PrefillCfg<NT>::NTB]) {
   using C = PrefillCfg<NT>;
   constexpr int KPOS = DENSE ? 32 : 64;       // positions per block
@@ -854,6 +856,7 @@ __device__ inline void prefill_phase(const SpmmArgs& a, const BufRes& res, uint1
   const uint32_t ipos = (uint32_t)(wave * WP + (lane % WP));
   auto load_idx = [&](int b) -> int {
     b = min(b, nb - 1);
+    b = b + rot < nb ? b + rot : b + rot - nb;     // the block order starts at block rot
     const uint32_t off = ((uint32_t)(kbase + b) * KPOS + ipos) * 4u;
     return (int)__builtin_amdgcn_raw_buffer_load_b32(rid, off, 0, 0);
   };
@@ -886,6 +889,7 @@ __device__ inline void prefill_phase(const SpmmArgs& a, const BufRes& res, uint1
   };
   auto load_a = [&](int b, PrefillA& st) {
     b = min(b, nb - 1);
+    b = b + rot < nb ? b + rot : b + rot - nb;
     const uint32_t blk = (uint32_t)(kbase + b) * (uint32_t)a.rows + vrow;
     st.v = __builtin_amdgcn_raw_buffer_load_b128(rv, blk * 64u + 16u * threadIdx.x, 0, 0);
     if constexpr (!DENSE)
@@ -1054,7 +1058,7 @@ __device__ inline v4i16 tr_read_b(const uint8_t* lds) {
 // shift is a branch, which is kept out of the other instantiations.
 template <int NT, bool DENSE, int TAIL>
 __device__ inline void prefill_phase_lds(const SpmmArgs& a, const BufRes& res, uint16_t* xs0, uint16_t* xs1,
-                                         uint32_t* ms0, uint32_t* ms1, int kbase, int nb, int rb, int n0,
+                                         uint32_t* ms0, uint32_t* ms1, int kbase, int nb, int rot, int rb, int n0,
                                          f32x16 (&acc)[2][PrefillCfg<NT>::NTB]) {
   using C = PrefillCfg<NT>;
   constexpr int KPOS = DENSE ? 32 : 64;       // positions per block
@@ -1090,6 +1094,7 @@ __device__ inline void prefill_phase_lds(const SpmmArgs& a, const BufRes& res, u
   const uint32_t ipos = (uint32_t)(wave * RPW + (lane % RPW));
   auto load_idx = [&](int b) -> int {
     b = min(b, nb - 1);
+    b = b + rot < nb ? b + rot : b + rot - nb;     // the block order starts at block rot
     return (int)__builtin_amdgcn_raw_buffer_load_b32(rid, ((uint32_t)(kbase + b) * KPOS + ipos) * 4u, 0, 0);
   };
   auto spread_idx = [&](int iw, int (&ci)[NJ]) {
@@ -1140,6 +1145,7 @@ __device__ inline void prefill_phase_lds(const SpmmArgs& a, const BufRes& res, u
   };
   auto load_a = [&](int b, PrefillA& st) {
     b = min(b, nb - 1);
+    b = b + rot < nb ? b + rot : b + rot - nb;
     const uint32_t blk = (uint32_t)(kbase + b) * (uint32_t)a.rows + vrow;
     st.v = __builtin_amdgcn_raw_buffer_load_b128(rv, blk * 64u + 16u * threadIdx.x, 0, 0);
     if constexpr (!DENSE)
@@ -1268,13 +1274,14 @@ __device__ inline void prefill_phase_lds(const SpmmArgs& a, const BufRes& res, u
 // dense first): the first dense and 2:4 block and the counts.
 struct KShare {
   int kd, nd, ks, ns;
+  int rd, rs;       // first block of the dense and 2:4 loops (the order wraps around)
 };
 __device__ inline KShare k_share(const TileK& tk, int split, int splits) {
   const int nblk = tk.nbd + tk.nbs;
   const int lo = (int)((int64_t)split * nblk / splits), hi = (int)((int64_t)(split + 1) * nblk / splits);
   const int d_lo = min(lo, tk.nbd), d_hi = min(hi, tk.nbd);
   const int s_lo = max(lo, tk.nbd) - tk.nbd, s_hi = max(hi, tk.nbd) - tk.nbd;
-  return {tk.kd0 + d_lo, d_hi - d_lo, tk.ks0 + s_lo, s_hi - s_lo};
+  return {tk.kd0 + d_lo, d_hi - d_lo, tk.ks0 + s_lo, s_hi - s_lo, 0, 0};
 }
 
 // X straight into LDS; TAIL: the token block ends past the batch (1: even
@@ -1283,8 +1290,8 @@ template <int NT, int TAIL>
 __device__ inline void prefill_body_lds(const SpmmArgs& a, const BufRes& res, uint16_t* xs0, uint16_t* xs1,
                                         uint32_t* ms0, uint32_t* ms1, const KShare& ks, int rb, int n0,
                                         f32x16 (&acc)[2][PrefillCfg<NT>::NTB]) {
-  prefill_phase_lds<NT, true, TAIL>(a, res, xs0, xs1, ms0, ms1, ks.kd, ks.nd, rb, n0, acc);
-  prefill_phase_lds<NT, false, TAIL>(a, res, xs0, xs1, ms0, ms1, ks.ks, ks.ns, rb, n0, acc);
+  prefill_phase_lds<NT, true, TAIL>(a, res, xs0, xs1, ms0, ms1, ks.kd, ks.nd, ks.rd, rb, n0, acc);
+  prefill_phase_lds<NT, false, TAIL>(a, res, xs0, xs1, ms0, ms1, ks.ks, ks.ns, ks.rs, rb, n0, acc);
 }
 
 // X through registers; FAST: 16-byte aligned X rows and a token block inside
@@ -1293,8 +1300,8 @@ template <int NT, bool FAST>
 __device__ inline void prefill_body_staged(const SpmmArgs& a, const BufRes& res, uint16_t* xs0, uint16_t* xs1,
                                            uint32_t* ms0, uint32_t* ms1, const KShare& ks, int rb, int n0,
                                            f32x16 (&acc)[2][PrefillCfg<NT>::NTB]) {
-  prefill_phase<NT, FAST, true>(a, res, xs0, xs1, ms0, ms1, ks.kd, ks.nd, rb, n0, acc);
-  prefill_phase<NT, FAST, false>(a, res, xs0, xs1, ms0, ms1, ks.ks, ks.ns, rb, n0, acc);
+  prefill_phase<NT, FAST, true>(a, res, xs0, xs1, ms0, ms1, ks.kd, ks.nd, ks.rd, rb, n0, acc);
+  prefill_phase<NT, FAST, false>(a, res, xs0, xs1, ms0, ms1, ks.ks, ks.ns, ks.rs, rb, n0, acc);
 }
 
 // Persistent launch: gridDim.x = 8 * per_xcd workgroups, workgroup L runs on
@@ -1375,7 +1382,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a0, Segs segs,
   for (int it = i_lo + slot; it < i_hi; it += per_xcd) {
     {
       const int split = SPLIT ? it % splits : 0, item = SPLIT ? it / splits : it;
-      const int tb = item / n_tr, gtrb = item % n_tr;
+      // items in groups of a.tb_group token blocks, row-block major inside a
+      // group (one token block per group: token-block major)
+      int tb, gtrb;
+      {
+        const int G = a.tb_group, full = n_tb / G * G;
+        if (item < full * n_tr) {
+          const int rem = item % (n_tr * G);
+          gtrb = rem / G;
+          tb = item / (n_tr * G) * G + rem % G;
+        } else {
+          const int r2 = item - full * n_tr, gt = n_tb - full;
+          gtrb = r2 / gt;
+          tb = full + r2 % gt;
+        }
+      }
       SpmmArgs a = a0;
       int trb0, row0;
       select_seg(segs, gtrb, a, trb0, row0);
@@ -1391,7 +1412,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a0, Segs segs,
           for (int e = 0; e < 16; ++e) acc[r][j][e] = 0.f;
 
       const TileK tk = tile_k(a, t);
-      const KShare ks = SPLIT ? k_share(tk, split, splits) : KShare{tk.kd0, tk.nbd, tk.ks0, tk.nbs};
+      KShare ks = SPLIT ? k_share(tk, split, splits) : KShare{tk.kd0, tk.nbd, tk.ks0, tk.nbs, 0, 0};
+      if (a.stagger) {
+        // tiles start their K loops at staggered blocks, so that tiles whose
+        // index lists walk X in the same order do not read the same rows at
+        // the same time
+        ks.rd = ks.nd ? (int)((int64_t)t * ks.nd / a.n_tiles) % ks.nd : 0;
+        ks.rs = ks.ns ? (int)((int64_t)t * ks.ns / a.n_tiles) % ks.ns : 0;
+      }
       const bool tail = n0 + NT > a.batch;
       bool direct = false;
       if constexpr (NT == 256) direct = a.x_lds;
@@ -1510,6 +1538,7 @@ struct PackedView {
   const int32_t* idx_24;
   const int32_t* tiles;
   int kd_total, ks_total;
+  uint32_t flags;       // HINM_PACKED_* (every weight of a group)
 };
 
 // `p` has been validated by the caller (for the per-tile layout it carries
@@ -1596,6 +1625,9 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
   a.kd_total = packed->kd_total;
   a.ks_total = packed->ks_total;
   a.part_rows = p.cout;
+  a.tb_group = hinm::option(HINM_OPT_PREFILL_TB_GROUP) > 0 ? (int)hinm::option(HINM_OPT_PREFILL_TB_GROUP)
+                                                            : ((packed->flags & HINM_PACKED_WINDOWED) ? 2 : 1);
+  a.stagger = hinm::option(HINM_OPT_PREFILL_STAGGER) == 0;
   Segs one;
   one.n = 0;
   if (segs) a.y_vec = a.y_vec && segs_y_vec(*segs);
@@ -1689,7 +1721,7 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
 static PackedView uniform_view(const hinm_packed_t& k) {
   const hinm_plan_t& p = k.plan;
   return {k.val_dense, k.idx_dense, k.val_24, k.meta_24, k.idx_24, nullptr,
-          p.n_tiles * (p.n_dense_pad / HINM_KB_DENSE), p.n_tiles * (p.n_24_pad / HINM_KB_24)};
+          p.n_tiles * (p.n_dense_pad / HINM_KB_DENSE), p.n_tiles * (p.n_24_pad / HINM_KB_24), k.flags};
 }
 
 extern "C" int hinm_spmm(const hinm_packed_t* packed, const void* x_bf16, int64_t batch, int64_t ldx, void* y_bf16,
@@ -1712,7 +1744,7 @@ extern "C" int hinm_spmm_tiles(const hinm_tpacked_t* packed, const void* x_bf16,
   if (!hinm::aligned(packed->tiles, 4)) return fail(HINM_EALIGN, "the tile table is not 4-byte aligned");
   const hinm_tplan_t& p = packed->plan;
   const PackedView v = {packed->val_dense, packed->idx_dense, packed->val_24, packed->meta_24, packed->idx_24,
-                        packed->tiles, p.dense_blocks, p.blocks_24};
+                        packed->tiles, p.dense_blocks, p.blocks_24, 0u};
   return spmm_impl(hinm::shape_plan(p), v, x_bf16, batch, ldx, y_bf16, ldy, nullptr, workspace, workspace_bytes,
                    stream);
 }
@@ -1846,8 +1878,9 @@ extern "C" int hinm_spmm_group(int n, const hinm_packed_t* const* packed, const 
     trb += q.n_tiles * (q.tile_rows / 64);
     row += q.cout;
   }
-  return spmm_impl(comb, uniform_view(*packed[0]), x_bf16, batch, ldx, y_bf16[0], ldy[0], nullptr, workspace,
-                   workspace_bytes, stream, &sg);
+  PackedView v0 = uniform_view(*packed[0]);
+  for (int g = 1; g < n; ++g) v0.flags &= packed[g]->flags;
+  return spmm_impl(comb, v0, x_bf16, batch, ldx, y_bf16[0], ldy[0], nullptr, workspace, workspace_bytes, stream, &sg);
 }
 
 // ---------------------------------------------------------------------------
