@@ -204,13 +204,17 @@ int hinm_abi_version(void);
  *                             major; 1 .. 64; same bits of Y)
  *   HINM_OPT_PREFILL_STAGGER  env HINM_PREFILL_STAGGER: 0 (default): the
  *                             batch > 64 kernel starts tile t's dense and
- *                             2:4 K loops at block t * n / n_tiles of its n
- *                             and wraps around, so tiles whose index lists
- *                             walk X in the same order (block-diagonal or
- *                             identity perms) do not read the same rows at
- *                             the same time; 1: every tile from its first
- *                             block.  Either order is deterministic; they
- *                             add the products in different orders.
+ *                             2:4 K loops, in token block tb, at block
+ *                             t * n / n_tiles + ((3 tb) mod 8) * n / 8 (mod
+ *                             n) of its n and wraps around, so tiles whose
+ *                             index lists walk X in the same order
+ *                             (block-diagonal or identity perms) do not read
+ *                             the same rows at the same time, and XCDs on
+ *                             different token blocks do not read a tile's
+ *                             packed values at the same time; 1: every tile
+ *                             from its first block.  Either order is
+ *                             deterministic; they add the products in
+ *                             different orders.
  * A change applies to products launched afterwards; a workspace sized under
  * other settings may then be too small (HINM_EWORKSPACE). */
 typedef enum {

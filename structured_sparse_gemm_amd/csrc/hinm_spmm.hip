@@ -1417,11 +1417,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a0, Segs segs,
       const TileK tk = tile_k(a, t);
       KShare ks = SPLIT ? k_share(tk, split, splits) : KShare{tk.kd0, tk.nbd, tk.ks0, tk.nbs, 0, 0};
       if (a.stagger) {
-        // tiles start their K loops at staggered blocks, so that tiles whose
-        // index lists walk X in the same order do not read the same rows at
-        // the same time
-        ks.rd = ks.nd ? (int)((int64_t)t * ks.nd / a.n_tiles) % ks.nd : 0;
-        ks.rs = ks.ns ? (int)((int64_t)t * ks.ns / a.n_tiles) % ks.ns : 0;
+        // Items start their K loops at staggered blocks: tile t at t/n_tiles
+        // of its range, so that tiles whose index lists walk X in the same
+        // order do not read the same rows at the same time, plus (3 tb mod
+        // 8)/8 for token block tb, so that the XCDs, which work on different
+        // token blocks at once, reach a tile's packed values at different
+        // times (the first read comes from HBM, the later ones from the
+        // last-level cache).  The order depends on (tile, token block) only,
+        // so every schedule of the items gives the same bits.
+        const int64_t tq = (3 * tb) & 7;
+        ks.rd = ks.nd ? (int)(((int64_t)t * ks.nd / a.n_tiles + tq * ks.nd / 8) % ks.nd) : 0;
+        ks.rs = ks.ns ? (int)(((int64_t)t * ks.ns / a.n_tiles + tq * ks.ns / 8) % ks.ns) : 0;
       }
       const bool tail = n0 + NT > a.batch;
       bool direct = false;
