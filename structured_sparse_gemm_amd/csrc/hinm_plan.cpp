@@ -5,6 +5,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "hinm_internal.h"
@@ -283,22 +284,48 @@ SpmmShape spmm_shape(const hinm_plan_t* p, int64_t batch) {
   }
   if (p->tile_rows % 64 == 0) {
     s.path = kPathPrefill;
-    s.nt = batch >= 1024 ? 256 : 128;
-    if (option(HINM_OPT_PREFILL_NT) != 0) s.nt = (int)option(HINM_OPT_PREFILL_NT);
-    s.n_tblocks = (int)((batch + s.nt - 1) / s.nt);
+    const int64_t rblocks = (int64_t)p->n_tiles * (p->tile_rows / 64);
+    const int nblk = p->n_dense_pad / HINM_KB_DENSE + p->n_24_pad / HINM_KB_24;
+    const int kunits = p->n_dense_pad / HINM_KB_DENSE + 2 * (p->n_24_pad / HINM_KB_24);
+    const int64_t per_xcd_max = option(HINM_OPT_PREFILL_PER_XCD) > 0 ? option(HINM_OPT_PREFILL_PER_XCD) : 64;
     // Fewer work items than compute units: split each item's K range over 2
     // or 4 workgroups (at most 512 in all, two per compute unit; each keeps
     // >= 8 K-blocks); partial sums through the workspace.  With 256 items or
     // more the partials' traffic costs more than the idle units: with the
     // weight streamed from HBM, 2 splits at 256 items were slower.
-    const int64_t items = (int64_t)p->n_tiles * (p->tile_rows / 64) * s.n_tblocks;
-    const int nblk = p->n_dense_pad / HINM_KB_DENSE + p->n_24_pad / HINM_KB_24;
-    int splits = 1;
-    if (option(HINM_OPT_PREFILL_SPLITS) != 0) {
-      splits = (int)option(HINM_OPT_PREFILL_SPLITS);
-    } else if (items < 256) {
-      while (splits < 4 && items * splits * 2 <= 512 && nblk / (splits * 2) >= 8) splits *= 2;
+    auto split_of = [&](int64_t items) {
+      int sp = 1;
+      if (option(HINM_OPT_PREFILL_SPLITS) != 0) {
+        sp = (int)option(HINM_OPT_PREFILL_SPLITS);
+      } else if (items < 256) {
+        while (sp < 4 && items * sp * 2 <= 512 && nblk / (sp * 2) >= 8) sp *= 2;
+      }
+      return sp;
+    };
+    // Rounds of the persistent grid (8 XCDs x up to per_xcd workgroups) and
+    // its size for a token block of nt.
+    auto grid_of = [&](int nt, int64_t* rounds, int64_t* nwg) {
+      const int64_t wi = rblocks * ((batch + nt - 1) / nt) * split_of(rblocks * ((batch + nt - 1) / nt));
+      const int64_t per_xcd = std::min(per_xcd_max, (wi + 7) / 8);
+      *rounds = ((wi + 7) / 8 + per_xcd - 1) / per_xcd;
+      *nwg = 8 * per_xcd;
+    };
+    // Token block: 256 from batch 1024; from 256 to 1023 tokens, 256 when it
+    // takes fewer rounds of the grid, or as many rounds and at least as many
+    // workgroups with a long K range (>= 120 units, a 2:4 block counting two);
+    // else 128 (measured over batches 256-896 on 4096x11008, 4096x4096 and
+    // 11008x4096 weights).
+    s.nt = batch >= 1024 ? 256 : 128;
+    if (batch >= 256 && batch < 1024) {
+      int64_t r128, w128, r256, w256;
+      grid_of(128, &r128, &w128);
+      grid_of(256, &r256, &w256);
+      if (r256 < r128 || (r256 == r128 && kunits >= 120 && w256 >= w128)) s.nt = 256;
     }
+    if (option(HINM_OPT_PREFILL_NT) != 0) s.nt = (int)option(HINM_OPT_PREFILL_NT);
+    s.n_tblocks = (int)((batch + s.nt - 1) / s.nt);
+    const int64_t items = rblocks * s.n_tblocks;
+    const int splits = split_of(items);
     if (splits > 1 && items <= kWsCounters) {
       s.splits = splits;
       s.ws_counter_bytes = kWsCounterBytes;
