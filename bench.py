@@ -9,7 +9,8 @@ the one-time pack are timed beside it and reported in the same JSON line,
 with one row per workload and batch of the five configurations (each with
 its roofline fractions), the 13-point batch sweep of the 32-layer 7B-shaped
 stack, the dense torch.matmul comparator, the GPU's empirical peaks and its
-clocks, the side rows of the later steps and the CPU oracle baseline.
+clocks, the side rows (output-row map, boundary search, per-tile v_s, gyro
+permutation, block-diagonal perms) and the CPU oracle baseline.
 
 Inputs are resident in HBM before timing starts; successive products rotate
 through enough copies of the packed weight, X and Y (>= 1 GiB) that the
