@@ -492,8 +492,15 @@ __global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(SpmmArgs a0, Seg
   static_assert(GT / CPR <= 64, "a gather step covers at most one block's positions per lane group");
   constexpr int MAXCH = MAXP * CPR / GT;       // X chunks per gather thread per round
   constexpr int NB = NTOK / 16;
-  constexpr int DPF = MAXB < 8 ? MAXB : 8;   // packed-value blocks in flight ahead of the multiplies
-  constexpr int P0 = DPF < 4 ? DPF : 4;       // of which issued before the first X gathers
+  // Packed-value blocks in flight ahead of the multiplies, and how many of
+  // them go out before the first X gathers: (4, 8) at 16 tokens, (2, 6) at
+  // 32 and 64, where each gathered X row is a larger share of the load
+  // queue (swept: 1.5-3.5% faster than (4, 8) at 48-64 tokens; wider
+  // windows were slower).
+  constexpr int DPF_ = NTOK == 16 ? 8 : 6;
+  constexpr int DPF = MAXB < DPF_ ? MAXB : DPF_;
+  constexpr int P0_ = NTOK == 16 ? 4 : 2;
+  constexpr int P0 = DPF < P0_ ? DPF : P0_;
   __shared__ __attribute__((aligned(16))) uint16_t xs[MAXP * NTOK];
   __shared__ int s_last;
 
