@@ -795,6 +795,10 @@ struct PrefillCfg {
   static constexpr int CPR = NT / 8;          // 16-byte chunks per gathered row
   static constexpr int PG = 256 / CPR;        // position groups per workgroup
   static constexpr int DA = 4;                // packed-value prefetch depth (blocks)
+  // The block loops are unrolled four times over compile-time register sets
+  // and step k uses packed-value set k % DA, so DA must divide 4 (a depth of
+  // 3 or 6 would pair blocks with the wrong values).
+  static_assert(4 % DA == 0, "packed-value prefetch depth must divide the unroll of 4");
 };
 
 // This thread's share of one block's packed values (16 bytes) and 2:4
