@@ -186,7 +186,7 @@ int hinm_abi_version(void);
  *                             256 from batch 1024, else 128)
  *   HINM_OPT_PREFILL_SPLITS   env HINM_PREFILL_SPLITS: K split of each
  *                             batch > 64 work item, 1, 2 or 4 (default 0: 2
- *                             or 4 below 256 items, else 1; a different split
+ *                             or 4 up to 128 items, else 1; a different split
  *                             may change the last bits of Y)
  *   HINM_OPT_PREFILL_PATH     env HINM_PREFILL_PATH=staged -> 1: the
  *                             batch > 64 kernel gathers X through registers

@@ -288,16 +288,19 @@ SpmmShape spmm_shape(const hinm_plan_t* p, int64_t batch) {
     const int nblk = p->n_dense_pad / HINM_KB_DENSE + p->n_24_pad / HINM_KB_24;
     const int kunits = p->n_dense_pad / HINM_KB_DENSE + 2 * (p->n_24_pad / HINM_KB_24);
     const int64_t per_xcd_max = option(HINM_OPT_PREFILL_PER_XCD) > 0 ? option(HINM_OPT_PREFILL_PER_XCD) : 64;
-    // Fewer work items than compute units: split each item's K range over 2
-    // or 4 workgroups (at most 512 in all, two per compute unit; each keeps
-    // >= 8 K-blocks); partial sums through the workspace.  With 256 items or
-    // more the partials' traffic costs more than the idle units: with the
-    // weight streamed from HBM, 2 splits at 256 items were slower.
+    // At most half as many work items as compute units: split each item's K
+    // range over 2 or 4 workgroups (at most 512 in all, two per compute unit;
+    // each keeps >= 8 K-blocks); partial sums through the workspace.  With
+    // more items a split cannot take work off the busiest compute units (172
+    // items split 2 ways still put two half items on some of them), and its
+    // partials only add traffic: up_proj (172 row blocks) at batch 65-128
+    // ran 2-9% faster unsplit; with the weight streamed from HBM, 2 splits at
+    // 256 items were slower too.
     auto split_of = [&](int64_t items) {
       int sp = 1;
       if (option(HINM_OPT_PREFILL_SPLITS) != 0) {
         sp = (int)option(HINM_OPT_PREFILL_SPLITS);
-      } else if (items < 256) {
+      } else if (items <= 128) {
         while (sp < 4 && items * sp * 2 <= 512 && nblk / (sp * 2) >= 8) sp *= 2;
       }
       return sp;

@@ -196,8 +196,9 @@ def test_workspace_sizes(lib):
     p = hinm.plan(11008, 4096, 64, 0.75, 0.55)
     for b in (0, 2048, 4096):                  # 1376 and 2752 work items: no K split
         assert hinm.spmm_workspace_bytes(p, b) == 0
-    # 172 items of 128 tokens: split 2 ways; per item and split 256 threads x 32 fp32 partials
-    assert hinm.spmm_workspace_bytes(p, 65) == counters + 2 * 172 * 256 * 128
+    assert hinm.spmm_workspace_bytes(p, 65) == 0        # 172 items of 128 tokens: more than 128, no split
+    # 128 items of 128 tokens: split 4 ways; per item and split 256 threads x 32 fp32 partials
+    assert hinm.spmm_workspace_bytes(hinm.plan(4096, 11008, 64, 0.75, 0.55), 200) == counters + 4 * 128 * 256 * 128
     for b in (1, 16, 64):
         assert hinm.spmm_workspace_bytes(p, b) % 4 == 0
     q = hinm.plan(4096, 4096, 64, 0.5, 0.25)   # 64 items at batch 128: split 4 ways
