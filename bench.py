@@ -461,9 +461,12 @@ def cpu_baseline(w, batch):
         threads = os.cpu_count()
     p = oh.plan(w.cout, w.cin, w.tile_rows, w.t_s, w.v_s)
     bits = w.w_bf16.view(__import__("torch").int16).numpy().view(np.uint16)
-    t0 = time.perf_counter()
-    _, inter = oh.pack(bits, w.importance.numpy(), w.perm.numpy(), p, with_intermediates=True)
-    t_pack = time.perf_counter() - t0
+    pack_times = []
+    for _ in range(4):                       # one warm-up, then the median of three
+        t0 = time.perf_counter()
+        _, inter = oh.pack(bits, w.importance.numpy(), w.perm.numpy(), p, with_intermediates=True)
+        pack_times.append(time.perf_counter() - t0)
+    t_pack = sorted(pack_times[1:])[1]
     wh = oh.masked_weight(bits, inter["mask"])
     xf = synth.as_f64(w.x_bf16)
     t0 = time.perf_counter()
@@ -477,12 +480,42 @@ def cpu_baseline(w, batch):
     t_prod = (time.perf_counter() - t0) / reps
     useful = 2 * p.cout * (p.cin - p.z) * batch
     return {"value": round(useful / t_prod / 1e12, 4), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": (f"whole workload: oracle pack of the 4096x11008 weight once ({t_pack:.2f} s), then its "
-                       f"float64 product at batch {batch} {reps} times ({t_prod:.3f} s each, {t_prod * reps:.1f} s); "
-                       f"value = useful flops / mean product time"),
+            "sample": (f"whole workload: oracle pack of the 4096x11008 weight (median of 3 after one warm-up: "
+                       f"{t_pack:.2f} s), then its float64 product at batch {batch} {reps} times ({t_prod:.3f} s each, "
+                       f"{t_prod * reps:.1f} s); value = useful flops / mean product time"),
             "pack_s": round(t_pack, 3), "product_s": round(t_prod, 4), "product_reps": reps,
             "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
 
+
+
+def cpu_baseline_stack(batches=(1, 16, 2048)):
+    """CPU-baseline leg for the stack sweep: the oracle packs one layer's seven weights (the stack's layer 0),
+    then runs their float64 products at each batch; a forward is 32 such layers."""
+    import numpy as np
+    import torch
+
+    import oracle.hinm as oh
+    import synth
+    whs, pack_s = [], 0.0
+    for proj in range(len(synth.STACK_PROJS)):
+        w = synth.stack_layer(0, proj, batch=1)
+        p = oh.plan(w.cout, w.cin, w.tile_rows, w.t_s, w.v_s)
+        bits = w.w_bf16.view(torch.int16).numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        _, inter = oh.pack(bits, w.importance.numpy(), w.perm.numpy(), p, with_intermediates=True)
+        pack_s += time.perf_counter() - t0
+        whs.append(oh.masked_weight(bits, inter["mask"]))
+    per = {}
+    for b in batches:
+        xs = {cin: synth.as_f64(torch.randn(cin, b, generator=torch.Generator().manual_seed(b)).to(torch.bfloat16))
+              for cin in sorted({wh.shape[1] for wh in whs})}
+        t0 = time.perf_counter()
+        for wh in whs:
+            oh.spmm(wh, xs[wh.shape[1]])
+        per[str(b)] = round((time.perf_counter() - t0) * 32 * 1e3, 1)
+    return {"oracle_ms_per_forward": per, "oracle_pack_s_per_layer": round(pack_s, 2),
+            "oracle_sample": ("one layer's seven products (layer 0 of the stack, oracle pack then float64 "
+                              "products) timed once per batch, times 32 layers")}
 
 
 def cpu_baseline_boundary(wb):
@@ -719,6 +752,8 @@ def main():
     stack = None if args.no_stack else stack_sweep(hinm, torch, synth, dev, not args.no_dense)
     log("CPU oracle baseline")
     cpu = None if args.no_cpu else cpu_baseline(w, B)
+    if cpu is not None and stack is not None:
+        stack.update(cpu_baseline_stack())
 
     line = {
         "metric": "HiNM SpMM effective TFLOP/s + HBM GB/s, 4096x11008 bf16 at batch 16 and 2048",
