@@ -183,7 +183,11 @@ int hinm_abi_version(void);
  *                             count may change the last bits of Y.
  *   HINM_OPT_PREFILL_NT       env HINM_PREFILL_NT: token block of the
  *                             batch > 64 kernel, 128 or 256 (default 0:
- *                             256 from batch 1024, else 128)
+ *                             256 from batch 1024; from 256 to 1023, 256
+ *                             when it takes fewer rounds of the persistent
+ *                             grid, or as many with at least as many
+ *                             workgroups and >= 120 K units per tile (a
+ *                             2:4 block counting two); else 128)
  *   HINM_OPT_PREFILL_SPLITS   env HINM_PREFILL_SPLITS: K split of each
  *                             batch > 64 work item, 1, 2 or 4 (default 0: 2
  *                             or 4 up to 128 items, else 1; a different split
