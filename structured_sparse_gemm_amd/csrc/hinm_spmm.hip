@@ -482,7 +482,7 @@ __device__ inline int xs_gran(int p, int g) {
   else return 4 * p + (g ^ (((p >> 1) & 1) | (((p >> 3) & 1) << 1)));
 }
 
-template <int NTOK, int MAXB, bool FAST, int NG>
+template <int NTOK, int MAXB, bool FAST, int NG, bool ONE = false>
 __global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(SpmmArgs a0, Segs segs, int splits, int n_tb,
                                                                 float* __restrict__ part,
                                                                 unsigned* __restrict__ counters) {
@@ -586,6 +586,56 @@ __global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(SpmmArgs a0, Seg
     // lists name every X row at most once, so a lane meets that row at most
     // once a round.
     const int fixrow = (!FAST && vt > 0 && vt < 8 && (vt & 1)) ? a.cin - 1 : -2;
+    if (ONE && a.batch == 1) {
+      // Batch 1 (its own instantiation; the run-time test keeps the general
+      // gather below in it, which the compiler schedules better around this
+      // one than it does alone): a 2-byte load of each gathered
+      // element (always aligned, never past the buffer's end), the rest of
+      // its 16-token granule zero.  16-byte loads would start 2 bytes past a
+      // dword at every odd row of a contiguous X (1.4-1.6 us more for the
+      // q/k/v and gate/up groups), and a quarter of the registers holds the
+      // round.
+      static_assert(!ONE || (NTOK == 16 && !FAST), "batch 1 runs the 16-token kernel");
+      uint32_t x1[MAXCH];
+      auto issue1 = [&](int r0) {
+        const int r1 = min(r0 + MAXB, b_hi);
+        const int nbr = r1 - r0;
+        const int nd_r = max(0, min(r1, tk.nbd) - r0);
+        const uint32_t dbase = (uint32_t)(tk.kd0 + r0) * 32u;
+        const uint32_t sbase = (uint32_t)(tk.ks0 + max(0, r0 - tk.nbd)) * 64u;
+        int cidx[MAXCH];
+#pragma unroll
+        for (int j = 0; j < MAXCH; ++j) {
+          const int blk = (PPJ * j) >> 6;
+          const int slot = pofs + ((PPJ * j) & 63);
+          const bool dense = blk < nd_r;
+          const uint32_t li = dense ? dbase + 32u * blk + 2u * (slot >> 2) + (slot & 1)
+                                    : sbase + 64u * (blk - nd_r) + slot;
+          const __amdgpu_buffer_rsrc_t r = dense ? res.id : res.is;
+          const bool ok = blk < nbr && !(dense && (slot & 2));
+          const int v = (int)__builtin_amdgcn_raw_buffer_load_b32(r, ok ? li * 4u : kOob, 0, 0);
+          cidx[j] = ok ? v : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < MAXCH; ++j) {
+          const int ci = cidx[j];
+          // the second 8-token chunk's lanes have an offset past the buffer (xcol)
+          const uint32_t off = ci < 0 ? kOob : __umul24((uint32_t)ci, res.ldx_bytes) + xcol;
+          x1[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(res.x, off, 0, 0);
+        }
+      };
+      if (nrounds > 0) issue1(b_lo);
+      __syncthreads();   // the first X gathers are on their way: let the packed values go
+      for (int r = 0; r < nrounds; ++r) {
+#pragma unroll
+        for (int j = 0; j < MAXCH; ++j)
+          *reinterpret_cast<u32x4*>(xs + xs_gran<NB>(pofs + PPJ * j, (gt % CPR) >> 1) * 16 + 8 * (gt & 1)) =
+              u32x4{x1[j], 0u, 0u, 0u};
+        if (r + 1 < nrounds) issue1(b_lo + (r + 1) * MAXB);
+        __syncthreads();   // X rows are in LDS
+        __syncthreads();   // the row waves are done with them
+      }
+    } else {
     u32x4 xr[MAXCH];
     int fix_j = -1;
     auto issue = [&](int r0) {
@@ -644,6 +694,7 @@ __global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(SpmmArgs a0, Seg
       if (r + 1 < nrounds) issue(b_lo + (r + 1) * MAXB);
       __syncthreads();   // X rows are in LDS
       __syncthreads();   // the row waves are done with them
+    }
     }
   } else {
     // Each role holds its own barriers (the condition is uniform per wave),
@@ -1685,7 +1736,8 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
     // 16 tokens: 24 blocks a round (48 KB of LDS), 2 gather waves; 32 and
     // 64 tokens: 96 KB rounds (24 / 12 blocks) with 4 gather waves.
     const dim3 grid(p.n_tiles * (p.tile_rows / 64) * sh.splits, sh.n_tblocks), b6(384), b8(512);
-    switch (sh.nt * 2 + (fast ? 1 : 0)) {
+    switch (batch == 1 ? 1 : sh.nt * 2 + (fast ? 1 : 0)) {
+      case 1: hipLaunchKernelGGL((decode5_kernel<16, 24, false, 2, true>), grid, b6, 0, stream, a, sg, sh.splits, sh.n_tblocks, part, counters); break;
       case 33: hipLaunchKernelGGL((decode5_kernel<16, 24, true, 2>), grid, b6, 0, stream, a, sg, sh.splits, sh.n_tblocks, part, counters); break;
       case 32: hipLaunchKernelGGL((decode5_kernel<16, 24, false, 2>), grid, b6, 0, stream, a, sg, sh.splits, sh.n_tblocks, part, counters); break;
       case 65: hipLaunchKernelGGL((decode5_kernel<32, 24, true, 4>), grid, b8, 0, stream, a, sg, sh.splits, sh.n_tblocks, part, counters); break;

@@ -268,6 +268,36 @@ def test_spmm_decode_ragged_full_width(unaligned):
         check_y(y, oh.spmm(c.w_hat, xf), np.abs(c.w_hat) @ np.abs(xf), f"q_proj batch {b}")
 
 
+def test_spmm_decode_small_batch_x_layouts_bit_identical():
+    """Batches of 1 to 7 tokens (one partial 8-token chunk per X row), X rows at every 2-byte alignment: a
+    contiguous X (odd row pitch at odd batches), odd and even row strides, and X starting 2 bytes past a
+    dword.  Chunks that start 2 bytes past a dword are loaded from the dword boundary and shifted back in
+    LDS; the product must be bit-identical to the same product from a copy of X with 16-byte rows (the
+    same kernel, adding the same terms in the same order), and within the bar of the oracle.  The last
+    input channel is kept in every tile, so the end of the X buffer is exercised too."""
+    w = synth.small(256, 1032, 64, 0.6, 0.35, 1, seed=31)
+    w.importance[:, -1] = w.importance.max() * 4.0
+    c = Case(w)
+    cin = w.cin
+    for b in (1, 2, 3, 4, 5, 7):
+        g = torch.Generator().manual_seed(500 + b)
+        x = torch.randn(cin, b, generator=g).to(torch.bfloat16)
+        ref16 = torch.zeros(cin, 16, dtype=torch.bfloat16, device=DEV)
+        ref16[:, :b] = x.to(DEV)
+        y_ref = hinm.spmm(c.pk, ref16[:, :b])
+        xf = synth.as_f64(x)
+        for ldx in sorted({b, b + 1, b + 2, 2 * b + 1}):
+            for shift in (0, 1):
+                buf = torch.zeros(cin * ldx + shift + 8, dtype=torch.bfloat16, device=DEV)
+                xd = buf[shift:shift + cin * ldx].view(cin, ldx)[:, :b]
+                xd.copy_(x.to(DEV))
+                print(f"[spmm]   batch={b} ldx={ldx} base+{2 * shift} bytes", flush=True)
+                y = hinm.spmm(c.pk, xd)
+                torch.cuda.synchronize()
+                assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), (b, ldx, shift)
+        check_y(y_ref, oh.spmm(c.w_hat, xf), np.abs(c.w_hat) @ np.abs(xf), f"small batch {b}")
+
+
 @pytest.mark.parametrize("batch", [16, 100])
 def test_spmm_x_beyond_32bit_offsets(batch):
     """X whose row stride puts its last row past 2^31 bytes (4096 rows of 300000 elements, 2.46 GB).
