@@ -801,13 +801,20 @@ __global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(SpmmArgs a0, Seg
   float sum[OPT];
   for (int k = 0; k < OPT; ++k) sum[k] = 0.f;
   for (int sp0 = 0; sp0 < splits; sp0 += 8) {
+    // up to 8 splits' loads in flight at once; none for splits past the last
     float v[8][OPT];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < 8; ++u) {
+      if (sp0 + u < splits) {
 #pragma unroll
-      for (int k = 0; k < OPT; ++k)
-        v[u][k] = __hip_atomic_load(p0 + min(sp0 + u, splits - 1) * plane + threadIdx.x + 256 * k, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
+        for (int k = 0; k < OPT; ++k)
+          v[u][k] = __hip_atomic_load(p0 + (sp0 + u) * plane + threadIdx.x + 256 * k, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+#pragma unroll
+        for (int k = 0; k < OPT; ++k) v[u][k] = 0.f;
+      }
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
 #pragma unroll
