@@ -1533,22 +1533,40 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a0, Segs segs,
         if (threadIdx.x == 0) s_last = arrive(ctr, splits);
         __syncthreads();
         if (!s_last) continue;
+        // per accumulator: up to SV splits' partials in flight at once,
+        // added in split order from zero
+        constexpr int SV = 4;
+        const int64_t sstride = (int64_t)n_items * 256 * NACC;
+#pragma unroll
         for (int r = 0; r < 2; ++r)
-          for (int j = 0; j < C::NTB; ++j)
-            for (int e = 0; e < 16; ++e) acc[r][j][e] = 0.f;
-        for (int sp = 0; sp < splits; ++sp) {
-          const float* ps = a.ws + ((int64_t)sp * n_items + item) * 256 * NACC + threadIdx.x;
-          for (int r = 0; r < 2; ++r)
-            for (int j = 0; j < C::NTB; ++j) {
-              float v[16];
 #pragma unroll
-              for (int e = 0; e < 16; ++e)
-                v[e] = __hip_atomic_load(ps + ((r * C::NTB + j) * 16 + e) * 256, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
+          for (int j = 0; j < C::NTB; ++j) {
+            const float* pg = a.ws + (int64_t)item * 256 * NACC + (r * C::NTB + j) * 16 * 256 + threadIdx.x;
+            float sum[16];
 #pragma unroll
-              for (int e = 0; e < 16; ++e) acc[r][j][e] += v[e];
+            for (int e = 0; e < 16; ++e) sum[e] = 0.f;
+            for (int sp0 = 0; sp0 < splits; sp0 += SV) {
+              float v[SV][16];
+#pragma unroll
+              for (int u = 0; u < SV; ++u) {
+                if (sp0 + u < splits) {
+#pragma unroll
+                  for (int e = 0; e < 16; ++e)
+                    v[u][e] = __hip_atomic_load(pg + (sp0 + u) * sstride + e * 256, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+                } else {
+#pragma unroll
+                  for (int e = 0; e < 16; ++e) v[u][e] = 0.f;
+                }
+              }
+#pragma unroll
+              for (int u = 0; u < SV; ++u)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) sum[e] = (sp0 + u < splits) ? sum[e] + v[u][e] : sum[e];
             }
-        }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[r][j][e] = sum[e];
+          }
       }
 
       // epilogue: acc[r][j][e] is row 32r + 8(e/4) + 4(lane/32) + e%4, token tok_w + 32j + lane%32.
