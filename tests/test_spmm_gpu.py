@@ -269,22 +269,23 @@ def test_spmm_decode_ragged_full_width(unaligned):
 
 
 def test_spmm_decode_small_batch_x_layouts_bit_identical():
-    """Batches of 1 to 7 tokens (one partial 8-token chunk per X row), X rows at every 2-byte alignment: a
-    contiguous X (odd row pitch at odd batches), odd and even row strides, and X starting 2 bytes past a
-    dword.  Chunks that start 2 bytes past a dword are loaded from the dword boundary and shifted back in
-    LDS; the product must be bit-identical to the same product from a copy of X with 16-byte rows (the
-    same kernel, adding the same terms in the same order), and within the bar of the oracle.  The last
-    input channel is kept in every tile, so the end of the X buffer is exercised too."""
+    """Batches of 1 to 63 tokens (every token-block width), X rows at every 2-byte alignment: a contiguous X
+    (odd row pitch at odd batches), odd and even row strides, and X starting 2 bytes past a dword.  At batch
+    1 every element is a 2-byte load; otherwise rows that are not 16-byte aligned take 16-byte loads from
+    2-byte-aligned addresses (the last row's partial chunk one token early).  The product must be
+    bit-identical to the same product from a copy of X with 64-token rows (the same kernel, adding the same
+    terms in the same order), and within the bar of the oracle.  The last input channel is kept in every
+    tile, so the end of the X buffer is exercised too."""
     w = synth.small(256, 1032, 64, 0.6, 0.35, 1, seed=31)
     w.importance[:, -1] = w.importance.max() * 4.0
     c = Case(w)
     cin = w.cin
-    for b in (1, 2, 3, 4, 5, 7):
+    for b in (1, 2, 3, 4, 5, 7, 9, 15, 17, 31, 33, 45, 63):
         g = torch.Generator().manual_seed(500 + b)
         x = torch.randn(cin, b, generator=g).to(torch.bfloat16)
-        ref16 = torch.zeros(cin, 16, dtype=torch.bfloat16, device=DEV)
-        ref16[:, :b] = x.to(DEV)
-        y_ref = hinm.spmm(c.pk, ref16[:, :b])
+        ref64 = torch.zeros(cin, 64, dtype=torch.bfloat16, device=DEV)
+        ref64[:, :b] = x.to(DEV)
+        y_ref = hinm.spmm(c.pk, ref64[:, :b])
         xf = synth.as_f64(x)
         for ldx in sorted({b, b + 1, b + 2, 2 * b + 1}):
             for shift in (0, 1):
