@@ -18,6 +18,10 @@ ARCH = "gfx950"
 # accumulators stay in ordinary VGPRs: with one wave per SIMD the compiler
 # would otherwise park them in AGPRs and copy them at every loop back edge.
 DEVICE_FLAGS = ("-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form=1")
+# The product kernels: leading scalar kernel arguments (up to nine) are
+# preloaded into SGPRs at wave launch, so the first loads of a decode launch
+# do not wait for the argument buffer.
+FILE_FLAGS = {"hinm_spmm.hip": ("-mllvm", "-amdgpu-kernarg-preload-count=9")}
 
 
 def _hipcc() -> str:
@@ -34,7 +38,7 @@ def build(verbose: bool = False) -> str:
     def compile_one(src: str) -> str:
         obj = os.path.join(objdir, src.rsplit(".", 1)[0] + ".o")
         cmd = [hipcc, "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
-               "-Wno-unused-function", *DEVICE_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
+               "-Wno-unused-function", *DEVICE_FLAGS, *FILE_FLAGS.get(src, ()), "-I", INCLUDE, "-I", CSRC, "-c",
                os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l

@@ -482,8 +482,17 @@ __device__ inline int xs_gran(int p, int g) {
   else return 4 * p + (g ^ (((p >> 1) & 1) | (((p >> 3) & 1) << 1)));
 }
 
-template <int NTOK, int MAXB, bool FAST, int NG, bool ONE = false>
-__global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(SpmmArgs a0, Segs segs, int splits, int n_tb,
+// The leading arguments (index lists, their block totals, per-tile counts,
+// the tile table, rows per tile, K splits) are the ones the first loads of a
+// one-weight launch depend on; being plain scalars, they are preloaded into
+// SGPRs at wave launch, so the index loads go out without waiting for the
+// argument buffer.  A group (GROUP) takes them from its segment table.
+template <int NTOK, int MAXB, bool FAST, int NG, bool ONE = false, bool GROUP = true>
+__global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(const int32_t* __restrict__ k_idx_d,
+                                                                const int32_t* __restrict__ k_idx_s,
+                                                                const int32_t* __restrict__ k_tiles, int k_kd_total,
+                                                                int k_ks_total, int k_nkb_d, int k_nkb_s, int k_rows,
+                                                                int splits, SpmmArgs a0, Segs segs, int n_tb,
                                                                 float* __restrict__ part,
                                                                 unsigned* __restrict__ counters) {
   constexpr int CPR = NTOK / 8;                // 16-byte chunks per X row
@@ -508,29 +517,40 @@ __global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(SpmmArgs a0, Seg
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool gather = wave >= 4;
   const int kc = lane >> 4, i16 = lane & 15;
-  const int nrb = a0.rows / 64;
+  const int nrb = k_rows / 64;
   const int split = blockIdx.x % splits;
   const int gtrb = blockIdx.x / splits;          // row block over all weights of a group
   SpmmArgs a = a0;
-  int trb0, row0;                                // this weight's first row block and partial-sum row
-  select_seg(segs, gtrb, a, trb0, row0);
+  int trb0 = 0, row0 = 0;                        // this weight's first row block and partial-sum row
+  if constexpr (GROUP) select_seg(segs, gtrb, a, trb0, row0);
   const int trb = gtrb - trb0;                   // tile * nrb + row block
   const int t = trb / nrb, rb = trb % nrb;
   const int tb = blockIdx.y;
   const int n0 = tb * NTOK;
   const int row = rb * 64 + (wave & 3) * 16 + (lane & 15);   // tile row of this lane's A fragment
-  const TileK tk = tile_k(a, t);
+  TileK tk;
+  if constexpr (GROUP) {
+    tk = tile_k(a, t);
+  } else if (k_tiles) {
+    tk = {k_tiles[4 * t], (k_tiles[4 * t + 1] + 31) / 32, k_tiles[4 * t + 2], (k_tiles[4 * t + 3] + 63) / 64};
+  } else {
+    tk = {t * k_nkb_d, k_nkb_d, t * k_nkb_s, k_nkb_s};
+  }
   const int nblk = tk.nbd + tk.nbs;
-  const int b_lo = (int)((int64_t)split * nblk / splits), b_hi = (int)((int64_t)(split + 1) * nblk / splits);
+  // 32-bit: at most 64 splits of at most 2^19 blocks
+  const int b_lo = split * nblk / splits, b_hi = (split + 1) * nblk / splits;
 
+  // The index resources come first; each role makes the others it uses
+  // inside its own branch, so that the gather waves' first loads wait for
+  // nothing but the preloaded arguments.
   BufRes res;
-  res.x = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, (int)(uint32_t)(((int64_t)(a.cin - 1) * a.ldx + a.batch) * 2), kBufferWord3);
-  res.vd = __builtin_amdgcn_make_buffer_rsrc((void*)a.val_d, (short)0, (int)((uint32_t)a.kd_total * a.rows * 64u), kBufferWord3);
-  res.vs = __builtin_amdgcn_make_buffer_rsrc((void*)a.val_s, (short)0, (int)((uint32_t)a.ks_total * a.rows * 64u), kBufferWord3);
-  res.meta = __builtin_amdgcn_make_buffer_rsrc((void*)a.meta, (short)0, (int)((uint32_t)a.ks_total * a.rows * 8u), kBufferWord3);
-  res.id = __builtin_amdgcn_make_buffer_rsrc((void*)a.idx_d, (short)0, (int)((uint32_t)a.kd_total * 32u * 4u), kBufferWord3);
-  res.is = __builtin_amdgcn_make_buffer_rsrc((void*)a.idx_s, (short)0, (int)((uint32_t)a.ks_total * 64u * 4u), kBufferWord3);
-  res.ldx_bytes = (uint32_t)a.ldx * 2u;
+  if constexpr (GROUP) {
+    res.id = __builtin_amdgcn_make_buffer_rsrc((void*)a.idx_d, (short)0, (int)((uint32_t)a.kd_total * 32u * 4u), kBufferWord3);
+    res.is = __builtin_amdgcn_make_buffer_rsrc((void*)a.idx_s, (short)0, (int)((uint32_t)a.ks_total * 64u * 4u), kBufferWord3);
+  } else {
+    res.id = __builtin_amdgcn_make_buffer_rsrc((void*)k_idx_d, (short)0, (int)((uint32_t)k_kd_total * 32u * 4u), kBufferWord3);
+    res.is = __builtin_amdgcn_make_buffer_rsrc((void*)k_idx_s, (short)0, (int)((uint32_t)k_ks_total * 64u * 4u), kBufferWord3);
+  }
 
   f32x4 acc[2][NB];
   for (int h = 0; h < 2; ++h)
@@ -539,8 +559,8 @@ __global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(SpmmArgs a0, Seg
   // end does not wait for them: rows grow0 + e (one split) or the rows of
   // the final reduction (several splits).
   constexpr int OPT = 64 * NTOK / 256;
-  const int64_t grow0 = (int64_t)t * a.rows + rb * 64 + (wave & 3) * 16 + 4 * kc;
-  const int64_t grow_base = (int64_t)t * a.rows + rb * 64;
+  const int64_t grow0 = (int64_t)t * k_rows + rb * 64 + (wave & 3) * 16 + 4 * kc;
+  const int64_t grow_base = (int64_t)t * k_rows + rb * 64;
   int64_t yrow[OPT > 4 ? OPT : 4];
   if (threadIdx.x < 256) {
     constexpr int NR = OPT > 4 ? OPT : 4;
@@ -563,6 +583,8 @@ __global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(SpmmArgs a0, Seg
   // barriers a round: X rows are in LDS; the row waves are done with them.
   const int nrounds = (b_hi - b_lo + MAXB - 1) / MAXB;
   if (gather) {
+    res.x = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, (int)(uint32_t)(((int64_t)(a.cin - 1) * a.ldx + a.batch) * 2), kBufferWord3);
+    res.ldx_bytes = (uint32_t)a.ldx * 2u;
     // Gather thread gt takes 16-byte chunk gt % CPR of LDS positions
     // gt / CPR + PPJ * j; position p is slot p % 64 of block p / 64, so the
     // block of step j is a compile-time constant and the dense / 2:4 choice
@@ -699,6 +721,9 @@ __global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(SpmmArgs a0, Seg
   } else {
     // Each role holds its own barriers (the condition is uniform per wave),
     // so the two roles keep disjoint register sets.
+    res.vd = __builtin_amdgcn_make_buffer_rsrc((void*)a.val_d, (short)0, (int)((uint32_t)a.kd_total * a.rows * 64u), kBufferWord3);
+    res.vs = __builtin_amdgcn_make_buffer_rsrc((void*)a.val_s, (short)0, (int)((uint32_t)a.ks_total * a.rows * 64u), kBufferWord3);
+    res.meta = __builtin_amdgcn_make_buffer_rsrc((void*)a.meta, (short)0, (int)((uint32_t)a.ks_total * a.rows * 8u), kBufferWord3);
     u32x4 av[MAXB];
     uint64_t mv[MAXB];
     // Loads of block r0 + j into slot j; a block past this split's range
@@ -1761,15 +1786,31 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
     // 16 tokens: 24 blocks a round (48 KB of LDS), 2 gather waves; 32 and
     // 64 tokens: 96 KB rounds (24 / 12 blocks) with 4 gather waves.
     const dim3 grid(p.n_tiles * (p.tile_rows / 64) * sh.splits, sh.n_tblocks), b6(384), b8(512);
+    // the arguments the first loads depend on, preloaded into SGPRs (a group
+    // takes them from its segment table)
+    const int32_t* kid = a.idx_d;
+    const int32_t* kis = a.idx_s;
+    const int32_t* ktl = a.tiles;
+    const int kdt = a.kd_total, kst = a.ks_total, knd = a.nkb_d, kns = a.nkb_s, krw = a.rows, ksp = sh.splits;
+#define HINM_DECODE5(NT_, MB_, F_, NG_, ONE_, BLK_)                                                                   \
+  do {                                                                                                              \
+    if (segs)                                                                                                       \
+      hipLaunchKernelGGL((decode5_kernel<NT_, MB_, F_, NG_, ONE_, true>), grid, BLK_, 0, stream, kid, kis, ktl, kdt, \
+                         kst, knd, kns, krw, ksp, a, sg, sh.n_tblocks, part, counters);                             \
+    else                                                                                                            \
+      hipLaunchKernelGGL((decode5_kernel<NT_, MB_, F_, NG_, ONE_, false>), grid, BLK_, 0, stream, kid, kis, ktl,     \
+                         kdt, kst, knd, kns, krw, ksp, a, sg, sh.n_tblocks, part, counters);                        \
+  } while (0)
     switch (batch == 1 ? 1 : sh.nt * 2 + (fast ? 1 : 0)) {
-      case 1: hipLaunchKernelGGL((decode5_kernel<16, 24, false, 2, true>), grid, b6, 0, stream, a, sg, sh.splits, sh.n_tblocks, part, counters); break;
-      case 33: hipLaunchKernelGGL((decode5_kernel<16, 24, true, 2>), grid, b6, 0, stream, a, sg, sh.splits, sh.n_tblocks, part, counters); break;
-      case 32: hipLaunchKernelGGL((decode5_kernel<16, 24, false, 2>), grid, b6, 0, stream, a, sg, sh.splits, sh.n_tblocks, part, counters); break;
-      case 65: hipLaunchKernelGGL((decode5_kernel<32, 24, true, 4>), grid, b8, 0, stream, a, sg, sh.splits, sh.n_tblocks, part, counters); break;
-      case 64: hipLaunchKernelGGL((decode5_kernel<32, 24, false, 4>), grid, b8, 0, stream, a, sg, sh.splits, sh.n_tblocks, part, counters); break;
-      case 129: hipLaunchKernelGGL((decode5_kernel<64, 12, true, 4>), grid, b8, 0, stream, a, sg, sh.splits, sh.n_tblocks, part, counters); break;
-      default: hipLaunchKernelGGL((decode5_kernel<64, 12, false, 4>), grid, b8, 0, stream, a, sg, sh.splits, sh.n_tblocks, part, counters); break;
+      case 1: HINM_DECODE5(16, 24, false, 2, true, b6); break;
+      case 33: HINM_DECODE5(16, 24, true, 2, false, b6); break;
+      case 32: HINM_DECODE5(16, 24, false, 2, false, b6); break;
+      case 65: HINM_DECODE5(32, 24, true, 4, false, b8); break;
+      case 64: HINM_DECODE5(32, 24, false, 4, false, b8); break;
+      case 129: HINM_DECODE5(64, 12, true, 4, false, b8); break;
+      default: HINM_DECODE5(64, 12, false, 4, false, b8); break;
     }
+#undef HINM_DECODE5
   } else if (sh.path == hinm::kPathDecode) {
     const dim3 grid(p.n_tiles * (p.tile_rows / 16), sh.n_tblocks), block(kDecWaves * 64);
     const bool fast = a.x_vec && (batch % sh.nt == 0);
