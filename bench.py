@@ -783,7 +783,7 @@ def main():
                    "roofline": {"bound": "hbm", "achieved": round(gbs_d, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": round(gbs_d / HBM_PEAK_GBS, 4), "traffic": measured_traffic(Bd),
                                 "frac_of_measured_read_peak": round(gbs_d / peaks["read_1gib_gbs"], 4),
-                                "kernel": "decode5_kernel<16,24,true,2,false,false> (one launch per call)"},
+                                "kernel": "decode5_kernel<16,24,true,2,false> (one launch per call)"},
                    "useful_tflops": round(algd["useful_flops"] / (rd["ms_step"] * 1e-3) / 1e12, 3)},
         "batch_2048_hbm_gbs": round(alg["bytes"] / (ms * 1e-3) / 1e9, 1),
         "pack_ms": [round(v, 2) for v in pack_ms],

@@ -19,6 +19,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <climits>
 #include <mutex>
 #include <type_traits>
 
@@ -86,14 +87,10 @@ struct Segs {
   Seg s[kMaxSeg];
 };
 
-// The weight of concatenated row block gtrb: patches a's per-weight fields and
-// returns the first row block and row of that weight.
-__device__ inline void select_seg(const Segs& segs, int gtrb, SpmmArgs& a, int& trb0, int& row0) {
-  trb0 = 0;
-  row0 = 0;
-  if (segs.n <= 1) return;
-  int g = 0;
-  for (int k = 1; k < segs.n; ++k) g = gtrb >= segs.s[k].trb0 ? k : g;
+// Weight g of a group: patches a's per-weight fields and returns the first
+// row block and row of that weight.  select_seg finds the weight of
+// concatenated row block gtrb by a scan of the table.
+__device__ inline void seg_fields(const Segs& segs, int g, SpmmArgs& a, int& trb0, int& row0) {
   const Seg& S = segs.s[g];
   a.val_d = S.val_d;
   a.idx_d = S.idx_d;
@@ -110,6 +107,14 @@ __device__ inline void select_seg(const Segs& segs, int gtrb, SpmmArgs& a, int& 
   a.ks_total = S.ks_total;
   trb0 = S.trb0;
   row0 = S.row0;
+}
+__device__ inline void select_seg(const Segs& segs, int gtrb, SpmmArgs& a, int& trb0, int& row0) {
+  trb0 = 0;
+  row0 = 0;
+  if (segs.n <= 1) return;
+  int g = 0;
+  for (int k = 1; k < segs.n; ++k) g = gtrb >= segs.s[k].trb0 ? k : g;
+  seg_fields(segs, g, a, trb0, row0);
 }
 
 // Tile t's K-blocks: first dense block and count, first 2:4 block and count.
@@ -482,19 +487,15 @@ __device__ inline int xs_gran(int p, int g) {
   else return 4 * p + (g ^ (((p >> 1) & 1) | (((p >> 3) & 1) << 1)));
 }
 
-// The leading arguments (index lists, their block totals, per-tile counts,
-// the tile table, rows per tile, K splits) are the ones the first loads of a
-// one-weight launch depend on; being plain scalars, they are preloaded into
-// SGPRs at wave launch, so the index loads go out without waiting for the
-// argument buffer.  A group (GROUP) takes them from its segment table.
-template <int NTOK, int MAXB, bool FAST, int NG, bool ONE = false, bool GROUP = true>
-__global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(const int32_t* __restrict__ k_idx_d,
-                                                                const int32_t* __restrict__ k_idx_s,
-                                                                const int32_t* __restrict__ k_tiles, int k_kd_total,
-                                                                int k_ks_total, int k_nkb_d, int k_nkb_s, int k_rows,
-                                                                int splits, SpmmArgs a0, Segs segs, int n_tb,
-                                                                float* __restrict__ part,
-                                                                unsigned* __restrict__ counters) {
+// The split decode's body, shared by its one-weight and group kernels
+// below.  k_* are the arguments its first loads depend on (index lists,
+// their block totals, per-tile counts, the tile table) for one weight; a
+// group (GROUP) takes them from weight k_seg of its segment table instead.
+template <int NTOK, int MAXB, bool FAST, int NG, bool ONE, bool GROUP>
+__device__ __attribute__((always_inline)) inline void decode5_body(
+    const int32_t* __restrict__ k_idx_d, const int32_t* __restrict__ k_idx_s, const int32_t* __restrict__ k_tiles,
+    int k_kd_total, int k_ks_total, int k_nkb_d, int k_nkb_s, int k_rows, int splits, int k_seg, const SpmmArgs& a0,
+    const Segs* segs, int n_tb, float* __restrict__ part, unsigned* __restrict__ counters) {
   constexpr int CPR = NTOK / 8;                // 16-byte chunks per X row
   constexpr int MAXP = MAXB * 64;              // LDS positions per round
   constexpr int GT = 64 * NG;                  // gather threads (NG gather waves)
@@ -522,7 +523,7 @@ __global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(const int32_t* _
   const int gtrb = blockIdx.x / splits;          // row block over all weights of a group
   SpmmArgs a = a0;
   int trb0 = 0, row0 = 0;                        // this weight's first row block and partial-sum row
-  if constexpr (GROUP) select_seg(segs, gtrb, a, trb0, row0);
+  if constexpr (GROUP) seg_fields(*segs, k_seg, a, trb0, row0);
   const int trb = gtrb - trb0;                   // tile * nrb + row block
   const int t = trb / nrb, rb = trb % nrb;
   const int tb = blockIdx.y;
@@ -850,6 +851,70 @@ __global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(const int32_t* _
     const int n = o % NTOK;
     if (n0 + n < a.batch && yrow[k] >= 0) a.y[yrow[k] * a.ldy + n0 + n] = bf16_rne(sum[k]);
   }
+}
+
+// The rest of a one-weight split decode's arguments: only fields its body
+// reads, so that no argument-buffer load brings in a word the kernel does
+// not use (the compiler reuses such a word's register at once, and must
+// then wait for the load in flight before the first index loads).
+struct DecArgs {
+  const uint16_t* val_d;
+  const uint16_t* val_s;
+  const uint64_t* meta;
+  const uint16_t* x;
+  uint16_t* y;
+  const int32_t* out_rows;
+  int64_t ldy;
+  int ldx;                   // below 2^23 on this path
+  int batch, cin, cout, part_rows, n_tb;
+};
+
+// One weight.  The leading arguments are plain scalars, preloaded into SGPRs
+// at wave launch, so the index loads go out without waiting for the
+// argument buffer.
+template <int NTOK, int MAXB, bool FAST, int NG, bool ONE = false>
+__global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(const int32_t* __restrict__ k_idx_d,
+                                                                const int32_t* __restrict__ k_idx_s,
+                                                                const int32_t* __restrict__ k_tiles, int k_kd_total,
+                                                                int k_ks_total, int k_nkb_d, int k_nkb_s, int k_rows,
+                                                                int splits, DecArgs d, float* __restrict__ part,
+                                                                unsigned* __restrict__ counters) {
+  SpmmArgs a0{};
+  a0.val_d = d.val_d;
+  a0.val_s = d.val_s;
+  a0.meta = d.meta;
+  a0.x = d.x;
+  a0.y = d.y;
+  a0.out_rows = d.out_rows;
+  a0.ldx = d.ldx;
+  a0.ldy = d.ldy;
+  a0.batch = d.batch;
+  a0.cin = d.cin;
+  a0.cout = d.cout;
+  a0.part_rows = d.part_rows;
+  a0.rows = k_rows;
+  a0.kd_total = k_kd_total;
+  a0.ks_total = k_ks_total;
+  decode5_body<NTOK, MAXB, FAST, NG, ONE, false>(k_idx_d, k_idx_s, k_tiles, k_kd_total, k_ks_total, k_nkb_d, k_nkb_s,
+                                                 k_rows, splits, 0, a0, nullptr, d.n_tb, part, counters);
+}
+
+// A group of up to 8 weights.  b1..b7 are the first concatenated row blocks
+// of weights 1..7 (INT_MAX past the last weight), preloaded like the
+// one-weight kernel's leading arguments, so a workgroup finds its weight
+// without reading the segment table and then reads that weight's fields in
+// one round trip.
+template <int NTOK, int MAXB, bool FAST, int NG, bool ONE = false>
+__global__ __launch_bounds__(256 + 64 * NG) void decode5_group_kernel(int k_rows, int splits, int b1, int b2, int b3,
+                                                                      int b4, int b5, int b6, int b7, SpmmArgs a0,
+                                                                      Segs segs, int n_tb, float* __restrict__ part,
+                                                                      unsigned* __restrict__ counters) {
+  static_assert(kMaxSeg == 8, "seven boundaries");
+  const int gtrb = blockIdx.x / splits;
+  const int g = (gtrb >= b1) + (gtrb >= b2) + (gtrb >= b3) + (gtrb >= b4) + (gtrb >= b5) + (gtrb >= b6) +
+                (gtrb >= b7);
+  decode5_body<NTOK, MAXB, FAST, NG, ONE, true>(nullptr, nullptr, nullptr, 0, 0, 0, 0, k_rows, splits, g, a0, &segs,
+                                                n_tb, part, counters);
 }
 
 // ---------------------------------------------------------------------------
@@ -1787,19 +1852,24 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
     // 64 tokens: 96 KB rounds (24 / 12 blocks) with 4 gather waves.
     const dim3 grid(p.n_tiles * (p.tile_rows / 64) * sh.splits, sh.n_tblocks), b6(384), b8(512);
     // the arguments the first loads depend on, preloaded into SGPRs (a group
-    // takes them from its segment table)
+    // takes them from its segment table, and preloads its weight boundaries)
     const int32_t* kid = a.idx_d;
     const int32_t* kis = a.idx_s;
     const int32_t* ktl = a.tiles;
     const int kdt = a.kd_total, kst = a.ks_total, knd = a.nkb_d, kns = a.nkb_s, krw = a.rows, ksp = sh.splits;
+    // a group's weight boundaries in concatenated row blocks, INT_MAX past the last weight
+    int gb[kMaxSeg];
+    for (int g = 0; g < kMaxSeg; ++g) gb[g] = segs && g < sg.n ? sg.s[g].trb0 : INT_MAX;
+    const DecArgs da{a.val_d, a.val_s, a.meta, a.x, a.y, a.out_rows, a.ldy, (int)a.ldx, a.batch, a.cin, a.cout,
+                     a.part_rows, sh.n_tblocks};
 #define HINM_DECODE5(NT_, MB_, F_, NG_, ONE_, BLK_)                                                                   \
   do {                                                                                                              \
     if (segs)                                                                                                       \
-      hipLaunchKernelGGL((decode5_kernel<NT_, MB_, F_, NG_, ONE_, true>), grid, BLK_, 0, stream, kid, kis, ktl, kdt, \
-                         kst, knd, kns, krw, ksp, a, sg, sh.n_tblocks, part, counters);                             \
+      hipLaunchKernelGGL((decode5_group_kernel<NT_, MB_, F_, NG_, ONE_>), grid, BLK_, 0, stream, krw, ksp, gb[1],    \
+                         gb[2], gb[3], gb[4], gb[5], gb[6], gb[7], a, sg, sh.n_tblocks, part, counters);            \
     else                                                                                                            \
-      hipLaunchKernelGGL((decode5_kernel<NT_, MB_, F_, NG_, ONE_, false>), grid, BLK_, 0, stream, kid, kis, ktl,     \
-                         kdt, kst, knd, kns, krw, ksp, a, sg, sh.n_tblocks, part, counters);                        \
+      hipLaunchKernelGGL((decode5_kernel<NT_, MB_, F_, NG_, ONE_>), grid, BLK_, 0, stream, kid, kis, ktl, kdt, kst, \
+                         knd, kns, krw, ksp, da, part, counters);                                                  \
   } while (0)
     switch (batch == 1 ? 1 : sh.nt * 2 + (fast ? 1 : 0)) {
       case 1: HINM_DECODE5(16, 24, false, 2, true, b6); break;
