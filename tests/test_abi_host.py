@@ -382,3 +382,17 @@ def test_group_host_errors(lib):
     assert lib.hinm_spmm_group(2, arr(k1, k2), fake, 0, 0, ys, (ctypes.c_int64 * 2)(0, 0), None, 0, None) == 0
     bad = hinm.PackedT(p2.raw, fake, None, fake, fake, fake)
     assert lib.hinm_spmm_group(2, arr(k1, bad), fake, 16, 16, ys, ldy, None, 0, None) == 1
+
+
+def test_group_size_limits(lib):
+    """hinm_spmm_group takes 1 to 8 weights; other counts fail on the host before any launch."""
+    p = hinm.plan(4096, 4096, 64, 0.5, 0.25)
+    pks = [_fake_packed(p) for _ in range(9)]
+    ptrs = (ctypes.c_void_p * 9)(*[ctypes.addressof(k) for k in pks])
+    ys = (ctypes.c_void_p * 9)(*([1 << 20] * 9))
+    ldys = (ctypes.c_int64 * 9)(*([16] * 9))
+    for n in (0, 9, -1):
+        assert lib.hinm_spmm_group(n, ptrs, 1 << 20, 16, 16, ys, ldys, None, 0, None) == 1
+        assert "weights" in lib.hinm_last_error().decode()
+    with pytest.raises(ValueError):
+        hinm.Group([object()] * 9)

@@ -76,3 +76,12 @@ def test_group_32_row_tiles_run_one_launch_each():
     ys = hinm.spmm_group(grp, x)
     for pk, y in zip(pks, ys):
         assert torch.equal(y.view(torch.int16), hinm.spmm(pk, x).view(torch.int16))
+
+
+def test_group_of_eight_weights():
+    """The largest group (8 weights, so every weight boundary of the split decode is a real one), rows
+    and regions differing per weight, at split-decode and prefill batches."""
+    shapes = [(64, 0.75, 0.55), (128, 0.5, 0.25), (192, 0.6, 0.6), (64, 0.8, 0.7), (256, 0.75, 0.5),
+              (128, 0.5, 0.5), (320, 0.7, 0.45), (64, 0.55, 0.3)]
+    ws = [synth.small(rows, 1024, 64, t, v, 1, seed=40 + i) for i, (rows, t, v) in enumerate(shapes)]
+    _check_group(ws, (1, 5, 16, 40, 64, 200), "eight")
