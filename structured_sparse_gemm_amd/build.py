@@ -21,7 +21,7 @@ DEVICE_FLAGS = ("-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-m
 # The product kernels: leading scalar kernel arguments (up to nine) are
 # preloaded into SGPRs at wave launch, so the first loads of a decode launch
 # do not wait for the argument buffer.
-FILE_FLAGS = {"hinm_spmm.hip": ("-mllvm", "-amdgpu-kernarg-preload-count=9")}
+FILE_FLAGS = {"hinm_spmm.hip": ("-mllvm", "-amdgpu-kernarg-preload-count=10")}
 
 
 def _hipcc() -> str:

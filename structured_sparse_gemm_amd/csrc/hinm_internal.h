@@ -42,6 +42,7 @@ struct SpmmShape {
   int n_rblocks;   // 64-row blocks per tile
   int n_kunits;    // K work units per tile (dense block = 1, 2:4 block = 2)
   int splits;      // K splits (>= 1)
+  int64_t split_rows;  // split decode: row blocks with `splits` workgroups; the rest have 2 x splits
   int64_t ws_counter_bytes;  // arrival counters at the start of the workspace (split decode)
   int64_t ws_bytes;
 };

@@ -257,6 +257,7 @@ SpmmShape spmm_shape(const hinm_plan_t* p, int64_t batch) {
   s.n_rblocks = (p->tile_rows + 63) / 64;
   s.n_kunits = p->n_dense_pad / HINM_KB_DENSE + 2 * (p->n_24_pad / HINM_KB_24);
   s.splits = 1;
+  s.split_rows = 0;
   s.ws_bytes = 0;
   s.ws_counter_bytes = 0;
   if (batch <= 64) {
@@ -273,9 +274,23 @@ SpmmShape spmm_shape(const hinm_plan_t* p, int64_t batch) {
       if (base <= kWsCounters)
         while (splits < 64 && base * splits * 2 <= target && nblk / (splits * 2) >= 4) splits *= 2;
       s.splits = splits;
-      if (splits > 1) {
+      s.split_rows = (int64_t)p->n_tiles * (p->tile_rows / 64);
+      // At 16 tokens two workgroups share a compute unit, so 512 run at
+      // once.  When base x splits workgroups leave some units with two
+      // whole ranges and others with one (gate and up together: 344 row
+      // blocks), the last row blocks take twice the splits, so that exactly
+      // 512 run: the first slots hold the whole ranges, the second slots
+      // the halves, and no unit holds more than one and a half ranges.
+      const int64_t slots = 512;
+      int splits_hi = splits;
+      if (s.nt == 16 && s.n_tblocks == 1 && option(HINM_OPT_DECODE_WGS) == 256 && base * splits < slots &&
+          base * splits * 2 > slots && slots % splits == 0 && nblk / (splits * 2) >= 4 && base <= kWsCounters) {
+        s.split_rows = 2 * base - slots / splits;
+        splits_hi = 2 * splits;
+      }
+      if (splits_hi > 1) {
         s.ws_counter_bytes = kWsCounterBytes;
-        s.ws_bytes = kWsCounterBytes + (int64_t)splits * s.n_tblocks * p->cout * s.nt * 4;
+        s.ws_bytes = kWsCounterBytes + (int64_t)splits_hi * s.n_tblocks * p->cout * s.nt * 4;
       }
       return s;
     }

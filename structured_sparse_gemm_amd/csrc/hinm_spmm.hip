@@ -487,6 +487,19 @@ __device__ inline int xs_gran(int p, int g) {
   else return 4 * p + (g ^ (((p >> 1) & 1) | (((p >> 3) & 1) << 1)));
 }
 
+// Workgroup bid of a split decode -> its row block, K split and the number
+// of splits of that row block: the first r1 row blocks have `splits`
+// workgroups each, the others twice as many.
+struct WgSplit {
+  int gtrb, split, nsp;
+};
+__device__ inline WgSplit wg_split(int bid, int splits, int r1) {
+  const int nlo = r1 * splits;
+  if (bid < nlo) return {bid / splits, bid % splits, splits};
+  const int q = bid - nlo, n2 = 2 * splits;
+  return {r1 + q / n2, q % n2, n2};
+}
+
 // The split decode's body, shared by its one-weight and group kernels
 // below.  k_* are the arguments its first loads depend on (index lists,
 // their block totals, per-tile counts, the tile table) for one weight; a
@@ -494,7 +507,8 @@ __device__ inline int xs_gran(int p, int g) {
 template <int NTOK, int MAXB, bool FAST, int NG, bool ONE, bool GROUP>
 __device__ __attribute__((always_inline)) inline void decode5_body(
     const int32_t* __restrict__ k_idx_d, const int32_t* __restrict__ k_idx_s, const int32_t* __restrict__ k_tiles,
-    int k_kd_total, int k_ks_total, int k_nkb_d, int k_nkb_s, int k_rows, int splits, int k_seg, const SpmmArgs& a0,
+    int k_kd_total, int k_ks_total, int k_nkb_d, int k_nkb_s, int k_rows, int k_splits, int k_r1, int k_seg,
+    const SpmmArgs& a0,
     const Segs* segs, int n_tb, float* __restrict__ part, unsigned* __restrict__ counters) {
   constexpr int CPR = NTOK / 8;                // 16-byte chunks per X row
   constexpr int MAXP = MAXB * 64;              // LDS positions per round
@@ -519,8 +533,10 @@ __device__ __attribute__((always_inline)) inline void decode5_body(
   const bool gather = wave >= 4;
   const int kc = lane >> 4, i16 = lane & 15;
   const int nrb = k_rows / 64;
-  const int split = blockIdx.x % splits;
-  const int gtrb = blockIdx.x / splits;          // row block over all weights of a group
+  const WgSplit ws = wg_split(blockIdx.x, k_splits, k_r1);
+  const int split = ws.split;
+  const int splits = ws.nsp;                     // K splits of this row block
+  const int gtrb = ws.gtrb;                      // row block over all weights of a group
   SpmmArgs a = a0;
   int trb0 = 0, row0 = 0;                        // this weight's first row block and partial-sum row
   if constexpr (GROUP) seg_fields(*segs, k_seg, a, trb0, row0);
@@ -877,7 +893,8 @@ __global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(const int32_t* _
                                                                 const int32_t* __restrict__ k_idx_s,
                                                                 const int32_t* __restrict__ k_tiles, int k_kd_total,
                                                                 int k_ks_total, int k_nkb_d, int k_nkb_s, int k_rows,
-                                                                int splits, DecArgs d, float* __restrict__ part,
+                                                                int splits, int k_r1, DecArgs d,
+                                                                float* __restrict__ part,
                                                                 unsigned* __restrict__ counters) {
   SpmmArgs a0{};
   a0.val_d = d.val_d;
@@ -896,7 +913,7 @@ __global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(const int32_t* _
   a0.kd_total = k_kd_total;
   a0.ks_total = k_ks_total;
   decode5_body<NTOK, MAXB, FAST, NG, ONE, false>(k_idx_d, k_idx_s, k_tiles, k_kd_total, k_ks_total, k_nkb_d, k_nkb_s,
-                                                 k_rows, splits, 0, a0, nullptr, d.n_tb, part, counters);
+                                                 k_rows, splits, k_r1, 0, a0, nullptr, d.n_tb, part, counters);
 }
 
 // A group of up to 8 weights.  b1..b7 are the first concatenated row blocks
@@ -905,15 +922,16 @@ __global__ __launch_bounds__(256 + 64 * NG) void decode5_kernel(const int32_t* _
 // without reading the segment table and then reads that weight's fields in
 // one round trip.
 template <int NTOK, int MAXB, bool FAST, int NG, bool ONE = false>
-__global__ __launch_bounds__(256 + 64 * NG) void decode5_group_kernel(int k_rows, int splits, int b1, int b2, int b3,
-                                                                      int b4, int b5, int b6, int b7, SpmmArgs a0,
-                                                                      Segs segs, int n_tb, float* __restrict__ part,
+__global__ __launch_bounds__(256 + 64 * NG) void decode5_group_kernel(int k_rows, int splits, int k_r1, int b1, int b2,
+                                                                      int b3, int b4, int b5, int b6, int b7,
+                                                                      SpmmArgs a0, Segs segs, int n_tb,
+                                                                      float* __restrict__ part,
                                                                       unsigned* __restrict__ counters) {
   static_assert(kMaxSeg == 8, "seven boundaries");
-  const int gtrb = blockIdx.x / splits;
+  const int gtrb = wg_split(blockIdx.x, splits, k_r1).gtrb;
   const int g = (gtrb >= b1) + (gtrb >= b2) + (gtrb >= b3) + (gtrb >= b4) + (gtrb >= b5) + (gtrb >= b6) +
                 (gtrb >= b7);
-  decode5_body<NTOK, MAXB, FAST, NG, ONE, true>(nullptr, nullptr, nullptr, 0, 0, 0, 0, k_rows, splits, g, a0, &segs,
+  decode5_body<NTOK, MAXB, FAST, NG, ONE, true>(nullptr, nullptr, nullptr, 0, 0, 0, 0, k_rows, splits, k_r1, g, a0, &segs,
                                                 n_tb, part, counters);
 }
 
@@ -1850,13 +1868,17 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
     float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + sh.ws_counter_bytes);
     // 16 tokens: 24 blocks a round (48 KB of LDS), 2 gather waves; 32 and
     // 64 tokens: 96 KB rounds (24 / 12 blocks) with 4 gather waves.
-    const dim3 grid(p.n_tiles * (p.tile_rows / 64) * sh.splits, sh.n_tblocks), b6(384), b8(512);
+    // the first split_rows row blocks take sh.splits workgroups, the rest twice as many
+    const int64_t nrb_all = (int64_t)p.n_tiles * (p.tile_rows / 64);
+    const dim3 grid((unsigned)(sh.split_rows * sh.splits + (nrb_all - sh.split_rows) * 2 * sh.splits), sh.n_tblocks),
+        b6(384), b8(512);
     // the arguments the first loads depend on, preloaded into SGPRs (a group
     // takes them from its segment table, and preloads its weight boundaries)
     const int32_t* kid = a.idx_d;
     const int32_t* kis = a.idx_s;
     const int32_t* ktl = a.tiles;
     const int kdt = a.kd_total, kst = a.ks_total, knd = a.nkb_d, kns = a.nkb_s, krw = a.rows, ksp = sh.splits;
+    const int kr1 = (int)sh.split_rows;
     // a group's weight boundaries in concatenated row blocks, INT_MAX past the last weight
     int gb[kMaxSeg];
     for (int g = 0; g < kMaxSeg; ++g) gb[g] = segs && g < sg.n ? sg.s[g].trb0 : INT_MAX;
@@ -1865,11 +1887,11 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
 #define HINM_DECODE5(NT_, MB_, F_, NG_, ONE_, BLK_)                                                                   \
   do {                                                                                                              \
     if (segs)                                                                                                       \
-      hipLaunchKernelGGL((decode5_group_kernel<NT_, MB_, F_, NG_, ONE_>), grid, BLK_, 0, stream, krw, ksp, gb[1],    \
-                         gb[2], gb[3], gb[4], gb[5], gb[6], gb[7], a, sg, sh.n_tblocks, part, counters);            \
+      hipLaunchKernelGGL((decode5_group_kernel<NT_, MB_, F_, NG_, ONE_>), grid, BLK_, 0, stream, krw, ksp, kr1,      \
+                         gb[1], gb[2], gb[3], gb[4], gb[5], gb[6], gb[7], a, sg, sh.n_tblocks, part, counters);     \
     else                                                                                                            \
       hipLaunchKernelGGL((decode5_kernel<NT_, MB_, F_, NG_, ONE_>), grid, BLK_, 0, stream, kid, kis, ktl, kdt, kst, \
-                         knd, kns, krw, ksp, da, part, counters);                                                  \
+                         knd, kns, krw, ksp, kr1, da, part, counters);                                             \
   } while (0)
     switch (batch == 1 ? 1 : sh.nt * 2 + (fast ? 1 : 0)) {
       case 1: HINM_DECODE5(16, 24, false, 2, true, b6); break;
