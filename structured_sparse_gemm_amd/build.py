@@ -18,7 +18,7 @@ ARCH = "gfx950"
 # accumulators stay in ordinary VGPRs: with one wave per SIMD the compiler
 # would otherwise park them in AGPRs and copy them at every loop back edge.
 DEVICE_FLAGS = ("-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form=1")
-# The product kernels: leading scalar kernel arguments (up to nine) are
+# The product kernels: leading scalar kernel arguments (up to ten) are
 # preloaded into SGPRs at wave launch, so the first loads of a decode launch
 # do not wait for the argument buffer.
 FILE_FLAGS = {"hinm_spmm.hip": ("-mllvm", "-amdgpu-kernarg-preload-count=10")}
