@@ -258,6 +258,7 @@ SpmmShape spmm_shape(const hinm_plan_t* p, int64_t batch) {
   s.n_kunits = p->n_dense_pad / HINM_KB_DENSE + 2 * (p->n_24_pad / HINM_KB_24);
   s.splits = 1;
   s.split_rows = 0;
+  s.two_per_cu = false;
   s.ws_bytes = 0;
   s.ws_counter_bytes = 0;
   if (batch <= 64) {
@@ -276,14 +277,17 @@ SpmmShape spmm_shape(const hinm_plan_t* p, int64_t batch) {
       s.splits = splits;
       s.split_rows = (int64_t)p->n_tiles * (p->tile_rows / 64);
       // At 16 tokens two workgroups share a compute unit, so 512 run at
-      // once.  When base x splits workgroups leave some units with two
-      // whole ranges and others with one (gate and up together: 344 row
-      // blocks), the last row blocks take twice the splits, so that exactly
-      // 512 run: the first slots hold the whole ranges, the second slots
-      // the halves, and no unit holds more than one and a half ranges.
+      // once; at 32 tokens too when the launch has more than 256 (the
+      // kernel then takes smaller rounds).  When base x splits workgroups
+      // leave some units with two whole ranges and others with one (gate
+      // and up together: 344 row blocks), the last row blocks take twice
+      // the splits, so that exactly 512 run: the first slots hold the whole
+      // ranges, the second slots the halves, and no unit holds more than
+      // one and a half ranges.
+      s.two_per_cu = s.nt == 16 || (s.nt == 32 && base * splits > 256);
       const int64_t slots = 512;
       int splits_hi = splits;
-      if (s.nt == 16 && s.n_tblocks == 1 && option(HINM_OPT_DECODE_WGS) == 256 && base * splits < slots &&
+      if (s.two_per_cu && s.n_tblocks == 1 && option(HINM_OPT_DECODE_WGS) == 256 && base * splits < slots &&
           base * splits * 2 > slots && slots % splits == 0 && nblk / (splits * 2) >= 4 && base <= kWsCounters) {
         s.split_rows = 2 * base - slots / splits;
         splits_hi = 2 * splits;

@@ -1893,12 +1893,20 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
       hipLaunchKernelGGL((decode5_kernel<NT_, MB_, F_, NG_, ONE_>), grid, BLK_, 0, stream, kid, kis, ktl, kdt, kst, \
                          knd, kns, krw, ksp, kr1, da, part, counters);                                             \
   } while (0)
-    switch (batch == 1 ? 1 : sh.nt * 2 + (fast ? 1 : 0)) {
+    // 32 and 64 tokens: 96 KB rounds and four gather waves (one workgroup
+    // per compute unit); at 32 tokens, when a launch has more workgroups
+    // than compute units, 48 KB rounds and two gather waves instead (130
+    // VGPRs), so that two workgroups share a unit and all of them run at
+    // once.
+    const int key = batch == 1 ? 1 : sh.nt * 2 + (fast ? 1 : 0) + (sh.nt > 16 && sh.two_per_cu ? 1000 : 0);
+    switch (key) {
       case 1: HINM_DECODE5(16, 24, false, 2, true, b6); break;
       case 33: HINM_DECODE5(16, 24, true, 2, false, b6); break;
       case 32: HINM_DECODE5(16, 24, false, 2, false, b6); break;
       case 65: HINM_DECODE5(32, 24, true, 4, false, b8); break;
       case 64: HINM_DECODE5(32, 24, false, 4, false, b8); break;
+      case 1065: HINM_DECODE5(32, 12, true, 2, false, b6); break;
+      case 1064: HINM_DECODE5(32, 12, false, 2, false, b6); break;
       case 129: HINM_DECODE5(64, 12, true, 4, false, b8); break;
       default: HINM_DECODE5(64, 12, false, 4, false, b8); break;
     }
