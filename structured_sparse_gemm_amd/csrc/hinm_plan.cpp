@@ -283,11 +283,13 @@ SpmmShape spmm_shape(const hinm_plan_t* p, int64_t batch) {
       // and up together: 344 row blocks), the last row blocks take twice
       // the splits, so that exactly 512 run: the first slots hold the whole
       // ranges, the second slots the halves, and no unit holds more than
-      // one and a half ranges.
+      // one and a half ranges.  At 64 tokens (one workgroup per unit) the
+      // same split turns the second round of whole ranges into halves that
+      // start as the first round's halves finish.
       s.two_per_cu = s.nt == 16 || (s.nt == 32 && base * splits > 256);
       const int64_t slots = 512;
       int splits_hi = splits;
-      if (s.two_per_cu && s.n_tblocks == 1 && option(HINM_OPT_DECODE_WGS) == 256 && base * splits < slots &&
+      if (s.n_tblocks == 1 && option(HINM_OPT_DECODE_WGS) == 256 && base * splits < slots &&
           base * splits * 2 > slots && slots % splits == 0 && nblk / (splits * 2) >= 4 && base <= kWsCounters) {
         s.split_rows = 2 * base - slots / splits;
         splits_hi = 2 * splits;

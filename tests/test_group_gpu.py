@@ -48,7 +48,7 @@ def test_group_qkv_shapes():
 
 def test_group_gate_up_shapes():
     ws = [synth.stack_layer(7, proj, batch=1) for proj in (4, 5)]
-    _check_group(ws, (1, 16, 32, 300), "gate/up")
+    _check_group(ws, (1, 16, 32, 64, 300), "gate/up")
 
 
 def test_group_mixed_regions_and_ragged_batches():
@@ -96,7 +96,7 @@ def test_split_decode_two_split_counts():
     pk, wh = _packed(w)
     need = hinm.spmm_workspace_bytes(pk.plan, 16)
     assert need >= 2 * 19200 * 16 * 4          # partial planes for two splits
-    for b in (1, 7, 16, 17, 25, 32):
+    for b in (1, 7, 16, 17, 25, 32, 33, 64):
         x = torch.randn(2048, b, generator=torch.Generator().manual_seed(60 + b)).to(torch.bfloat16)
         print(f"[two split counts] batch {b}", flush=True)
         y = hinm.spmm(pk, x.to(DEV))
@@ -104,4 +104,4 @@ def test_split_decode_two_split_counts():
         xf = synth.as_f64(x)
         check_y(y, oh.spmm(wh, xf), np.abs(wh) @ np.abs(xf), f"two split counts batch {b}")
     w2 = synth.small(1024, 2048, 64, 0.5, 0.25, 1, seed=51)
-    _check_group([w, w2], (1, 16, 20, 32), "two split counts")
+    _check_group([w, w2], (1, 16, 20, 32, 48), "two split counts")
