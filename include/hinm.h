@@ -180,11 +180,12 @@ int hinm_abi_version(void);
  *   HINM_OPT_DECODE_WGS       env HINM_DECODE_WGS: about how many
  *                             workgroups the batch <= 64 kernel splits K over
  *                             (default 256; 1 .. 2^20).  With the default,
- *                             at batch <= 16 a launch whose row blocks times
- *                             splits fall between 256 and 512 gives its last
- *                             row blocks twice the splits, so that 512
- *                             workgroups run.  A different split count may
- *                             change the last bits of Y.
+ *                             a launch whose row blocks times splits fall
+ *                             between 256 and 512 gives its last row blocks
+ *                             twice the splits, so that 512 workgroups run
+ *                             (two share a compute unit at batch <= 32).  A
+ *                             different split count may change the last bits
+ *                             of Y.
  *   HINM_OPT_PREFILL_NT       env HINM_PREFILL_NT: token block of the
  *                             batch > 64 kernel, 128 or 256 (default 0:
  *                             256 from batch 1024; from 256 to 1023, 256
