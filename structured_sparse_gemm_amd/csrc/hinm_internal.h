@@ -43,6 +43,7 @@ struct SpmmShape {
   int n_kunits;    // K work units per tile (dense block = 1, 2:4 block = 2)
   int splits;      // K splits (>= 1)
   int64_t split_rows;  // split decode: row blocks with `splits` workgroups; the rest have 2 x splits
+  bool split_mix;      // prefill: two split counts (items whole or in two K halves, one piece a workgroup)
   bool two_per_cu;     // split decode: two workgroups share a compute unit (16 tokens always; 32 tokens
                        // with the smaller rounds, used when the launch has more than 256 workgroups)
   int64_t ws_counter_bytes;  // arrival counters at the start of the workspace (split decode)

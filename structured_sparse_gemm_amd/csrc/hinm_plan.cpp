@@ -258,6 +258,7 @@ SpmmShape spmm_shape(const hinm_plan_t* p, int64_t batch) {
   s.n_kunits = p->n_dense_pad / HINM_KB_DENSE + 2 * (p->n_24_pad / HINM_KB_24);
   s.splits = 1;
   s.split_rows = 0;
+  s.split_mix = false;
   s.two_per_cu = false;
   s.ws_bytes = 0;
   s.ws_counter_bytes = 0;
@@ -354,6 +355,32 @@ SpmmShape spmm_shape(const hinm_plan_t* p, int64_t batch) {
       s.splits = splits;
       s.ws_counter_bytes = kWsCounterBytes;
       s.ws_bytes = kWsCounterBytes + (int64_t)splits * items * 256 * s.nt;   // 256 threads x NT/4 floats
+    } else if (splits == 1 && s.nt == 128 && s.n_tblocks >= 2 && items > 256 && items < 512 &&
+               per_xcd_max == 64 && option(HINM_OPT_PREFILL_SPLITS) == 0 && items <= kWsCounters) {
+      // Between 256 and 512 items the grid's 512 workgroups would leave some
+      // compute units with two items and others with one (q, k and v
+      // together at batch 129-256: 384; up_proj: 344).  On each XCD the
+      // first items run whole and the rest in two K halves, one piece a
+      // workgroup, so that a unit holds at most an item and a half; partial
+      // sums only for the halved items, and only while they fit the
+      // allocation-free product's scratch, so that both entry points always
+      // run the same schedule.  Only with 128-token items in two or more
+      // token blocks: with 256-token items the partial sums cost more than
+      // the balance gains (2% slower for gate/up at batch 256 and up_proj at
+      // 512), and with one token block the 7B-shaped stack at batch 128 ran
+      // 1% slower although gate/up alone ran 1% faster.
+      int64_t n_half = 0;
+      for (int x = 0; x < 8; ++x) {
+        const int64_t nx = (x + 1) * items / 8 - x * items / 8;
+        n_half += nx - std::min(nx, std::max<int64_t>(0, 2 * nx - 64));
+      }
+      const int64_t ws = kWsCounterBytes + 2 * n_half * 256 * s.nt;
+      if (ws <= (int64_t)HINM_NOALLOC_SCRATCH_BYTES) {
+        s.splits = 2;
+        s.split_mix = true;
+        s.ws_counter_bytes = kWsCounterBytes;
+        s.ws_bytes = ws;
+      }
     }
     return s;
   }

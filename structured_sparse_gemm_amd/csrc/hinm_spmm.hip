@@ -1502,8 +1502,9 @@ __device__ inline BufRes make_res(const SpmmArgs& a) {
   return res;
 }
 
-template <int NT, bool SPLIT>
+template <int NT, bool SPLIT, bool MIX = false>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a0, Segs segs, int n_tb) {
+  static_assert(!MIX || SPLIT, "two split counts are a K split");
   using C = PrefillCfg<NT>;
   __shared__ __attribute__((aligned(16))) uint16_t xs_a[64 * C::PITCH];
   __shared__ __attribute__((aligned(16))) uint16_t xs_b[64 * C::PITCH];
@@ -1558,10 +1559,45 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a0, Segs segs,
     __syncthreads();
   }
 
-  const int i_lo = (int)((int64_t)xcd * items / 8), i_hi = (int)((int64_t)(xcd + 1) * items / 8);
+  // Pieces of this XCD: with one split count, pieces (item, split) of the
+  // XCD's contiguous range; with two (MIX), the XCD's items in order,
+  // the first wx whole and the rest in two halves, wx chosen so that the XCD
+  // has one piece per workgroup: the whole items take the first slots of
+  // their compute units and halves the second ones.  Partial sums are kept
+  // for the halved items only, numbered over all XCDs (m_h0: those of the
+  // XCDs before this one; n_half: all of them).  Its own instantiation
+  // (MIX), so that the one-count split keeps its code.
+  constexpr bool mix = MIX;
+  int i_lo, i_hi, m_lo = 0, m_wx = 0, m_h0 = 0, n_half = 0;
+  if constexpr (mix) {
+    for (int x = 0; x < 8; ++x) {
+      const int lo = (int)((int64_t)x * n_items / 8), nx = (int)((int64_t)(x + 1) * n_items / 8) - lo;
+      const int wx = min(nx, max(0, 2 * nx - per_xcd));
+      if (x < xcd) m_h0 += nx - wx;
+      if (x == xcd) {
+        m_lo = lo;
+        m_wx = wx;
+        i_lo = 0;
+        i_hi = wx + 2 * (nx - wx);
+      }
+      n_half += nx - wx;
+    }
+  } else {
+    i_lo = (int)((int64_t)xcd * items / 8);
+    i_hi = (int)((int64_t)(xcd + 1) * items / 8);
+  }
   for (int it = i_lo + slot; it < i_hi; it += per_xcd) {
     {
-      const int split = SPLIT ? it % splits : 0, item = SPLIT ? it / splits : it;
+      int split = SPLIT ? it % splits : 0, item = SPLIT ? it / splits : it, nsp = splits;
+      int pidx = item, pstride = n_items;          // partial sums: plane split, entry pidx of pstride
+      if constexpr (mix) {
+        const bool whole = it < m_wx;
+        item = m_lo + (whole ? it : m_wx + (it - m_wx) / 2);
+        split = whole ? 0 : (it - m_wx) % 2;
+        nsp = whole ? 1 : 2;
+        pidx = m_h0 + (whole ? 0 : (it - m_wx) / 2);
+        pstride = n_half;
+      }
       // items in groups of a.tb_group token blocks, row-block major inside a
       // group (one token block per group: token-block major)
       int tb, gtrb;
@@ -1592,7 +1628,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a0, Segs segs,
           for (int e = 0; e < 16; ++e) acc[r][j][e] = 0.f;
 
       const TileK tk = tile_k(a, t);
-      KShare ks = SPLIT ? k_share(tk, split, splits) : KShare{tk.kd0, tk.nbd, tk.ks0, tk.nbs, 0, 0};
+      KShare ks = SPLIT ? k_share(tk, split, nsp) : KShare{tk.kd0, tk.nbd, tk.ks0, tk.nbs, 0, 0};
       if (a.stagger) {
         // Items start their K loops at staggered blocks: tile t at t/n_tiles
         // of its range, so that tiles whose index lists walk X in the same
@@ -1622,7 +1658,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a0, Segs segs,
       }
       __syncthreads();
 
-      if constexpr (SPLIT) {
+      if (SPLIT && (!MIX || nsp > 1)) {
         // Partials part[split][item][NACC][thread] (the accumulators' own
         // register order, lanes adjacent) through agent-scope
         // (device-coherent) stores and loads; each workgroup waits for its
@@ -1630,7 +1666,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a0, Segs segs,
         // partials in split order and puts the counter back to 0.
         constexpr int NACC = 2 * C::NTB * 16;
         unsigned* ctr = reinterpret_cast<unsigned*>(reinterpret_cast<char*>(a.ws) - hinm::kWsCounterBytes) + item;
-        float* my = a.ws + ((int64_t)split * n_items + item) * 256 * NACC + threadIdx.x;
+        float* my = a.ws + ((int64_t)split * pstride + pidx) * 256 * NACC + threadIdx.x;
         for (int r = 0; r < 2; ++r)
           for (int j = 0; j < C::NTB; ++j)
             for (int e = 0; e < 16; ++e)
@@ -1638,26 +1674,26 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a0, Segs segs,
                                  __HIP_MEMORY_SCOPE_AGENT);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (threadIdx.x == 0) s_last = arrive(ctr, splits);
+        if (threadIdx.x == 0) s_last = arrive(ctr, nsp);
         __syncthreads();
         if (!s_last) continue;
         // per accumulator: up to SV splits' partials in flight at once,
         // added in split order from zero
         constexpr int SV = 4;
-        const int64_t sstride = (int64_t)n_items * 256 * NACC;
+        const int64_t sstride = (int64_t)pstride * 256 * NACC;
 #pragma unroll
         for (int r = 0; r < 2; ++r)
 #pragma unroll
           for (int j = 0; j < C::NTB; ++j) {
-            const float* pg = a.ws + (int64_t)item * 256 * NACC + (r * C::NTB + j) * 16 * 256 + threadIdx.x;
+            const float* pg = a.ws + (int64_t)pidx * 256 * NACC + (r * C::NTB + j) * 16 * 256 + threadIdx.x;
             float sum[16];
 #pragma unroll
             for (int e = 0; e < 16; ++e) sum[e] = 0.f;
-            for (int sp0 = 0; sp0 < splits; sp0 += SV) {
+            for (int sp0 = 0; sp0 < nsp; sp0 += SV) {
               float v[SV][16];
 #pragma unroll
               for (int u = 0; u < SV; ++u) {
-                if (sp0 + u < splits) {
+                if (sp0 + u < nsp) {
 #pragma unroll
                   for (int e = 0; e < 16; ++e)
                     v[u][e] = __hip_atomic_load(pg + (sp0 + u) * sstride + e * 256, __ATOMIC_RELAXED,
@@ -1670,7 +1706,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(SpmmArgs a0, Segs segs,
 #pragma unroll
               for (int u = 0; u < SV; ++u)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) sum[e] = (sp0 + u < splits) ? sum[e] + v[u][e] : sum[e];
+                for (int e = 0; e < 16; ++e) sum[e] = (sp0 + u < nsp) ? sum[e] + v[u][e] : sum[e];
             }
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[r][j][e] = sum[e];
@@ -1860,6 +1896,7 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
       sh.n_tblocks = (int)((batch + 63) / 64);
       sh.splits = 1;
       a.splits = 1;
+      sh.split_mix = false;
     }
   }
   if (sh.path == hinm::kPathDecodeSplit) {
@@ -1935,7 +1972,8 @@ static int spmm_impl(const hinm_plan_t& p, const PackedView& packed_v, const voi
       if (sh.splits > 1) hipLaunchKernelGGL((prefill_kernel<256, true>), dim3(nwg), dim3(256), 0, stream, a, sg, sh.n_tblocks);
       else hipLaunchKernelGGL((prefill_kernel<256, false>), dim3(nwg), dim3(256), 0, stream, a, sg, sh.n_tblocks);
     } else {
-      if (sh.splits > 1) hipLaunchKernelGGL((prefill_kernel<128, true>), dim3(nwg), dim3(256), 0, stream, a, sg, sh.n_tblocks);
+      if (sh.split_mix) hipLaunchKernelGGL((prefill_kernel<128, true, true>), dim3(nwg), dim3(256), 0, stream, a, sg, sh.n_tblocks);
+      else if (sh.splits > 1) hipLaunchKernelGGL((prefill_kernel<128, true>), dim3(nwg), dim3(256), 0, stream, a, sg, sh.n_tblocks);
       else hipLaunchKernelGGL((prefill_kernel<128, false>), dim3(nwg), dim3(256), 0, stream, a, sg, sh.n_tblocks);
     }
   } else {

@@ -88,10 +88,10 @@ def test_group_of_eight_weights():
 
 
 def test_split_decode_two_split_counts():
-    """300 row blocks at batch <= 32: two workgroups share a compute unit (at 17-32 tokens with the
+    """300 row blocks at batch <= 64: two workgroups share a compute unit (at 17-32 tokens with the
     smaller rounds), so 512 run at once; the first 88 row blocks run whole and the last 212 split in two
-    (88 + 424 = 512 workgroups).  Alone and as a group with a second weight (the split rule then sees
-    300 + 16 row blocks)."""
+    (88 + 424 = 512 workgroups); at 33-64 tokens the same split over one workgroup per unit.  Alone
+    and as a group with a second weight (300 + 16 row blocks)."""
     w = synth.small(19200, 2048, 64, 0.75, 0.55, 1, seed=50)
     pk, wh = _packed(w)
     need = hinm.spmm_workspace_bytes(pk.plan, 16)
@@ -105,3 +105,21 @@ def test_split_decode_two_split_counts():
         check_y(y, oh.spmm(wh, xf), np.abs(wh) @ np.abs(xf), f"two split counts batch {b}")
     w2 = synth.small(1024, 2048, 64, 0.5, 0.25, 1, seed=51)
     _check_group([w, w2], (1, 16, 20, 32, 48), "two split counts")
+
+
+def test_prefill_two_split_counts():
+    """150 row blocks in two 128-token blocks (batch 129-255): 300 items for the 512-workgroup grid, so
+    on each XCD the first items run whole and the rest in two K halves.  Alone, and as the q/k/v group
+    at batch 200 (384 items)."""
+    w = synth.small(9600, 2048, 64, 0.75, 0.55, 1, seed=52)
+    pk, wh = _packed(w)
+    assert hinm.spmm_workspace_bytes(pk.plan, 200) > 0          # the split's partial sums
+    for b in (129, 200, 255):
+        x = torch.randn(2048, b, generator=torch.Generator().manual_seed(70 + b)).to(torch.bfloat16)
+        print(f"[prefill two split counts] batch {b}", flush=True)
+        y = hinm.spmm(pk, x.to(DEV))
+        torch.cuda.synchronize()
+        xf = synth.as_f64(x)
+        check_y(y, oh.spmm(wh, xf), np.abs(wh) @ np.abs(xf), f"prefill two split counts batch {b}")
+    ws = [synth.stack_layer(4, proj, batch=1) for proj in (0, 1, 2)]
+    _check_group(ws, (200,), "qkv prefill two split counts")
