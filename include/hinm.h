@@ -195,8 +195,11 @@ int hinm_abi_version(void);
  *                             2:4 block counting two); else 128)
  *   HINM_OPT_PREFILL_SPLITS   env HINM_PREFILL_SPLITS: K split of each
  *                             batch > 64 work item, 1, 2 or 4 (default 0: 2
- *                             or 4 up to 128 items, else 1; a different split
- *                             may change the last bits of Y)
+ *                             or 4 up to 128 items; between 256 and 512
+ *                             items of 128 tokens in two or more token
+ *                             blocks, the first items of each XCD whole and
+ *                             the rest in two halves; else 1; a different
+ *                             split may change the last bits of Y)
  *   HINM_OPT_PREFILL_PATH     env HINM_PREFILL_PATH=staged -> 1: the
  *                             batch > 64 kernel gathers X through registers
  *                             instead of straight into LDS (same bits of Y)
