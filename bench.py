@@ -765,7 +765,7 @@ def main():
                    "batch": B, "regions_per_tile": {"dense": p.n_dense, "two_four": p.n_24, "pruned": p.n_pruned}},
         "roofline": {"bound": "mfma", "achieved": round(value, 3), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(value / MFMA_BF16_PEAK_TFLOPS, 5), "traffic": measured_traffic(B),
-                     "kernel": "prefill_kernel<256, false> (one launch per step)",
+                     "kernel": "prefill_kernel<256, false, false> (one launch per step)",
                      "kernel_source_hash": kernel_source_hash(),
                      "frac_of_measured_matmul_peak": round(value / peaks["matmul_bf16_8192_tflops"], 4),
                      "per_launch": {"useful_flops": alg["useful_flops"], "algorithmic_bytes": alg["bytes"],
