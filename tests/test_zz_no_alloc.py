@@ -26,6 +26,8 @@ def _packed(cout, cin, seed):
     ((1024, 4096), (64, 16)),        # split decode: 16 row blocks, K split 16 ways
     ((4096, 4096), (128, 100)),      # batch > 64 with the K split (64 items, 4 ways: 32 MiB of partials)
     ((512, 2048), (300, 65)),        # 8 tiles: K split at 128-token blocks, ragged tails
+    ((19200, 2048), (40, 16)),       # split decode with two split counts (300 row blocks)
+    ((9600, 2048), (200, 129)),      # batch > 64 with two split counts (300 items of 128 tokens)
 ])
 def test_noalloc_matches_spmm(shape, batches):
     cout, cin = shape
