@@ -396,3 +396,43 @@ def test_group_size_limits(lib):
         assert "weights" in lib.hinm_last_error().decode()
     with pytest.raises(ValueError):
         hinm.Group([object()] * 9)
+
+
+@pytest.mark.parametrize("rblocks", [64, 200, 257, 300, 344, 511, 512])
+def test_split_decode_workspace_follows_the_split_rule(lib, rblocks):
+    """The split decode's partial-sum planes, read back through the workspace query: a power-of-two split
+    for about 256 workgroups (each keeping >= 4 K-blocks); when row blocks x splits fall strictly between 256
+    and 512, the last row blocks take twice the splits (two planes more than one split needs), at every
+    batch up to 64."""
+    cout, cin = 64 * rblocks, 2048
+    p = hinm.plan(cout, cin, 64, 0.75, 0.55)
+    nblk = p.n_dense_pad // 32 + p.n_24_pad // 64
+    splits = 1
+    while splits < 64 and rblocks * splits * 2 <= 256 and nblk // (splits * 2) >= 4:
+        splits *= 2
+    mixed = rblocks * splits < 512 < 2 * rblocks * splits and nblk // (2 * splits) >= 4
+    planes = 2 * splits if mixed else splits
+    for b, nt in ((1, 16), (16, 16), (17, 32), (32, 32), (40, 64), (64, 64)):
+        want = 0 if planes == 1 else 65536 + planes * cout * nt * 4
+        assert hinm.spmm_workspace_bytes(p, b) == want, (rblocks, b)
+
+
+@pytest.mark.parametrize("rblocks,batch,mixed", [(150, 200, True), (150, 129, True), (150, 128, False),
+                                                 (100, 200, False), (255, 200, True), (172, 512, False)])
+def test_prefill_workspace_follows_the_two_count_rule(lib, rblocks, batch, mixed):
+    """The batch > 64 kernel's two split counts, read back through the workspace query: with 128-token
+    items in two or more token blocks and between 256 and 512 items, each XCD's first items run whole and
+    the rest in two halves (so that the XCD has one piece per workgroup of 64), and partial sums are kept
+    for the halved items only; otherwise no workspace (more than 128 items, one split)."""
+    cout, cin = 64 * rblocks, 2048
+    p = hinm.plan(cout, cin, 64, 0.75, 0.55)
+    got = hinm.spmm_workspace_bytes(p, batch)
+    if not mixed:
+        assert got == 0
+        return
+    items = rblocks * -(-batch // 128)
+    n_half = 0
+    for x in range(8):
+        nx = (x + 1) * items // 8 - x * items // 8
+        n_half += nx - min(nx, max(0, 2 * nx - 64))
+    assert got == 65536 + 2 * n_half * 256 * 128
