@@ -324,6 +324,14 @@ SpmmShape spmm_shape(const hinm_plan_t* p, int64_t batch) {
         sp = (int)option(HINM_OPT_PREFILL_SPLITS);
       } else if (items <= 128) {
         while (sp < 4 && items * sp * 2 <= 512 && nblk / (sp * 2) >= 8) sp *= 2;
+      } else if (items * 2 > 448 && items * 2 <= 512 && kunits >= 120 && nblk / 2 >= 8) {
+        // Nearly one item per compute unit on a long K range (down_proj at
+        // batch 1024: 256 items of 256 tokens): one workgroup alone on a unit
+        // hides its latencies poorly, and two halves per unit pay for their
+        // partial sums (65.8 -> 60.8 us); with shorter K ranges (q_proj,
+        // up_proj) or fewer items (192: some units would hold two halves and
+        // others one) the split is slower.
+        sp = 2;
       }
       return sp;
     };
