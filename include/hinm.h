@@ -195,8 +195,9 @@ int hinm_abi_version(void);
  *                             2:4 block counting two); else 128)
  *   HINM_OPT_PREFILL_SPLITS   env HINM_PREFILL_SPLITS: K split of each
  *                             batch > 64 work item, 1, 2 or 4 (default 0: 2
- *                             or 4 up to 128 items; between 256 and 512
- *                             items of 128 tokens in two or more token
+ *                             or 4 up to 128 items; 2 with 225 to 256 items
+ *                             on a K range of >= 120 units; between 256 and
+ *                             512 items of 128 tokens in two or more token
  *                             blocks, the first items of each XCD whole and
  *                             the rest in two halves; else 1; a different
  *                             split may change the last bits of Y)
