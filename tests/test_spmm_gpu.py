@@ -299,6 +299,27 @@ def test_spmm_decode_small_batch_x_layouts_bit_identical():
         check_y(y_ref, oh.spmm(c.w_hat, xf), np.abs(c.w_hat) @ np.abs(xf), f"small batch {b}")
 
 
+def test_spmm_batch1_wide_inputs():
+    """Batch 1 gathers each element with a 2-byte load.  Input widths from 4100 to 16384 channels, the last
+    channel kept in every tile (its element ends the X buffer): a contiguous X (rows 2 bytes apart) must
+    give the same bits as the same X with 8-token rows, and both meet the oracle's bar."""
+    for cin, cout in ((15872, 64), (15860, 64), (15876, 64), (16384, 64), (4100, 256)):
+        w = synth.small(cout, cin, 64, 0.6, 0.35, 1, seed=cin)
+        w.importance[:, -1] = w.importance.max() * 4.0
+        c = Case(w)
+        x = torch.randn(cin, 1, generator=torch.Generator().manual_seed(cin)).to(torch.bfloat16)
+        x[-1] = 1.5                                                    # never zero: a lost element shows
+        wide = torch.zeros(cin, 8, dtype=torch.bfloat16, device=DEV)
+        wide[:, :1] = x.to(DEV)
+        print(f"[spmm]   batch 1, cin={cin}, contiguous X and 8-token rows", flush=True)
+        y = hinm.spmm(c.pk, x.to(DEV))
+        y_ref = hinm.spmm(c.pk, wide[:, :1])
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), cin
+        xf = synth.as_f64(x)
+        check_y(y, oh.spmm(c.w_hat, xf), np.abs(c.w_hat) @ np.abs(xf), f"batch 1 cin {cin}")
+
+
 @pytest.mark.parametrize("batch", [16, 100])
 def test_spmm_x_beyond_32bit_offsets(batch):
     """X whose row stride puts its last row past 2^31 bytes (4096 rows of 300000 elements, 2.46 GB).
