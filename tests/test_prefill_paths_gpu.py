@@ -179,3 +179,27 @@ def test_prefill_split_k_default_full_size():
     torch.cuda.synchronize()
     xf = synth.as_f64(x)
     check_y(y, oh.spmm(wh, xf), np.abs(wh) @ np.abs(xf), "q_proj batch 128")
+
+
+def test_prefill_nearly_one_item_per_unit_k_halves():
+    """down_proj 4096x11008 at batches 800, 1000 and 1023: 4 token blocks of 256 (the last one ragged) x 64
+    tiles = 256 items on a long K range, so each item's K range is split in two (the workspace holds the
+    arrival counters and the halves' partial sums).  Every output row against the oracle, and the unsplit
+    schedule of the same product within the same bar."""
+    w = synth.down_proj(batch=16)
+    pk = hinm.pack(w.w_bf16.to(DEV), w.importance.to(DEV), w.tile_rows, w.t_s, w.v_s, w.perm.to(DEV))
+    _, _, inter = oracle_pack(w)
+    wh = oh.masked_weight(bits_of(w.w_bf16), inter["mask"])
+    for batch in (800, 1000, 1023):
+        assert hinm.spmm_workspace_bytes(pk.plan, batch) > 0, "the K split is not in effect"
+        x = torch.randn(w.cin, batch, generator=torch.Generator().manual_seed(7 + batch)).to(torch.bfloat16)
+        xd = x.to(DEV)
+        print(f"[prefill] down_proj batch={batch} (K halves)", flush=True)
+        y = hinm.spmm(pk, xd)
+        with hinm.options(prefill_splits=1):
+            y1 = hinm.spmm(pk, xd)
+        torch.cuda.synchronize()
+        xf = synth.as_f64(x)
+        ref, scale = oh.spmm(wh, xf), np.abs(wh) @ np.abs(xf)
+        check_y(y, ref, scale, f"down_proj batch {batch}, K halves")
+        check_y(y1, ref, scale, f"down_proj batch {batch}, unsplit")
