@@ -1450,17 +1450,27 @@ __device__ inline void prefill_phase_lds(const SpmmArgs& a, const BufRes& res, u
 
 // FAST: 16-byte aligned X rows and a token block inside the batch; TAIL: the
 // token block ends past the batch (1: even batch, 2: odd batch).
-// Share `split` of an item's K range split `splits` ways (blocks in order,
-// dense first): the first dense and 2:4 block and the counts.
+// Share `split` of an item's K range split `splits` ways: the first dense and
+// 2:4 block and the counts.  The blocks stay in order, dense first.  Cut in
+// two, the range is cut by cost: a 2:4 block gathers 64 X rows against a
+// dense block's 32, so a dense block counts one unit and a 2:4 block two (a
+// cut inside a 2:4 block goes to its start, the same rule for both halves,
+// so the halves partition the blocks).  Cut in four, it is cut by block
+// count: the cost cut was measured slower there (down_proj 4096x11008 at
+// batch 128 / 256 / 512: 21.7 / 30.7 / 42.3 -> 24.1 / 31.8 / 43.2 us, four
+// balanced splits finishing and handing over their partial sums together),
+// while in two it was faster (batch 800 / 1024: 61.6 / 60.1 -> 60.3 / 58.8;
+// up_proj 11008x4096 at batch 256, halves: 30.2 -> 29.1).
 struct KShare {
   int kd, nd, ks, ns;
   int rd, rs;       // first block of the dense and 2:4 loops (the order wraps around)
 };
 __device__ inline KShare k_share(const TileK& tk, int split, int splits) {
-  const int nblk = tk.nbd + tk.nbs;
-  const int lo = (int)((int64_t)split * nblk / splits), hi = (int)((int64_t)(split + 1) * nblk / splits);
+  const int w = splits == 2 ? 2 : 1;                 // units of a 2:4 block
+  const int64_t units = tk.nbd + w * (int64_t)tk.nbs;
+  const int lo = (int)((int64_t)split * units / splits), hi = (int)((int64_t)(split + 1) * units / splits);
   const int d_lo = min(lo, tk.nbd), d_hi = min(hi, tk.nbd);
-  const int s_lo = max(lo, tk.nbd) - tk.nbd, s_hi = max(hi, tk.nbd) - tk.nbd;
+  const int s_lo = (max(lo, tk.nbd) - tk.nbd) / w, s_hi = (max(hi, tk.nbd) - tk.nbd) / w;
   return {tk.kd0 + d_lo, d_hi - d_lo, tk.ks0 + s_lo, s_hi - s_lo, 0, 0};
 }
 
