@@ -199,8 +199,11 @@ int hinm_abi_version(void);
  *                             on a K range of >= 120 units; between 256 and
  *                             512 items of 128 tokens in two or more token
  *                             blocks, the first items of each XCD whole and
- *                             the rest in two halves; else 1; a different
- *                             split may change the last bits of Y)
+ *                             the rest in two halves; else 1.  Cut in
+ *                             two, an item's K range is cut by cost (a
+ *                             dense block one unit, a 2:4 block two); in
+ *                             four, by block count.  A different split may
+ *                             change the last bits of Y)
  *   HINM_OPT_PREFILL_PATH     env HINM_PREFILL_PATH=staged -> 1: the
  *                             batch > 64 kernel gathers X through registers
  *                             instead of straight into LDS (same bits of Y)
